@@ -1,0 +1,178 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each case patches one plausible error into the oracle (a dropped term, a wrong
+sign or operand, a wrong index or tie rule, a misplaced rounding) and checks
+that at least one pin then fails. CPU only; nothing here touches a GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import dualflow as odf
+
+
+def _gelu_tanh(x):
+    return 0.5 * x * (1 + np.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _attn_noscale(q, K, V):
+    s = K @ q
+    m = s.max()
+    p = np.exp(s - m)
+    return (p @ V) / p.sum(), m + math.log(p.sum())
+
+
+def _ln_unbiased(x, g, eps):
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).sum(axis=-1, keepdims=True) / (x.shape[-1] - 1)
+    return (x - mu) / np.sqrt(var + eps) * g
+
+
+def _ln_no_eps(x, g, eps):
+    mu = x.mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True)) * g
+
+
+def _mix_no_floor(l1, l2):
+    p1 = odf.softmax(np.asarray(l1, float))
+    if l2 is None:
+        return p1, 1.0, int(np.argmax(p1))
+    p2 = odf.softmax(np.asarray(l2, float))
+    a = float(np.sum(p1 * p1))
+    p = a * p1 + (1 - a) * p2
+    return p, a, int(np.argmax(p))
+
+
+def _mix_swapped(l1, l2):
+    p1 = odf.softmax(np.asarray(l1, float))
+    if l2 is None:
+        return p1, 1.0, int(np.argmax(p1))
+    p2 = odf.softmax(np.asarray(l2, float))
+    a = min(1.0, max(0.5, float(np.sum(p1 * p1))))
+    p = a * p2 + (1 - a) * p1
+    return p, a, int(np.argmax(p))
+
+
+def _mix_alpha_half_plus(l1, l2):
+    p1 = odf.softmax(np.asarray(l1, float))
+    if l2 is None:
+        return p1, 1.0, int(np.argmax(p1))
+    p2 = odf.softmax(np.asarray(l2, float))
+    a = 0.5 * (1 + float(np.sum(p1 * p1)))
+    p = a * p1 + (1 - a) * p2
+    return p, a, int(np.argmax(p))
+
+
+def _topk_upper_ties(r, k):
+    r = np.asarray(r, float)
+    idx = np.argsort(-r[::-1], kind="stable")
+    return (len(r) - 1 - idx)[:k].astype(np.int32)
+
+
+def _round_via_f32(x, dtype):
+    if dtype == "bf16":
+        import torch
+        x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+        return torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def _round_truncate(x, dtype):
+    if dtype == "bf16":
+        m, e = np.frexp(np.asarray(x, dtype=np.float64))
+        return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def _qkv_aux_writes(p, u, cfg):
+    q, k, v = _orig_qkv(p, u, cfg)
+    if len(u) == 2:
+        qkv2 = odf._matvec(p["w_qkv"], u[1])
+        k = odf.round_to(qkv2[cfg.d:2 * cfg.d], cfg.dtype).reshape(cfg.H, cfg.Dh)
+        v = odf.round_to(qkv2[2 * cfg.d:], cfg.dtype).reshape(cfg.H, cfg.Dh)
+    return q, k, v
+
+
+def _qkv_no_round(p, u, cfg):
+    d = cfg.d
+    qkv1 = odf._matvec(p["w_qkv"], u[0])
+    q = [qkv1[:d]]
+    if len(u) == 2:
+        q.append(odf.couple_query(odf._matvec(p["w_qkv"], u[1])[:d], p["a"], q[0]))
+    return q, qkv1[d:2 * d].reshape(cfg.H, cfg.Dh), qkv1[2 * d:].reshape(cfg.H, cfg.Dh)
+
+
+_orig_qkv = odf.qkv_rows
+
+
+def _attend_excl_new(q, K, V, pos):
+    n = max(pos, 1)
+    o, _ = odf.attention_one(q, K[:n], V[:n])
+    return o
+
+
+MUTATIONS = [
+    ("gelu_tanh_approx", "gelu", _gelu_tanh, [pins.pin_gelu]),
+    ("attention_no_scale", "attention_one", _attn_noscale, [pins.pin_attention_sdpa]),
+    ("layernorm_unbiased_var", "layer_norm", _ln_unbiased, [pins.pin_layer_norm]),
+    ("layernorm_no_eps", "layer_norm", _ln_no_eps, [pins.pin_layer_norm]),
+    ("alpha_without_floor", "mix_head", _mix_no_floor, [pins.pin_mix_properties, pins.pin_mix_golden]),
+    ("mixture_weights_swapped", "mix_head", _mix_swapped, [pins.pin_mix_properties, pins.pin_mix_golden]),
+    ("alpha_half_one_plus_cp", "mix_head", _mix_alpha_half_plus, [pins.pin_mix_properties, pins.pin_mix_golden]),
+    ("topk_ties_to_upper", "topk_ids", _topk_upper_ties, [pins.pin_topk]),
+    ("bf16_double_rounding", "round_to", _round_via_f32, [pins.pin_round_bf16]),
+    ("bf16_truncation", "round_to", _round_truncate, [pins.pin_round_bf16]),
+    ("query_coupling_sign", "couple_query", lambda q2, a, q1: q2 - a * q1,
+     [lambda: pins.pin_query_coupling(pins.TINY_BF16)]),
+    ("query_coupling_wrong_operand", "couple_query", lambda q2, a, q1: q2 + a * q2,
+     [lambda: pins.pin_query_coupling(pins.TINY_BF16)]),
+    ("mid_coupling_wrong_operand", "couple_mid", lambda g2, b, g1: g2 + b * g2,
+     [lambda: pins.pin_mid_coupling(pins.TINY_BF16)]),
+    ("mid_coupling_rounded_primary", "couple_mid", lambda g2, b, g1: g2 + b * odf._round_bf16(g1),
+     [lambda: pins.pin_mid_coupling(pins.TINY_BF16)]),
+    ("out_coupling_wrong_operand", "couple_out", lambda y2, c, y1: y2 + c * y2,
+     [lambda: pins.pin_out_coupling(pins.TINY_BF16)]),
+    ("out_coupling_dropped", "couple_out", lambda y2, c, y1: y2,
+     [lambda: pins.pin_out_coupling(pins.TINY_F32)]),
+    ("aux_writes_kv", "qkv_rows", _qkv_aux_writes, [lambda: pins.pin_aux_onoff(pins.TINY_BF16)]),
+    ("kv_not_rounded", "qkv_rows", _qkv_no_round, [lambda: pins.pin_prefill_equals_decode(pins.TINY_BF16),
+                                                    lambda: pins.pin_query_coupling(pins.TINY_BF16)]),
+    ("attend_excludes_new_entry", "attend", _attend_excl_new,
+     [lambda: pins.pin_prefill_equals_decode(pins.TINY_F32), lambda: pins.pin_query_coupling(pins.TINY_F32)]),
+]
+
+
+@pytest.mark.parametrize("name,attr,fn,checks", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, attr, fn, checks):
+    monkeypatch.setattr(odf, attr, fn)
+    caught = False
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            caught = True
+            break
+    assert caught, f"planted mistake '{name}' passed every pin"
+
+
+def test_moe_aux_gates_from_primary_is_caught(monkeypatch):
+    orig = odf._mlp_moe
+
+    def wrong(p, v, flows, dtype, k, r1_given, tr=None):
+        y, ids, gates = orig(p, v, 1, dtype, k, r1_given, tr)
+        if flows == 1:
+            return y, ids, gates
+        # aux reuses the primary gates instead of its own
+        g = gates[0]
+        yy = [y[0], np.zeros_like(y[0])]
+        for j, e in enumerate(ids):
+            gg = odf.gelu(p["w_eup"][e] @ v[1]) + p["b"] * odf.gelu(p["w_eup"][e] @ v[0])
+            yy[1] = yy[1] + g[j] * (p["w_edown"][e] @ odf.round_to(gg, dtype))
+        yy[1] = yy[1] + p["c"] * yy[0]
+        return yy, ids, np.stack([g, g])
+
+    monkeypatch.setattr(odf, "_mlp_moe", wrong)
+    with pytest.raises(AssertionError):
+        pins.pin_moe_all_experts_is_full_mixture()
