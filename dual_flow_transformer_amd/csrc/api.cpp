@@ -1,0 +1,378 @@
+// C ABI of the dual-flow grouped decode step: argument checks, workspace
+// carving and the per-layer kernel sequence on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/dualflow.h"
+#include "df_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int dtype) { return dtype == DF_BF16 ? 2 : 4; }
+
+// Workspace regions (byte offsets from the workspace base).
+struct WsLayout {
+    size_t status, h, xd, xo, xf, q, part, logits, r, ids, gates, offsets, perm, inv, grows, yrows, total;
+};
+
+WsLayout layout(const df_config& c) {
+    const size_t es = elem_size(c.dtype);
+    const size_t M = 2 * (size_t)c.batch;
+    const bool moe = c.n_experts > 0;
+    const size_t P = (size_t)c.batch * (moe ? c.top_k : 0);
+    WsLayout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    L.status = take(kAlign);
+    L.h = take(M * c.d_model * 4);
+    L.xd = take(M * c.d_model * es);
+    L.xo = take(M * c.d_model * es);
+    L.xf = take(moe ? 0 : M * (size_t)c.ffn * es);
+    L.q = take(M * c.d_model * 4);
+    L.part = take(dfk::attention_part_floats(c.batch, c.n_heads, c.max_seq, c.head_dim) * 4);
+    L.logits = take(M * (size_t)c.vocab * 4);
+    L.r = take(moe ? M * c.n_experts * 4 : 0);
+    L.ids = take(P * 4);
+    L.gates = take(P * 2 * 4);
+    L.offsets = take(moe ? (size_t)(c.n_experts + 1) * 4 : 0);
+    L.perm = take(P * 4);
+    L.inv = take(P * 4);
+    L.grows = take(P * 2 * (size_t)c.expert_ffn * es);
+    L.yrows = take(P * 2 * (size_t)c.d_model * 4);
+    L.total = o;
+    return L;
+}
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
+
+int check_config(const df_config* c) {
+    if (!c) return DF_ERR_NULL;
+    if (c->dtype != DF_F32 && c->dtype != DF_BF16) return DF_ERR_DTYPE;
+    if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->vocab < 1 || c->batch < 1 ||
+        c->max_seq < 1 || c->n_experts < 0)
+        return DF_ERR_SHAPE;
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return DF_ERR_SHAPE;
+    if (c->d_model != c->n_heads * c->head_dim || c->d_model > 4096) return DF_ERR_SHAPE;
+    if (c->batch > 64) return DF_ERR_SHAPE;
+    if (!(c->ln_eps > 0.f)) return DF_ERR_ARG;
+    const bool moe = c->n_experts > 0;
+    if (moe) {
+        if (c->dtype != DF_BF16) return DF_ERR_DTYPE;
+        if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts || c->n_experts > 1024) return DF_ERR_SHAPE;
+        if (c->expert_ffn < 1 || c->expert_ffn % 256 != 0 || c->n_experts % 16 != 0) return DF_ERR_SHAPE;
+    } else {
+        if (c->ffn < 1) return DF_ERR_SHAPE;
+    }
+    if (c->dtype == DF_BF16) {
+        if (c->d_model % 256 != 0 || (!moe && c->ffn % 256 != 0) || c->vocab % 16 != 0) return DF_ERR_SHAPE;
+    } else {
+        if (c->batch > 8 || c->d_model % 4 != 0 || c->ffn % 4 != 0) return DF_ERR_SHAPE;
+    }
+    return DF_OK;
+}
+
+int check_weights(const df_config& c, const df_weights* w) {
+    if (!w) return DF_ERR_NULL;
+    const void* need[] = {w->tok_emb[0], w->tok_emb[1], w->pos_emb, w->ln1, w->ln2, w->lnf, w->w_qkv, w->w_o,
+                          w->cpl_a, w->cpl_b, w->cpl_c, w->w_out};
+    for (const void* p : need)
+        if (!p) return DF_ERR_NULL;
+    for (const void* p : need)
+        if (!aligned16(p)) return DF_ERR_ALIGN;
+    if (c.n_experts > 0) {
+        const void* moe[] = {w->w_router, w->w_exp_up, w->w_exp_down};
+        for (const void* p : moe)
+            if (!p) return DF_ERR_NULL;
+        for (const void* p : moe)
+            if (!aligned16(p)) return DF_ERR_ALIGN;
+    } else {
+        if (!w->w_up || !w->w_down) return DF_ERR_NULL;
+        if (!aligned16(w->w_up) || !aligned16(w->w_down)) return DF_ERR_ALIGN;
+    }
+    return DF_OK;
+}
+
+int check_kv(const df_kv* kv) {
+    if (!kv || !kv->k || !kv->v || !kv->len) return DF_ERR_NULL;
+    if (!aligned16(kv->k) || !aligned16(kv->v) || ((uintptr_t)kv->len & 3)) return DF_ERR_ALIGN;
+    return DF_OK;
+}
+
+int check_ws(const df_config& c, const void* ws, size_t ws_bytes) {
+    if (!ws) return DF_ERR_NULL;
+    if ((uintptr_t)ws % kAlign) return DF_ERR_ALIGN;
+    if (ws_bytes < layout(c).total) return DF_ERR_WORKSPACE;
+    return DF_OK;
+}
+
+// --- kernel timing with events --------------------------------------------
+struct Timing {
+    std::mutex mu;
+    int kclass = -1;
+    std::vector<hipEvent_t> ev;   // pairs
+    size_t used = 0;
+};
+Timing g_timing;
+constexpr size_t kMaxTimed = 65536;
+
+void timing_events(int kclass, hipEvent_t* start, hipEvent_t* stop) {
+    *start = nullptr;
+    *stop = nullptr;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.kclass != kclass || g_timing.used >= kMaxTimed) return;
+    while (g_timing.ev.size() < 2 * (g_timing.used + 1)) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        g_timing.ev.push_back(e);
+    }
+    *start = g_timing.ev[2 * g_timing.used];
+    *stop = g_timing.ev[2 * g_timing.used + 1];
+    ++g_timing.used;
+}
+
+struct Step {
+    const df_config& c;
+    const df_weights& w;
+    const df_kv& kv;
+    char* ws;
+    WsLayout L;
+    hipStream_t s;
+
+    template <typename P> P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
+
+    // One step over all layers; head: run the LM head and mixture head.
+    int run(const int32_t* tok, int tok_stride, int nflows, const float* router_logits, float* logits,
+            float* p_mix, float* alpha, int32_t* next_tok, int32_t* expert_ids, bool head) {
+        const size_t es = elem_size(c.dtype);
+        const int B = c.batch, d = c.d_model, L_ = c.n_layers;
+        const bool moe = c.n_experts > 0;
+        int32_t* status = at<int32_t>(L.status);
+        float* h = at<float>(L.h);
+        void* xd = ws + L.xd;
+        void* xo = ws + L.xo;
+        void* xf = ws + L.xf;
+        float* q = at<float>(L.q);
+        hipError_t e = dfk::embed_ln(c.dtype, w.tok_emb[0], w.tok_emb[1], w.pos_emb, tok, tok_stride, kv.len, B, d,
+                                     c.max_seq, c.vocab, nflows, w.ln1, c.ln_eps, h, xd, status, s);
+        if (e != hipSuccess) return DF_ERR_HIP;
+        const size_t kv_layer = (size_t)B * c.n_heads * c.max_seq * c.head_dim * es;
+        const size_t ffn = moe ? (size_t)c.expert_ffn : (size_t)c.ffn;
+        for (int l = 0; l < L_; ++l) {
+            char* kc = reinterpret_cast<char*>(kv.k) + l * kv_layer;
+            char* vc = reinterpret_cast<char*>(kv.v) + l * kv_layer;
+            dfk::GemvArgs g{};
+            g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.H = c.n_heads; g.Dh = c.head_dim; g.S_max = c.max_seq;
+            // Q/K/V projection: Q coupling and primary K/V append fused
+            g.x = xd; g.w = reinterpret_cast<const char*>(w.w_qkv) + (size_t)l * 3 * d * d * es;
+            g.N = 3 * d; g.K = d; g.epi = dfk::EPI_QKV; g.cpl = w.cpl_a + (size_t)l * d; g.q_out = q;
+            g.kc = kc; g.vc = vc; g.len = kv.len; g.status = status;
+            if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+            // shared-K/V attention of both queries over positions 0..len[b]
+            dfk::AttnArgs a{};
+            a.dtype = c.dtype; a.k = kc; a.v = vc; a.B = B; a.H = c.n_heads; a.S_max = c.max_seq; a.Dh = c.head_dim;
+            a.q = q; a.a = nullptr; a.nkeys = kv.len; a.nkeys_add = 1; a.nflows = nflows;
+            a.part = at<float>(L.part); a.o_rows = xo;
+            timing_events(0, &a.ev_start, &a.ev_stop);
+            if (dfk::attention(a, s) != hipSuccess) return DF_ERR_HIP;
+            // output projection + residual
+            g.x = xo; g.w = reinterpret_cast<const char*>(w.w_o) + (size_t)l * d * d * es;
+            g.N = d; g.K = d; g.epi = dfk::EPI_RESID; g.cpl = nullptr; g.h = h;
+            if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+            if (dfk::layer_norm_rows(c.dtype, h, w.ln2 + (size_t)l * d, c.ln_eps, B, d, nflows, xd, s) != hipSuccess)
+                return DF_ERR_HIP;
+            const float* cb = w.cpl_b + (size_t)l * ffn;
+            const float* cc = w.cpl_c + (size_t)l * d;
+            if (!moe) {
+                g.x = xd; g.w = reinterpret_cast<const char*>(w.w_up) + (size_t)l * ffn * d * es;
+                g.N = (int)ffn; g.K = d; g.epi = dfk::EPI_GELU_B; g.cpl = cb; g.x_out = xf;
+                if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+                g.x = xf; g.w = reinterpret_cast<const char*>(w.w_down) + (size_t)l * d * ffn * es;
+                g.N = d; g.K = (int)ffn; g.epi = dfk::EPI_RESID; g.cpl = cc; g.h = h;
+                if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+            } else {
+                const int E = c.n_experts;
+                g.x = xd; g.w = reinterpret_cast<const char*>(w.w_router) + (size_t)l * E * d * es;
+                g.N = E; g.K = d; g.epi = dfk::EPI_STORE; g.out_f32 = at<float>(L.r);
+                if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+                dfk::MoeArgs m{};
+                m.dtype = c.dtype; m.x = xd; m.r = at<float>(L.r);
+                m.r1_given = router_logits ? router_logits + (size_t)l * B * E : nullptr;
+                m.w_up = reinterpret_cast<const char*>(w.w_exp_up) + (size_t)l * E * ffn * d * es;
+                m.w_down = reinterpret_cast<const char*>(w.w_exp_down) + (size_t)l * E * d * ffn * es;
+                m.cpl_b = cb; m.cpl_c = cc; m.B = B; m.d = d; m.E = E; m.k = c.top_k; m.Fe = (int)ffn;
+                m.nflows = nflows; m.h = h;
+                m.ids_out = expert_ids ? expert_ids + (size_t)l * B * c.top_k : nullptr;
+                m.ids = at<int32_t>(L.ids); m.gates = at<float>(L.gates); m.offsets = at<int32_t>(L.offsets);
+                m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = ws + L.grows;
+                m.y_rows = at<float>(L.yrows);
+                if (dfk::moe(m, s) != hipSuccess) return DF_ERR_HIP;
+            }
+            const float* gn = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf;
+            if (dfk::layer_norm_rows(c.dtype, h, gn, c.ln_eps, B, d, nflows, xd, s) != hipSuccess) return DF_ERR_HIP;
+        }
+        if (head) {
+            float* lg = logits ? logits : at<float>(L.logits);
+            dfk::GemvArgs g{};
+            g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.x = xd; g.w = w.w_out; g.N = c.vocab; g.K = d;
+            g.epi = dfk::EPI_STORE; g.out_f32 = lg;
+            if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+            if (dfk::mix_head(lg, B, c.vocab, nflows == 2, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
+        }
+        if (dfk::len_add(kv.len, B, 1, s) != hipSuccess) return DF_ERR_HIP;
+        return DF_OK;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+size_t df_workspace_bytes(const df_config* cfg) {
+    if (check_config(cfg) != DF_OK) return 0;
+    return layout(*cfg).total;
+}
+
+int df_decode_step(const df_config* cfg, const df_weights* w, const df_kv* kv, const int32_t* d_tokens,
+                   int32_t aux_on, const float* d_router_logits, float* d_logits, float* d_p_mix, float* d_alpha,
+                   int32_t* d_next_tok, int32_t* d_expert_ids, void* d_ws, size_t ws_bytes, void* stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_weights(*cfg, w))) return rc;
+    if ((rc = check_kv(kv))) return rc;
+    if (!d_tokens || !d_p_mix || !d_alpha) return DF_ERR_NULL;
+    if (aux_on != 0 && aux_on != 1) return DF_ERR_ARG;
+    if (d_router_logits && cfg->n_experts == 0) return DF_ERR_ARG;
+    if ((d_logits && !aligned16(d_logits)) || !aligned16(d_p_mix)) return DF_ERR_ALIGN;
+    if ((rc = check_ws(*cfg, d_ws, ws_bytes))) return rc;
+    Step st{*cfg, *w, *kv, reinterpret_cast<char*>(d_ws), layout(*cfg), reinterpret_cast<hipStream_t>(stream)};
+    return st.run(d_tokens, 1, aux_on ? 2 : 1, d_router_logits, d_logits, d_p_mix, d_alpha, d_next_tok,
+                  d_expert_ids, true);
+}
+
+int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* kv, const int32_t* d_tokens,
+                       int32_t T, void* d_ws, size_t ws_bytes, void* stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_weights(*cfg, w))) return rc;
+    if ((rc = check_kv(kv))) return rc;
+    if (!d_tokens) return DF_ERR_NULL;
+    if (T < 0 || T > cfg->max_seq) return DF_ERR_SHAPE;
+    if ((rc = check_ws(*cfg, d_ws, ws_bytes))) return rc;
+    Step st{*cfg, *w, *kv, reinterpret_cast<char*>(d_ws), layout(*cfg), reinterpret_cast<hipStream_t>(stream)};
+    for (int t = 0; t < T; ++t) {
+        rc = st.run(d_tokens + t, T, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false);
+        if (rc) return rc;
+    }
+    return DF_OK;
+}
+
+int df_kv_append(const df_config* cfg, const df_kv* kv, int32_t layer, const int32_t* d_pos, const float* d_k,
+                 const float* d_v, int32_t* d_status, void* stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_kv(kv))) return rc;
+    if (!d_pos || !d_k || !d_v) return DF_ERR_NULL;
+    if (layer < 0 || layer >= cfg->n_layers) return DF_ERR_SHAPE;
+    const size_t es = elem_size(cfg->dtype);
+    const size_t kv_layer = (size_t)cfg->batch * cfg->n_heads * cfg->max_seq * cfg->head_dim * es;
+    hipError_t e = dfk::kv_append(cfg->dtype, reinterpret_cast<char*>(kv->k) + layer * kv_layer,
+                                  reinterpret_cast<char*>(kv->v) + layer * kv_layer, cfg->batch, cfg->n_heads,
+                                  cfg->max_seq, cfg->head_dim, d_pos, d_k, d_v, d_status,
+                                  reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t aux_on, float* d_p_mix,
+                float* d_alpha, int32_t* d_next_tok, void* stream) {
+    if (!d_logits || !d_p_mix || !d_alpha) return DF_ERR_NULL;
+    if (batch < 1 || vocab < 1) return DF_ERR_SHAPE;
+    if (aux_on != 0 && aux_on != 1) return DF_ERR_ARG;
+    hipError_t e = dfk::mix_head(d_logits, batch, vocab, aux_on, d_p_mix, d_alpha, d_next_tok,
+                                 reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_seq, int32_t head_dim) {
+    if (batch < 1 || n_heads < 1 || max_seq < 1 || (head_dim != 32 && head_dim != 64 && head_dim != 128)) return 0;
+    return align_up(dfk::attention_part_floats(batch, n_heads, max_seq, head_dim) * 4);
+}
+
+int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch, int32_t n_heads,
+                      int32_t max_seq, int32_t head_dim, const int32_t* d_len, const float* d_q, const float* d_a,
+                      float* d_o, float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+    if (dtype != DF_F32 && dtype != DF_BF16) return DF_ERR_DTYPE;
+    if (!d_k || !d_v || !d_len || !d_q || !d_o || !d_lse || !d_ws) return DF_ERR_NULL;
+    if (batch < 1 || n_heads < 1 || max_seq < 1 || (head_dim != 32 && head_dim != 64 && head_dim != 128))
+        return DF_ERR_SHAPE;
+    if (!aligned16(d_k) || !aligned16(d_v) || !aligned16(d_q) || (d_a && !aligned16(d_a)) ||
+        (uintptr_t)d_ws % kAlign)
+        return DF_ERR_ALIGN;
+    if (ws_bytes < df_attention_workspace_bytes(batch, n_heads, max_seq, head_dim)) return DF_ERR_WORKSPACE;
+    dfk::AttnArgs a{};
+    a.dtype = dtype; a.k = d_k; a.v = d_v; a.B = batch; a.H = n_heads; a.S_max = max_seq; a.Dh = head_dim;
+    a.q = d_q; a.a = d_a; a.nkeys = d_len; a.nkeys_add = 0; a.nflows = 2; a.part = reinterpret_cast<float*>(d_ws);
+    a.o_f32 = d_o; a.lse = d_lse; a.o_rows = nullptr;
+    timing_events(0, &a.ev_start, &a.ev_stop);
+    return dfk::attention(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+int df_device_status(void* d_ws, void* stream, int32_t* status_out) {
+    if (!d_ws || !status_out) return DF_ERR_NULL;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, d_ws, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return DF_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return DF_ERR_HIP;
+    const int32_t zero = 0;
+    if (hipMemcpyAsync(d_ws, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess) return DF_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return DF_ERR_HIP;
+    *status_out = v;
+    return DF_OK;
+}
+
+const char* df_status_str(int code) {
+    switch (code) {
+        case DF_OK: return "ok";
+        case DF_ERR_NULL: return "a required pointer is NULL";
+        case DF_ERR_SHAPE: return "unsupported or inconsistent sizes";
+        case DF_ERR_DTYPE: return "unknown or unsupported storage dtype";
+        case DF_ERR_ALIGN: return "misaligned pointer";
+        case DF_ERR_WORKSPACE: return "workspace too small";
+        case DF_ERR_KV_FULL: return "K/V cache full";
+        case DF_ERR_HIP: return "HIP launch error";
+        case DF_ERR_ARG: return "invalid argument";
+    }
+    return "unknown status code";
+}
+
+int df_timing_enable(int32_t kclass) {
+    if (kclass != 0) return DF_ERR_ARG;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.kclass = kclass;
+    g_timing.used = 0;
+    return DF_OK;
+}
+
+int df_timing_read(double* total_ms, int64_t* launches) {
+    if (!total_ms || !launches) return DF_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    double t = 0.0;
+    for (size_t i = 0; i < g_timing.used; ++i) {
+        if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return DF_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) return DF_ERR_HIP;
+        t += ms;
+    }
+    *total_ms = t;
+    *launches = (int64_t)g_timing.used;
+    g_timing.kclass = -1;
+    g_timing.used = 0;
+    return DF_OK;
+}
+
+}  // extern "C"

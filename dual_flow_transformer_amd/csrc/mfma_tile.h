@@ -1,0 +1,104 @@
+// Skinny-GEMM building blocks on gfx950 bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16), shared by the stacked-row GEMV and the MoE
+// expert kernels.
+//
+// Operand layout of one 16x16x32 product D = A B (A: 16 x 32, B: 32 x 16):
+// lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16] as
+// eight bf16 each, and receives D[4*(l/16) + r][l%16] in register r.
+// Here A is a 16-row tile of a weight matrix (each lane loads 16
+// contiguous bytes of one weight row) and B the transposed activation rows,
+// so D[i][j] = partial sum of weight row i with stacked row j.
+#pragma once
+
+#include "df_device.h"
+
+namespace dfk {
+namespace tile {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int RT = 2;           // 16-row weight tiles per workgroup
+constexpr int ROWS = 16 * RT;   // weight rows per workgroup
+
+// Stream k in [kbeg, kend) (multiple of 32*KU) through MFMAs for RT weight
+// tiles against the first `mtiles` activation tiles (wave-uniform).
+template <int MT, int KU>
+__device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const bf16_t* const (&xrow)[MT],
+                                         int mtiles, int kbeg, int kend, f32x4 (&acc)[RT][MT]) {
+    for (int k = kbeg; k < kend; k += 32 * KU) {
+        u32x4 a[RT][KU], bx[MT][KU];
+        #pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            #pragma unroll
+            for (int ku = 0; ku < KU; ++ku)
+                a[rt][ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[rt] + k + 32 * ku));
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            if (mt < mtiles) {
+                #pragma unroll
+                for (int ku = 0; ku < KU; ++ku)
+                    bx[mt][ku] = *reinterpret_cast<const u32x4*>(xrow[mt] + k + 32 * ku);
+            }
+        #pragma unroll
+        for (int ku = 0; ku < KU; ++ku)
+            #pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                #pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    if (mt < mtiles)
+                        acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a[rt][ku]), __builtin_bit_cast(bf16x8, bx[mt][ku]),
+                            acc[rt][mt], 0, 0, 0);
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void zero(f32x4 (&acc)[RT][MT]) {
+    #pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// Per-wave accumulators to LDS: red[w][rt][mt][r][lane].
+template <int MT>
+__device__ __forceinline__ void to_lds(float* red, int wv, int lane, const f32x4 (&acc)[RT][MT]) {
+    #pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) red[(((wv * RT + rt) * MT + mt) * 4 + r) * 64 + lane] = acc[rt][mt][r];
+}
+
+// Sum over the NW waves (in wave order) of output (weight row nl of the
+// workgroup, stacked row m).
+template <int MT>
+__device__ __forceinline__ float lds_sum(const float* red, int NW, int nl, int m) {
+    const int rt = nl >> 4, i = nl & 15, mt = m >> 4, j = m & 15;
+    const int idx = ((rt * MT + mt) * 4 + (i & 3)) * 64 + j + 16 * (i >> 2);
+    float s = 0.f;
+    for (int w = 0; w < NW; ++w) s += red[(size_t)w * RT * MT * 256 + idx];
+    return s;
+}
+
+inline int floor_pow2(int x) {
+    int r = 1;
+    while (r * 2 <= x) r *= 2;
+    return r;
+}
+
+// Waves per workgroup: about `target` waves over the grid, at most 16, K
+// divisible into equal 32*KU-multiples per wave, LDS within 128 KiB.
+inline int pick_waves(int n_wg, int K, int MT, int KU, int target) {
+    int nw = floor_pow2(target / (n_wg > 0 ? n_wg : 1) > 0 ? target / (n_wg > 0 ? n_wg : 1) : 1);
+    if (nw > 16) nw = 16;
+    if (nw > 64 / MT) nw = 64 / MT;
+    while (nw > 1 && (K % (nw * 32 * KU)) != 0) nw >>= 1;
+    return nw;
+}
+
+}  // namespace tile
+}  // namespace dfk

@@ -1,0 +1,239 @@
+// MoE MLP with router replay for the grouped decode step
+// (gist.science/es/paper/2608.12385, "Mecanismos Clave": in MoE models the
+// aux flow reuses the set of experts the primary router picked, applying
+// them with its own mixture weights).
+//
+// 1. moe_route (one workgroup): primary top-k per sequence (descending
+//    logit, ties to the lower expert id), softmax gates of both flows over
+//    the chosen ids, then a stable counting sort of the (sequence, rank)
+//    pairs by expert: offsets[E+1], perm (sorted slot -> pair), inv.
+// 2. moe_up: one workgroup per (expert, 32 rows of the expert FFN); the
+//    expert's stacked rows are the primary and aux rows of its pairs, so each
+//    touched expert's weights are read once for both flows; untouched experts
+//    exit without reading. Epilogue: GELU, then b coupling on the aux row.
+// 3. moe_down: same grouping over the expert's down projection.
+// 4. moe_combine: gate-weighted sum over the k ranks in rank order, c
+//    coupling on the aux output, residual add. Integer work (ids, offsets,
+//    perm) is exact; no atomics.
+#include <algorithm>
+
+#include "df_device.h"
+#include "df_internal.h"
+#include "mfma_tile.h"
+#include "../../include/dualflow.h"
+
+namespace dfk {
+namespace {
+
+using tile::f32x4;
+using tile::RT;
+using tile::ROWS;
+
+constexpr int kMaxK = 16;
+
+__global__ __launch_bounds__(256) void moe_route(const float* r, const float* r1_given, int B, int E, int k,
+                                                 int nflows, int32_t* ids, float* gates, int32_t* ids_out,
+                                                 int32_t* offsets, int32_t* perm, int32_t* inv) {
+    __shared__ int32_t s_ids[64 * kMaxK];
+    __shared__ int32_t s_cnt[1025];
+    const int tid = threadIdx.x;
+    if (tid < B) {
+        const int b = tid;
+        const float* r1 = r1_given ? r1_given + (size_t)b * E : r + (size_t)(2 * b) * E;
+        int sel[kMaxK];
+        float v1[kMaxK];
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            float bv = -INFINITY;
+            for (int e = 0; e < E; ++e) {
+                bool taken = false;
+                for (int q = 0; q < j; ++q) taken |= (sel[q] == e);
+                if (taken) continue;
+                const float v = r1[e];
+                if (best < 0 || v > bv) { best = e; bv = v; }
+            }
+            sel[j] = best;
+            v1[j] = bv;
+        }
+        // gates: softmax over the chosen ids, per flow
+        float mx = v1[0], s = 0.f;
+        for (int j = 1; j < k; ++j) mx = fmaxf(mx, v1[j]);
+        float e1[kMaxK];
+        for (int j = 0; j < k; ++j) { e1[j] = expf(v1[j] - mx); s += e1[j]; }
+        for (int j = 0; j < k; ++j) {
+            gates[((size_t)b * 2) * k + j] = e1[j] / s;
+            ids[(size_t)b * k + j] = sel[j];
+            s_ids[b * k + j] = sel[j];
+            if (ids_out) ids_out[(size_t)b * k + j] = sel[j];
+        }
+        if (nflows == 2) {
+            const float* r2 = r + (size_t)(2 * b + 1) * E;
+            float mx2 = r2[sel[0]], s2 = 0.f;
+            for (int j = 1; j < k; ++j) mx2 = fmaxf(mx2, r2[sel[j]]);
+            float e2[kMaxK];
+            for (int j = 0; j < k; ++j) { e2[j] = expf(r2[sel[j]] - mx2); s2 += e2[j]; }
+            for (int j = 0; j < k; ++j) gates[((size_t)b * 2 + 1) * k + j] = e2[j] / s2;
+        }
+    }
+    __syncthreads();
+    const int P = B * k;
+    for (int e = tid; e < E; e += blockDim.x) {
+        int c = 0;
+        for (int t = 0; t < P; ++t) c += (s_ids[t] == e);
+        s_cnt[e] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int e = 0; e < E; ++e) { const int c = s_cnt[e]; offsets[e] = acc; s_cnt[e] = acc; acc += c; }
+        offsets[E] = acc;
+    }
+    __syncthreads();
+    for (int t = tid; t < P; t += blockDim.x) {
+        const int e = s_ids[t];
+        int rank = 0;
+        for (int u = 0; u < t; ++u) rank += (s_ids[u] == e);
+        const int slot = s_cnt[e] + rank;
+        perm[slot] = t;
+        inv[t] = slot;
+    }
+}
+
+struct ExpParams {
+    const bf16_t* x;       // up: [2B][d] rows; down: g_rows [P][2][Fe]
+    const bf16_t* w;       // [E][N][K]
+    int N, K, k, nflows, kw;
+    const int32_t* offsets;
+    const int32_t* perm;
+    const float* cpl_b;
+    bf16_t* g_out;         // up: [P][2][Fe]
+    float* y_out;          // down: [P][2][d]
+    bool up;
+};
+
+// Stacked row m of an expert: slot s = off + m / nflows, flow f = m % nflows.
+template <int MT, int KU>
+__global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
+    extern __shared__ float red[];
+    const int e = blockIdx.y;
+    const int off = p.offsets[e], cnt = p.offsets[e + 1] - off;
+    if (cnt == 0) return;   // untouched expert: its weights are never read
+    const int M = cnt * p.nflows;
+    const int mtiles = min((M + 15) / 16, MT);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    const int n0 = blockIdx.x * ROWS;
+    const int li = lane & 15, lg = lane >> 4;
+    const bf16_t* W = p.w + (size_t)e * p.N * p.K;
+    const bf16_t* wrow[RT];
+    #pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int n = min(n0 + rt * 16 + li, p.N - 1);
+        wrow[rt] = W + (size_t)n * p.K + lg * 8;
+    }
+    // Several passes when one expert holds more than MT*16 stacked rows.
+    for (int mbase = 0; mbase < M; mbase += MT * 16) {
+        const int mt_here = min((M - mbase + 15) / 16, mtiles);
+        const bf16_t* xrow[MT];
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = min(mbase + mt * 16 + li, M - 1);
+            const int s = off + m / p.nflows, f = m - (m / p.nflows) * p.nflows;
+            size_t row;
+            if (p.up) row = (size_t)(2 * (p.perm[s] / p.k) + f);    // sequence b = pair / k
+            else row = (size_t)s * 2 + f;                         // g_rows[slot][flow]
+            xrow[mt] = p.x + row * p.K + lg * 8;
+        }
+        f32x4 acc[RT][MT];
+        tile::zero<MT>(acc);
+        tile::stream_k<MT, KU>(wrow, xrow, mt_here, wv * p.kw, (wv + 1) * p.kw, acc);
+        __syncthreads();
+        tile::to_lds<MT>(red, wv, lane, acc);
+        __syncthreads();
+        const int npairs = min(cnt - mbase / p.nflows, MT * 16 / p.nflows);
+        for (int t = threadIdx.x; t < ROWS * npairs; t += blockDim.x) {
+            const int nl = t % ROWS, q = t / ROWS;
+            const int n = n0 + nl;
+            if (n >= p.N) continue;
+            const int ml = q * p.nflows;   // local stacked row of the primary
+            const float y1 = tile::lds_sum<MT>(red, NW, nl, ml);
+            const float y2 = p.nflows == 2 ? tile::lds_sum<MT>(red, NW, nl, ml + 1) : 0.f;
+            const int s = off + mbase / p.nflows + q;
+            if (p.up) {
+                const float g1 = 0.5f * y1 * (1.0f + erff(y1 * 0.70710678118654752f));
+                p.g_out[((size_t)s * 2) * p.N + n] = df::f32_to_bf16(g1);
+                if (p.nflows == 2) {
+                    float g2 = 0.5f * y2 * (1.0f + erff(y2 * 0.70710678118654752f));
+                    g2 = fmaf(p.cpl_b[n], g1, g2);      // intermediate coupling b_l, per expert
+                    p.g_out[((size_t)s * 2 + 1) * p.N + n] = df::f32_to_bf16(g2);
+                }
+            } else {
+                p.y_out[((size_t)s * 2) * p.N + n] = y1;
+                if (p.nflows == 2) p.y_out[((size_t)s * 2 + 1) * p.N + n] = y2;
+            }
+        }
+    }
+}
+
+// y_f[b] = sum_j gate_f[b][j] * y(slot of (b, j))_f; y2 += c * y1; h += y.
+__global__ __launch_bounds__(256) void moe_combine(const float* y_rows, const float* gates, const int32_t* inv,
+                                                   const float* cpl_c, int d, int k, int nflows, float* h) {
+    const int b = blockIdx.x;
+    for (int n = threadIdx.x; n < d; n += blockDim.x) {
+        float y1 = 0.f, y2 = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const size_t s = inv[(size_t)b * k + j];
+            y1 = fmaf(gates[((size_t)b * 2) * k + j], y_rows[(s * 2) * d + n], y1);
+            if (nflows == 2) y2 = fmaf(gates[((size_t)b * 2 + 1) * k + j], y_rows[(s * 2 + 1) * d + n], y2);
+        }
+        h[(size_t)(2 * b) * d + n] += y1;
+        if (nflows == 2) {
+            if (cpl_c) y2 = fmaf(cpl_c[n], y1, y2);   // output coupling c_l
+            h[(size_t)(2 * b + 1) * d + n] += y2;
+        }
+    }
+}
+
+template <int MT>
+hipError_t launch_expert(ExpParams& p, int E, hipStream_t s) {
+    constexpr int KU = MT <= 2 ? 4 : 2;
+    const int nwg = (p.N + ROWS - 1) / ROWS;
+    const int nw = tile::pick_waves(nwg * E, p.K, MT, KU, 8192);
+    p.kw = p.K / nw;
+    const size_t lds = (size_t)nw * RT * MT * 256 * sizeof(float);
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_expert<MT, KU>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((moe_expert<MT, KU>), dim3(nwg, E), dim3(64 * nw), lds, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t moe(const MoeArgs& a, hipStream_t s) {
+    if (a.k > kMaxK || a.B > 64 || a.E > 1024 || a.dtype != DF_BF16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_route, dim3(1), dim3(256), 0, s, a.r, a.r1_given, a.B, a.E, a.k, a.nflows, a.ids,
+                       a.gates, a.ids_out, a.offsets, a.perm, a.inv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ExpParams up;
+    up.x = reinterpret_cast<const bf16_t*>(a.x);
+    up.w = reinterpret_cast<const bf16_t*>(a.w_up);
+    up.N = a.Fe; up.K = a.d; up.k = a.k; up.nflows = a.nflows; up.offsets = a.offsets; up.perm = a.perm;
+    up.cpl_b = a.cpl_b; up.g_out = reinterpret_cast<bf16_t*>(a.g_rows); up.y_out = nullptr; up.up = true;
+    e = launch_expert<2>(up, a.E, s);
+    if (e != hipSuccess) return e;
+    ExpParams dn = up;
+    dn.x = reinterpret_cast<const bf16_t*>(a.g_rows);
+    dn.w = reinterpret_cast<const bf16_t*>(a.w_down);
+    dn.N = a.d; dn.K = a.Fe; dn.g_out = nullptr; dn.y_out = a.y_rows; dn.up = false;
+    e = launch_expert<2>(dn, a.E, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(256), 0, s, a.y_rows, a.gates, a.inv, a.cpl_c, a.d, a.k,
+                       a.nflows, a.h);
+    return hipGetLastError();
+}
+
+}  // namespace dfk

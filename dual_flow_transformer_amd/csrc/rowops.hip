@@ -1,0 +1,220 @@
+// Row-wise kernels of the decode step: token + position embedding with the
+// first LayerNorm, LayerNorm of the stacked residual rows, the explicit K/V
+// write, the length update, and the mixture head.
+#include "df_device.h"
+#include "df_internal.h"
+#include "../../include/dualflow.h"
+
+namespace dfk {
+namespace {
+
+constexpr int kRowThreads = 256;
+constexpr int kMaxPerThread = 16;   // d <= 4096
+
+// LayerNorm of one row held in registers (x[e] is element tid + e*256).
+template <typename T>
+__device__ void ln_store(const float (&x)[kMaxPerThread], int d, const float* g, float eps, T* out,
+                         float* red) {
+    const int tid = threadIdx.x;
+    float s = 0.f;
+    #pragma unroll
+    for (int e = 0; e < kMaxPerThread; ++e) {
+        const int i = tid + e * kRowThreads;
+        if (i < d) s += x[e];
+    }
+    const float mean = df::block_sum(s, red) / (float)d;
+    float v = 0.f;
+    #pragma unroll
+    for (int e = 0; e < kMaxPerThread; ++e) {
+        const int i = tid + e * kRowThreads;
+        if (i < d) { const float t = x[e] - mean; v = fmaf(t, t, v); }
+    }
+    const float var = df::block_sum(v, red) / (float)d;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    #pragma unroll
+    for (int e = 0; e < kMaxPerThread; ++e) {
+        const int i = tid + e * kRowThreads;
+        if (i < d) df::St<T>::st(out, i, (x[e] - mean) * rstd * g[i]);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
+    const T* emb0, const T* emb1, const T* pos_emb, const int32_t* tok, int tok_stride,
+    const int32_t* len, int d, int S_max, int V, int nflows, const float* g, float eps, float* h, T* x,
+    int32_t* status) {
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    int pos = len[b];
+    pos = pos < 0 ? 0 : (pos >= S_max ? S_max - 1 : pos);
+    int t = tok[(size_t)b * tok_stride];
+    if (t < 0 || t >= V) {          // out-of-range token id: clamp and flag
+        if (status && threadIdx.x == 0) status[0] |= 2;
+        t = t < 0 ? 0 : V - 1;
+    }
+    for (int f = 0; f < nflows; ++f) {
+        const T* e = (f == 0 ? emb0 : emb1) + (size_t)t * d;
+        const T* pe = pos_emb + (size_t)pos * d;
+        const size_t row = (size_t)(2 * b + f) * d;
+        float xv[kMaxPerThread];
+        #pragma unroll
+        for (int k = 0; k < kMaxPerThread; ++k) {
+            const int i = threadIdx.x + k * kRowThreads;
+            xv[k] = 0.f;
+            if (i < d) {
+                xv[k] = df::St<T>::ld(e, i) + df::St<T>::ld(pe, i);
+                h[row + i] = xv[k];
+            }
+        }
+        ln_store<T>(xv, d, g, eps, x + row, red);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void ln_rows_kernel(const float* h, const float* g, float eps,
+                                                              int d, int nflows, T* x) {
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    for (int f = 0; f < nflows; ++f) {
+        const size_t row = (size_t)(2 * b + f) * d;
+        float xv[kMaxPerThread];
+        #pragma unroll
+        for (int k = 0; k < kMaxPerThread; ++k) {
+            const int i = threadIdx.x + k * kRowThreads;
+            xv[k] = i < d ? h[row + i] : 0.f;
+        }
+        ln_store<T>(xv, d, g, eps, x + row, red);
+    }
+}
+
+template <typename T>
+__global__ void kv_append_kernel(T* k, T* v, int H, int S_max, int Dh, const int32_t* pos,
+                                 const float* dk, const float* dv, int32_t* status) {
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const int p = pos[b];
+    if (p < 0 || p >= S_max) {
+        if (status && threadIdx.x == 0) status[0] |= 1;
+        return;
+    }
+    for (int i = threadIdx.x; i < Dh; i += blockDim.x) {
+        const size_t dst = ((size_t)bh * S_max + p) * Dh + i;
+        df::St<T>::st(k, dst, dk[(size_t)bh * Dh + i]);
+        df::St<T>::st(v, dst, dv[(size_t)bh * Dh + i]);
+    }
+}
+
+__global__ void len_add_kernel(int32_t* len, int B, int inc) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) len[b] += inc;
+}
+
+// Mixture head: one block of 1024 threads per sequence.
+__global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int V, int aux_on,
+                                                        float* p_mix, float* alpha, int32_t* next_tok) {
+    __shared__ float red[16];
+    __shared__ float bv[16];
+    __shared__ int bi[16];
+    const int b = blockIdx.x;
+    const float* l1 = logits + (size_t)b * 2 * V;
+    const float* l2 = l1 + V;
+    float mx1 = -INFINITY, mx2 = -INFINITY;
+    for (int v = threadIdx.x; v < V; v += blockDim.x) {
+        mx1 = fmaxf(mx1, l1[v]);
+        if (aux_on) mx2 = fmaxf(mx2, l2[v]);
+    }
+    mx1 = df::block_max(mx1, red);
+    if (aux_on) mx2 = df::block_max(mx2, red);
+    float s1 = 0.f, c1 = 0.f, s2 = 0.f;
+    for (int v = threadIdx.x; v < V; v += blockDim.x) {
+        const float e1 = __builtin_amdgcn_exp2f((l1[v] - mx1) * df::kLog2e);
+        s1 += e1;
+        c1 = fmaf(e1, e1, c1);
+        if (aux_on) s2 += __builtin_amdgcn_exp2f((l2[v] - mx2) * df::kLog2e);
+    }
+    s1 = df::block_sum(s1, red);
+    c1 = df::block_sum(c1, red);
+    if (aux_on) s2 = df::block_sum(s2, red);
+    float a = 1.f;
+    if (aux_on) a = fminf(1.f, fmaxf(0.5f, c1 / (s1 * s1)));
+    const float w1 = a / s1;
+    const float w2 = aux_on ? (1.f - a) / s2 : 0.f;
+    float best = -1.f;
+    int besti = 0x7fffffff;
+    float* out = p_mix + (size_t)b * V;
+    for (int v = threadIdx.x; v < V; v += blockDim.x) {
+        float p = __builtin_amdgcn_exp2f((l1[v] - mx1) * df::kLog2e) * w1;
+        if (aux_on) p = fmaf(__builtin_amdgcn_exp2f((l2[v] - mx2) * df::kLog2e), w2, p);
+        out[v] = p;
+        if (p > best) { best = p; besti = v; }
+    }
+    // argmax: larger value wins, equal values take the lower index
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(besti, o, 64);
+        if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { bv[w] = best; bi[w] = besti; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float bb = bv[0];
+        int ii = bi[0];
+        for (int k = 1; k < (int)(blockDim.x >> 6); ++k)
+            if (bv[k] > bb || (bv[k] == bb && bi[k] < ii)) { bb = bv[k]; ii = bi[k]; }
+        if (next_tok) next_tok[b] = ii;
+        alpha[b] = a;
+    }
+}
+
+}  // namespace
+
+hipError_t mix_head(const float* logits, int B, int V, int aux_on, float* p_mix, float* alpha,
+                    int32_t* next_tok, hipStream_t s) {
+    hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, logits, V, aux_on, p_mix, alpha, next_tok);
+    return hipGetLastError();
+}
+
+hipError_t kv_append(int dtype, void* k, void* v, int B, int H, int S_max, int Dh, const int32_t* pos,
+                     const float* dk, const float* dv, int32_t* status, hipStream_t s) {
+    const int threads = Dh < 64 ? 64 : Dh;
+    if (dtype == DF_BF16)
+        hipLaunchKernelGGL(kv_append_kernel<bf16_t>, dim3(B * H), dim3(threads), 0, s, (bf16_t*)k, (bf16_t*)v,
+                           H, S_max, Dh, pos, dk, dv, status);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<float>, dim3(B * H), dim3(threads), 0, s, (float*)k, (float*)v,
+                           H, S_max, Dh, pos, dk, dv, status);
+    return hipGetLastError();
+}
+
+hipError_t len_add(int32_t* len, int B, int inc, hipStream_t s) {
+    hipLaunchKernelGGL(len_add_kernel, dim3((B + 63) / 64), dim3(64), 0, s, len, B, inc);
+    return hipGetLastError();
+}
+
+hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* pos_emb, const int32_t* tok,
+                    int tok_stride, const int32_t* len, int B, int d, int S_max, int V, int nflows, const float* g,
+                    float eps, float* h, void* x, int32_t* status, hipStream_t s) {
+    if (dtype == DF_BF16)
+        hipLaunchKernelGGL(embed_ln_kernel<bf16_t>, dim3(B), dim3(kRowThreads), 0, s, (const bf16_t*)emb0,
+                           (const bf16_t*)emb1, (const bf16_t*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
+                           g, eps, h, (bf16_t*)x, status);
+    else
+        hipLaunchKernelGGL(embed_ln_kernel<float>, dim3(B), dim3(kRowThreads), 0, s, (const float*)emb0,
+                           (const float*)emb1, (const float*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
+                           g, eps, h, (float*)x, status);
+    return hipGetLastError();
+}
+
+hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps, int B, int d, int nflows,
+                           void* x, hipStream_t s) {
+    if (dtype == DF_BF16)
+        hipLaunchKernelGGL(ln_rows_kernel<bf16_t>, dim3(B), dim3(kRowThreads), 0, s, h, g, eps, d, nflows,
+                           (bf16_t*)x);
+    else
+        hipLaunchKernelGGL(ln_rows_kernel<float>, dim3(B), dim3(kRowThreads), 0, s, h, g, eps, d, nflows,
+                           (float*)x);
+    return hipGetLastError();
+}
+
+}  // namespace dfk

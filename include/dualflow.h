@@ -1,0 +1,203 @@
+/*
+ * dualflow.h - C ABI of the Dual-Flow Transformer grouped decode step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2608.12385, "Dual-Flow Transformers: Decoupling the
+ * Primary Prefill Path from Additional Decode Computation"; summarised on
+ * gist.science/es/paper/2608.12385, "Resumen Tecnico: Dual-Flow
+ * Transformers"): a primary flow, a standard causal Transformer, owns the
+ * single persistent K/V cache; an auxiliary flow with its own token
+ * embedding runs only from the last prompt position on, shares every
+ * attention, MLP and output matrix, couples one way to the primary through
+ * per-layer vectors a_l (query), b_l (MLP intermediate) and c_l (MLP
+ * output), attends the primary K/V and never writes it; the two output
+ * distributions are mixed as p_mix = alpha p_primary + (1 - alpha) p_aux
+ * with alpha from the primary's collision probability, at least 0.5; in MoE
+ * models the aux flow replays the primary's expert choice with its own gates
+ * (section "Mecanismos Clave"). Decode groups both flows so every weight and
+ * K/V region is read once (section "Costes de Inferencia vs.
+ * Entrenamiento").
+ *
+ * Conventions for every entry point:
+ *  - Pointers prefixed d_ are device memory owned by the caller; host structs
+ *    (df_config, df_weights, df_kv) are read during the call only.
+ *  - The library never allocates device memory. Scratch space is the
+ *    caller's workspace (d_ws, ws_bytes), sized by the *_workspace_bytes
+ *    queries, 256-byte aligned. A decode workspace must be zero-filled
+ *    before its first use (its first word is the device status word).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream) and returns DF_OK or a negative DF_ERR_* code. Host-side
+ *    argument checks run before anything is launched; a failed check
+ *    launches nothing. DF_ERR_HIP reports a launch error (the HIP error is
+ *    left for the caller to read with hipGetLastError).
+ *  - Storage dtype (weights, embeddings, K/V): DF_F32 or DF_BF16. Coupling
+ *    vectors and LayerNorm gains are always fp32. Arithmetic is fp32 with
+ *    fp32 accumulation; with DF_BF16 every projection input is rounded to
+ *    bf16 (nearest-even), as are appended K/V entries.
+ *  - Stacked rows: row 2b is the primary flow of sequence b, row 2b+1 its
+ *    aux flow ([B][2][...] layouts below).
+ *  - Results are deterministic: no atomics take part in any reduction.
+ */
+#ifndef DUALFLOW_H
+#define DUALFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DF_OK = 0,
+    DF_ERR_NULL = -1,       /* a required pointer is NULL */
+    DF_ERR_SHAPE = -2,      /* a size is out of range or unsupported */
+    DF_ERR_DTYPE = -3,      /* unknown storage dtype */
+    DF_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned (workspace: 256) */
+    DF_ERR_WORKSPACE = -5,  /* workspace smaller than the query returns */
+    DF_ERR_KV_FULL = -6,    /* a write position would be >= max_seq */
+    DF_ERR_HIP = -7,        /* a HIP launch failed */
+    DF_ERR_ARG = -8         /* another invalid argument */
+};
+
+enum { DF_F32 = 0, DF_BF16 = 1 };
+
+/* Model and batch sizes. n_experts == 0 selects the dense MLP (width ffn);
+ * n_experts > 0 selects the MoE MLP (top_k experts of width expert_ffn).
+ * Supported: head_dim in {32, 64, 128}; d_model == n_heads * head_dim;
+ * with DF_BF16, d_model, ffn and expert_ffn multiples of 256 and vocab and
+ * n_experts multiples of 16; batch <= 64 (stacked rows 2*batch <= 128). */
+typedef struct df_config {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_heads;
+    int32_t head_dim;
+    int32_t ffn;
+    int32_t vocab;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t expert_ffn;
+    int32_t batch;
+    int32_t max_seq;     /* cache capacity (positions) = rows of pos_emb */
+    int32_t dtype;       /* DF_F32 or DF_BF16 */
+    float ln_eps;        /* LayerNorm epsilon */
+} df_config;
+
+/* Parameters, all device pointers, row-major, layer-major stacks.
+ * Projection matrices are [out][in] (a GEMV reads whole rows). */
+typedef struct df_weights {
+    const void* tok_emb[2];    /* [vocab][d]: primary (0), aux (1) */
+    const void* pos_emb;       /* [max_seq][d], shared by both flows */
+    const float* ln1;          /* [L][d]  gain of the norm before attention */
+    const float* ln2;          /* [L][d]  gain of the norm before the MLP */
+    const float* lnf;          /* [d]     final norm gain */
+    const void* w_qkv;         /* [L][3d][d]: rows Q (h*Dh+i), then K, then V */
+    const void* w_o;           /* [L][d][d] */
+    const void* w_up;          /* [L][ffn][d]          (dense) */
+    const void* w_down;        /* [L][d][ffn]          (dense) */
+    const void* w_router;      /* [L][E][d]            (MoE) */
+    const void* w_exp_up;      /* [L][E][expert_ffn][d] (MoE) */
+    const void* w_exp_down;    /* [L][E][d][expert_ffn] (MoE) */
+    const float* cpl_a;        /* [L][d]   query coupling a_l */
+    const float* cpl_b;        /* [L][ffn or expert_ffn]  intermediate coupling b_l */
+    const float* cpl_c;        /* [L][d]   output coupling c_l */
+    const void* w_out;         /* [vocab][d] LM head */
+} df_weights;
+
+/* The single persistent K/V cache, written by the primary flow only.
+ * k, v: [L][batch][n_heads][max_seq][head_dim] in the storage dtype.
+ * len: [batch] int32, positions filled so far (the next write position). */
+typedef struct df_kv {
+    void* k;
+    void* v;
+    int32_t* len;
+} df_kv;
+
+/* Bytes of workspace df_decode_step and df_prefill_primary need. */
+size_t df_workspace_bytes(const df_config* cfg);
+
+/* One grouped decode step, both flows (gist.science/es/paper/2608.12385,
+ * sections "Arquitectura Central" and "Mecanismos Clave").
+ *  d_tokens [batch]: token of each sequence at position len[b].
+ *  aux_on: 1 = dual step; 0 = primary-only step (p_mix = p_primary,
+ *    alpha = 1; the primary numerics are bitwise those of a dual step).
+ *  d_router_logits [L][batch][n_experts] or NULL: MoE only, primary router
+ *    logits supplied by the caller (replacing the primary router output);
+ *    NULL computes them from w_router.
+ *  d_logits [batch][2][vocab] or NULL: raw logits of both flows (fp32).
+ *  d_p_mix [batch][vocab], d_alpha [batch]: the mixture output.
+ *  d_next_tok [batch] or NULL: argmax of p_mix, ties to the lowest id.
+ *  d_expert_ids [L][batch][top_k] or NULL: MoE expert ids of the primary
+ *    (replayed by the aux flow), by descending logit, ties to the lower id.
+ * Appends the primary K/V at len[b] in every layer, then len[b] += 1 (on
+ * the device). A sequence whose len[b] >= max_seq is not written and is
+ * flagged in the device status (df_device_status). */
+int df_decode_step(const df_config* cfg, const df_weights* w, const df_kv* kv,
+                   const int32_t* d_tokens, int32_t aux_on, const float* d_router_logits,
+                   float* d_logits, float* d_p_mix, float* d_alpha, int32_t* d_next_tok,
+                   int32_t* d_expert_ids, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Primary-only prefill of T tokens per sequence (d_tokens [batch][T]) at
+ * positions len[b] .. len[b]+T-1; the aux flow is skipped in prefill
+ * (section "Arquitectura Central"). Advances len[b] by T. Runs the same
+ * kernels as a primary-only decode step, one position at a time. */
+int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* kv,
+                       const int32_t* d_tokens, int32_t T, void* d_ws, size_t ws_bytes,
+                       void* stream);
+
+/* Write K/V entries of one layer at explicit positions: for each sequence b
+ * and head h, k[layer][b][h][d_pos[b]][:] = round(d_k[b][h][:]) (same for v),
+ * d_k, d_v fp32 [batch][n_heads][head_dim], rounded to the storage dtype.
+ * The decode step fuses this write into its QKV projection. Positions
+ * outside [0, max_seq) are skipped and flagged in d_status (int32, may be
+ * NULL). */
+int df_kv_append(const df_config* cfg, const df_kv* kv, int32_t layer, const int32_t* d_pos,
+                 const float* d_k, const float* d_v, int32_t* d_status, void* stream);
+
+/* The mixture head alone (section "Mecanismos Clave", mixture objective):
+ * d_logits [batch][2][vocab] fp32. p_f = softmax(logits_f) over the whole
+ * vocabulary; alpha = min(1, max(0.5, sum_v p_primary(v)^2));
+ * p_mix = alpha p_primary + (1 - alpha) p_aux. aux_on = 0: alpha = 1 and
+ * p_mix = p_primary (aux logits not read). d_next_tok may be NULL. */
+int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t aux_on,
+                float* d_p_mix, float* d_alpha, int32_t* d_next_tok, void* stream);
+
+/* Asymmetric shared-K/V attention alone (section "Mecanismos Clave"): for
+ * each sequence b and head h both queries attend cache positions
+ * 0 .. d_len[b]-1 of the one cache, which is read once for both.
+ *  d_k, d_v: [batch][n_heads][max_seq][head_dim] (one layer), storage dtype.
+ *  d_q: [batch][2][n_heads][head_dim] fp32, flow 0 = Q1, flow 1 = Q2raw.
+ *  d_a: [n_heads*head_dim] or NULL: if given Q2 = Q2raw + a * Q1.
+ *  d_o: [batch][2][n_heads][head_dim] fp32 outputs; d_lse: [batch][2][n_heads]
+ *  natural-log sum of exp of the scaled scores. Scores are q.k/sqrt(head_dim).
+ *  d_len[b] must lie in [1, max_seq]. */
+int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch,
+                      int32_t n_heads, int32_t max_seq, int32_t head_dim, const int32_t* d_len,
+                      const float* d_q, const float* d_a, float* d_o, float* d_lse,
+                      void* d_ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes df_attention_dual needs for these sizes. */
+size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_seq, int32_t head_dim);
+
+/* Reads and clears the device status word kept in a decode workspace
+ * (bit 0: a K/V write was skipped because len >= max_seq; bit 1: a token
+ * id outside [0, vocab) was clamped). Synchronises
+ * `stream`. */
+int df_device_status(void* d_ws, void* stream, int32_t* status_out);
+
+/* Text of a DF_* return code. */
+const char* df_status_str(int code);
+
+/* Kernel timing with HIP events on the launching stream. While enabled,
+ * every launch of the kernels of class `kclass` (0 = attention partial
+ * pass) is bracketed by a pair of events. df_timing_read synchronises
+ * them and returns the summed duration (ms) and the launch count, then
+ * disables timing. At most 65536 launches are recorded. */
+int df_timing_enable(int32_t kclass);
+int df_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUALFLOW_H */

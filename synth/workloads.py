@@ -126,11 +126,11 @@ class Inputs:
         return np.stack([normal((c.d,), c.seed, sid, c.sigma_w, c.dtype, offset=int(t) * c.d)
                          for t in tokens])
 
-    def pos_emb(self, rows=None) -> np.ndarray:
+    def pos_emb(self, rows=None, n_rows=None) -> np.ndarray:
         c = self.cfg
         sid = stream_id("pos_emb")
         if rows is None:
-            return normal((c.S_max, c.d), c.seed, sid, c.sigma_w, c.dtype)
+            return normal((n_rows or c.S_max, c.d), c.seed, sid, c.sigma_w, c.dtype)
         return np.stack([normal((c.d,), c.seed, sid, c.sigma_w, c.dtype, offset=int(p) * c.d) for p in rows])
 
     # -- per-layer parameters ---------------------------------------------------

@@ -1,0 +1,192 @@
+"""The grouped decode step on the GPU (df_decode_step, df_prefill_primary)
+against the oracle, teacher-forced on the same tokens.
+
+Bars (fp32 accumulation on the GPU, float64 in the oracle): logits within
+2e-2 max-abs, p_mix within 1e-3 max-abs; K/V write positions bit-exact
+(sentinel-filled cache); appended bf16 values within one bf16 ulp; MoE
+expert ids bit-exact. Invariants the pages state hold bitwise on the GPU:
+the primary flow and the cache do not depend on the aux flow; with a = b =
+c = 0 and tied embeddings the aux flow equals the primary flow."""
+import numpy as np
+import pytest
+import torch
+
+from dual_flow_transformer_amd.runtime import DecodeModel
+from gpu_util import argmax_agrees, bits_to_f64, max_abs, say
+from oracle import dualflow as odf
+from synth.workloads import C1_TINY, Config, Inputs
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = Config("gpu_small_bf16", L=2, d=256, H=2, Dh=128, F=1024, V=512, B=3, ctx=300, S_max=320,
+                    dtype="bf16", seed=21, sigma_w=0.05, sigma_ln=0.1)
+SMALL_F32 = Config("gpu_small_f32", L=2, d=128, H=2, Dh=64, F=256, V=300, B=2, ctx=40, S_max=64,
+                   dtype="f32", seed=22, sigma_w=0.05, sigma_ln=0.1)
+SMALL_MOE = Config("gpu_small_moe", L=2, d=256, H=2, Dh=128, F=0, V=512, B=8, ctx=40, S_max=64, dtype="bf16",
+                   moe=True, E=16, top_k=4, Fe=256, router_override=True, seed=23, sigma_w=0.05, sigma_ln=0.1)
+LOGIT_TOL, PMIX_TOL = 2e-2, 1e-3
+
+
+def _compare_step(cfg, gm: DecodeModel, r: odf.StepResult, aux_on=True):
+    lg = gm.logits.cpu().numpy()
+    pm = gm.p_mix.cpu().numpy()
+    al = gm.alpha.cpu().numpy()
+    nt = gm.next_tok.cpu().numpy()
+    flows = 2 if aux_on else 1
+    el = max_abs(lg[:, :flows], r.logits[:, :flows])
+    ep = max_abs(pm, r.p_mix)
+    ea = max_abs(al, r.alpha)
+    kl = float(np.max(np.sum(r.p_mix * (np.log(np.maximum(r.p_mix, 1e-30)) - np.log(np.maximum(pm, 1e-30))), -1)))
+    say(f"  logits max|d|={el:.3e} p_mix max|d|={ep:.3e} alpha max|d|={ea:.3e} KL={kl:.2e}")
+    assert el < LOGIT_TOL and ep < PMIX_TOL and ea < PMIX_TOL
+    for b in range(cfg.B):
+        assert argmax_agrees(pm[b], r.p_mix[b], nt[b], margin=2e-3)
+    return el, ep
+
+
+def _sentinel(gm: DecodeModel, cfg):
+    s = 0x4242 if cfg.dtype == "bf16" else 12345.0
+    gm.k[:, :, :, cfg.ctx:] = s
+    gm.v[:, :, :, cfg.ctx:] = s
+    return s
+
+
+def _check_writes(gm, cfg, lens0, cache: odf.Cache, sentinel):
+    for name, t in (("k", gm.k), ("v", gm.v)):
+        a = t.cpu().numpy()
+        sv = np.int16(sentinel) if cfg.dtype == "bf16" else np.float32(sentinel)
+        changed = np.any(a[:, :, :, cfg.ctx:] != sv, axis=-1)
+        want = np.zeros_like(changed)
+        for b in range(cfg.B):
+            want[:, b, :, lens0[b] - cfg.ctx] = True
+        assert np.array_equal(changed, want), f"{name} cache write positions differ"
+        for l in range(cfg.L):
+            for b in range(cfg.B):
+                got = bits_to_f64(t[l, b, :, lens0[b]], cfg.dtype)
+                ref = cache.appended[(l, b, int(lens0[b]))][0 if name == "k" else 1]
+                ulp = 2.0 ** -7 if cfg.dtype == "bf16" else 2.0 ** -20
+                assert np.all(np.abs(got - ref) <= ulp * np.abs(ref) + 1e-6), f"{name} values l={l} b={b}"
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_F32], ids=lambda c: c.name)
+def test_small_dense_steps(cfg):
+    say(f"decode case {cfg.name}")
+    gm = DecodeModel(cfg, fill="host")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    s = _sentinel(gm, cfg)
+    for step in range(2):
+        lens0 = gm.len.cpu().numpy().copy()
+        tok = src.step_tokens(step)
+        gm.decode_step(gm.tokens(tok))
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True)
+        say(f" step {step}")
+        _compare_step(cfg, gm, r)
+        if step == 0:
+            _check_writes(gm, cfg, lens0, cache, s)
+    assert np.array_equal(gm.len.cpu().numpy(), cache.lens)
+    assert gm.status() == 0
+
+
+def test_device_fill_matches_host_generator():
+    for cfg in (SMALL_BF16, SMALL_MOE, SMALL_F32):
+        say(f"fill check {cfg.name}")
+        a = DecodeModel(cfg, fill="device")
+        b = DecodeModel(cfg, fill="host")
+        for name in ("tok_emb", "pos_emb", "w_qkv", "w_o", "w_up", "w_down", "w_router", "w_eup", "w_edown",
+                     "w_out", "k", "v"):
+            x, y = getattr(a, name), getattr(b, name)
+            if x is None:
+                continue
+            if isinstance(x, list):
+                assert all(torch.equal(p, q) for p, q in zip(x, y)), name
+            else:
+                assert torch.equal(x, y), name
+
+
+def test_tiny_fp32_end_to_end():
+    """Prefill 62 prompt tokens (primary only), then 16 dual steps from the
+    last prompt position, teacher-forced on the oracle's greedy tokens."""
+    cfg = C1_TINY
+    say("tiny end-to-end")
+    m = odf.Model(Inputs(cfg))
+    cache, res = odf.run_tiny(m)
+    prompt = Inputs(cfg).prompt()
+    gm = DecodeModel(cfg, fill="host")
+    gm.len.zero_()
+    gm.prefill(gm.tokens(prompt[:, :-1]).contiguous())
+    tok = prompt[:, -1]
+    for s, r in enumerate(res):
+        gm.decode_step(gm.tokens(tok))
+        torch.cuda.synchronize()
+        say(f" step {s}")
+        _compare_step(cfg, gm, r)
+        tok = r.next_tok
+    assert int(gm.len[0].item()) == cfg.prompt_len + cfg.n_steps - 1
+    # the whole cache (prefill and decode entries)
+    n = int(cache.lens[0])
+    for l in range(cfg.L):
+        K, V = cache.layer(l)
+        assert max_abs(gm.k[l, :, :, :n].cpu().numpy(), K[:, :, :n]) < 1e-4
+        assert max_abs(gm.v[l, :, :, :n].cpu().numpy(), V[:, :, :n]) < 1e-4
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_MOE], ids=lambda c: c.name)
+def test_primary_independent_of_aux(cfg):
+    """Primary logits and every cache byte are bitwise the same with the aux
+    flow on or off (the aux flow never feeds back and never writes K/V)."""
+    say(f"aux on/off {cfg.name}")
+    src = Inputs(cfg)
+    a = DecodeModel(cfg, fill="device")
+    b = DecodeModel(cfg, fill="device")
+    for step in range(2):
+        tok = src.step_tokens(step)
+        rl = a.router_logits(step) if cfg.moe else None
+        a.decode_step(a.tokens(tok), aux_on=True, router_logits=rl)
+        b.decode_step(b.tokens(tok), aux_on=False, router_logits=rl)
+        torch.cuda.synchronize()
+        assert torch.equal(a.logits[:, 0], b.logits[:, 0])
+        if cfg.moe:
+            assert torch.equal(a.expert_ids, b.expert_ids)
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+    assert torch.equal(b.alpha, torch.ones_like(b.alpha))
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_MOE], ids=lambda c: c.name)
+def test_tied_zero_coupling_aux_equals_primary(cfg):
+    say(f"tied + zero coupling {cfg.name}")
+    c = cfg.replace(tie_emb=True, zero_cpl=True)
+    gm = DecodeModel(c, fill="device")
+    gm.decode_step(gm.tokens(Inputs(c).step_tokens(0)), aux_on=True, router_logits=None)
+    torch.cuda.synchronize()
+    assert torch.equal(gm.logits[:, 0], gm.logits[:, 1])
+
+
+def test_deterministic():
+    cfg = SMALL_BF16
+    outs = []
+    for _ in range(2):
+        gm = DecodeModel(cfg, fill="device")
+        gm.decode_step(gm.tokens(Inputs(cfg).step_tokens(0)))
+        torch.cuda.synchronize()
+        outs.append((gm.logits.clone(), gm.p_mix.clone(), gm.k.clone()))
+    assert all(torch.equal(x, y) for x, y in zip(*outs))
+
+
+def test_small_moe_router_replay():
+    cfg = SMALL_MOE
+    say("moe small")
+    gm = DecodeModel(cfg, fill="host")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    for step in range(2):
+        tok = src.step_tokens(step)
+        rl = gm.router_logits(step)
+        gm.decode_step(gm.tokens(tok), router_logits=rl)
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True, router_logits=rl.cpu().numpy())
+        assert np.array_equal(gm.expert_ids.cpu().numpy(), r.ids), "expert ids differ"
+        _compare_step(cfg, gm, r)
