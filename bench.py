@@ -1,0 +1,227 @@
+"""Dual-flow grouped decode benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c5|c3|c4]
+
+A step is one grouped decode step of the whole model (every layer, the LM
+head and the mixture head) for all B sequences, both flows. Inputs are seeded
+synthetic tensors of the workload's shapes, already resident in HBM when the
+timed region starts; each step decodes greedily from the previous step's
+mixture argmax, so the context grows by one position per step. Prints one
+JSON line: decode tokens/s, the roofline of the dominant kernel (the
+shared-K/V attention pass, timed with HIP events on its stream), the
+whole-step achieved bandwidth, the dual/primary byte and time ratios, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dual-flow decode tokens/s at 1 GPU; achieved HBM GB/s vs peak; dual/primary byte ratio"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", choices=["c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-primary-pass", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=0, help="oracle sample: layers (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, n_layers: int, min_seconds: float = 10.0):
+    """The CPU oracle as it stands, on a bounded sample: sequence 0 of the
+    workload through its first n_layers layers plus the LM head and mixture
+    head (inputs drawn and decoded before timing), repeated until at least
+    min_seconds of CPU work. Per-token time = layers scaled to the full depth
+    + head; value = tokens/s of one oracle instance."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dualflow as odf
+    from synth.workloads import Inputs
+
+    sub = cfg.replace(L=n_layers)
+    src = Inputs(sub)
+    model = odf.Model(src, keep_layers=True)
+    for l in range(n_layers):
+        model.layer(l)
+    model.w_out()
+    model.lnf()
+    cache = odf.Cache(sub, [0], src)
+    for l in range(n_layers):
+        cache.layer(l)
+    rl = None
+    if cfg.moe:
+        rl = np.stack([src.router_logits(0, l)[:1] for l in range(n_layers)])
+    tok = src.step_tokens(0)[:1]
+    # time the layers and the head separately: full-depth extrapolation
+    t_total, reps, t_head = 0.0, 0, 0.0
+    while t_total < min_seconds or reps < 1:
+        cache.lens[:] = cfg.ctx          # every repetition is the same step
+        t0 = time.perf_counter()
+        r = odf.decode_step(model, cache, tok, aux_on=True, router_logits=rl)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    h = np.zeros((1, 2, cfg.d))
+    t0 = time.perf_counter()
+    for i in range(reps):
+        for f in range(2):
+            odf._matvec(model.w_out(), odf.round_to(odf.layer_norm(h[0, f], model.lnf(), cfg.eps), cfg.dtype))
+        odf.mix_head(np.zeros(cfg.V), np.zeros(cfg.V))
+    t_head = (time.perf_counter() - t0) / reps
+    t_step = t_total / reps
+    t_layer = max(t_step - t_head, 1e-9) / n_layers
+    t_tok = t_layer * cfg.L + t_head
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": 1.0 / t_tok, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"sequence 0 of {cfg.B}, first {n_layers} of {cfg.L} layers + LM head + mixture head, "
+                       f"{reps} steps ({t_total:.1f} s); per-token time scaled to {cfg.L} layers"),
+            "seconds_per_token": t_tok, "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
+              "this build. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from dual_flow_transformer_amd import _abi
+    from dual_flow_transformer_amd.runtime import DecodeModel
+    from synth.workloads import PRESETS, Inputs
+
+    cfg = PRESETS[args.workload]
+    W, K = args.warmup, args.steps
+    S = cfg.ctx + W + K + 8
+    cfg = cfg.replace(S_max=S)
+    log(f"[bench] workload {cfg.name}: filling device inputs (S_max={S})")
+    t0 = time.time()
+    gm = DecodeModel(cfg, fill="device")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s; workspace {gm.ws_bytes / 2**20:.1f} MiB")
+    src = Inputs(cfg)
+    rls = None
+    if cfg.moe:
+        rls = [gm.router_logits(s) for s in range(W + K)]
+    tok0 = gm.tokens(src.step_tokens(0))
+    len0 = gm.len.clone()
+
+    def run(n, first, aux_on=True):
+        for i in range(n):
+            s = first + i
+            toks = tok0 if s == 0 else gm.next_tok
+            gm.decode_step(toks, aux_on=aux_on,
+                           router_logits=rls[s] if rls is not None else None, logits=False)
+
+    stream = torch.cuda.current_stream()
+    # warmup
+    run(W, 0)
+    torch.cuda.synchronize()
+    lens_start = gm.len.cpu().numpy().astype(np.int64)
+    # timed region: K dual steps
+    _abi.check(_abi.df_timing_enable(0), "df_timing_enable")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    run(K, W)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    rc, attn_ms, attn_n = _abi.df_timing_read()
+    _abi.check(rc, "df_timing_read")
+    ms = ev0.elapsed_time(ev1)
+    ms_step = ms / K
+    tok_s = cfg.B * K / (ms / 1e3)
+    status = gm.status()
+    log(f"[bench] {K} steps: {ms_step:.3f} ms/step (wall {wall / K * 1e3:.3f}), {tok_s:.1f} tok/s, status {status}")
+
+    # algorithmic bytes over the timed steps
+    es = 2 if cfg.dtype == "bf16" else 4
+    kv_attn = 0
+    for i in range(K):
+        keys = int((lens_start + i + 1).sum())
+        kv_attn += cfg.L * cfg.H * keys * cfg.Dh * es * 2
+    attn_bytes_per_launch = kv_attn / (K * cfg.L)
+    attn_avg_ms = attn_ms / max(attn_n, 1)
+    attn_gbs = attn_bytes_per_launch / (attn_avg_ms / 1e3) / 1e9
+    gm.len.copy_(torch.from_numpy(lens_start + K // 2).to(gm.len.device))
+    ab_dual = gm.algorithmic_bytes(aux_on=True)
+    ab_prim = gm.algorithmic_bytes(aux_on=False)
+    step_gbs = ab_dual["total"] / (ms_step / 1e3) / 1e9
+
+    prim_ms = None
+    if not args.no_primary_pass:
+        gm.len.copy_(len0)
+        run(W, 0, aux_on=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(K, W, aux_on=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        prim_ms = e0.elapsed_time(e1) / K
+        log(f"[bench] primary-only: {prim_ms:.3f} ms/step")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy of 1 GiB done")
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nl = args.cpu_layers or (2 if cfg.d >= 4096 else 4)
+        log(f"[bench] CPU oracle baseline on a sample ({nl} layers)")
+        del gm
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(cfg, nl)
+        log(f"[bench] oracle: {cpu['value']:.4f} tok/s ({cpu['seconds_per_token']:.2f} s/token)")
+
+    out = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded random-init weights, prefilled random K/V)",
+        "config": {"workload": cfg.name, "layers": cfg.L, "d_model": cfg.d, "heads": cfg.H, "head_dim": cfg.Dh,
+                   "ffn": cfg.F if not cfg.moe else None, "experts": cfg.E if cfg.moe else None,
+                   "top_k": cfg.top_k if cfg.moe else None, "expert_ffn": cfg.Fe if cfg.moe else None,
+                   "vocab": cfg.V, "global_batch": cfg.B, "context": cfg.ctx, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "attn_partial (shared-K/V dual-query attention, split-K pass)", "bound": "hbm",
+                     "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": attn_gbs / PEAK_HBM_GBS,
+                     "traffic": None, "avg_launch_ms": attn_avg_ms, "launches": attn_n,
+                     "algorithmic_bytes_per_launch": attn_bytes_per_launch},
+        "step_bandwidth": {"algorithmic_bytes": ab_dual["total"], "achieved_GBs": step_gbs,
+                           "frac": step_gbs / PEAK_HBM_GBS, "breakdown": ab_dual},
+        "byte_ratio": {"analytic_dual_over_primary": ab_dual["total"] / ab_prim["total"], "counter": None},
+        "primary_only_ms_per_step": prim_ms,
+        "dual_over_primary_time": (ms_step / prim_ms) if prim_ms else None,
+        "device_status": status,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,7 +27,7 @@ DF_BF16 = 1
 
 EXPORTS = ["df_workspace_bytes", "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
            "df_attention_dual", "df_attention_workspace_bytes", "df_device_status", "df_status_str",
-           "df_timing_enable", "df_timing_read"]
+           "df_timing_enable", "df_timing_read", "df_stacked_gemv", "df_stacked_gemv_workspace_bytes"]
 
 
 class df_config(ctypes.Structure):
@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.df_device_status.argtypes = [vp, vp, P(i32)]
         L.df_status_str.restype = ctypes.c_char_p
         L.df_status_str.argtypes = [ctypes.c_int]
+        L.df_stacked_gemv.restype = ctypes.c_int
+        L.df_stacked_gemv.argtypes = [i32, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+        L.df_stacked_gemv_workspace_bytes.restype = sz
+        L.df_stacked_gemv_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.df_timing_enable.restype = ctypes.c_int
         L.df_timing_enable.argtypes = [i32]
         L.df_timing_read.restype = ctypes.c_int
@@ -145,6 +149,14 @@ def df_device_status(d_ws, stream=0):
 
 def df_status_str(code: int) -> str:
     return lib().df_status_str(int(code)).decode()
+
+
+def df_stacked_gemv(dtype, d_x, d_w, rows, N, K, d_y, d_ws, ws_bytes, stream=0) -> int:
+    return lib().df_stacked_gemv(int(dtype), d_x, d_w, int(rows), int(N), int(K), d_y, d_ws, ws_bytes, stream)
+
+
+def df_stacked_gemv_workspace_bytes(dtype, rows, N, K) -> int:
+    return int(lib().df_stacked_gemv_workspace_bytes(int(dtype), int(rows), int(N), int(K)))
 
 
 def df_timing_enable(kclass: int = 0) -> int:

@@ -18,8 +18,28 @@ size_t elem_size(int dtype) { return dtype == DF_BF16 ? 2 : 4; }
 
 // Workspace regions (byte offsets from the workspace base).
 struct WsLayout {
-    size_t status, h, xd, xo, xf, q, part, logits, r, ids, gates, offsets, perm, inv, grows, yrows, total;
+    size_t status, h, xd, xo, xf, q, part, logits, r, ids, gates, offsets, perm, inv, grows, yrows, gpart, gcount,
+        total;
 };
+
+// Largest split-K partial buffer and row-block count over the model's GEMVs.
+void gemv_scratch(const df_config& c, size_t* part_floats, size_t* blocks) {
+    const bool moe = c.n_experts > 0;
+    const int d = c.d_model;
+    const int shapes[5][2] = {{3 * d, d}, {d, d}, {moe ? c.n_experts : c.ffn, d}, {d, moe ? 0 : c.ffn},
+                              {c.vocab, d}};
+    *part_floats = 0;
+    *blocks = 0;
+    for (int M : {2 * c.batch, c.batch}) {
+        for (auto& sh : shapes) {
+            if (sh[0] <= 0 || sh[1] <= 0) continue;
+            const dfk::GemvPlan pl = dfk::plan_gemv(c.dtype, sh[0], sh[1], M);
+            const size_t need = pl.part_floats > 0 ? pl.part_floats : (size_t)M * sh[0];
+            if (need > *part_floats) *part_floats = need;
+            if ((size_t)pl.nblocks > *blocks) *blocks = pl.nblocks;
+        }
+    }
+}
 
 WsLayout layout(const df_config& c) {
     const size_t es = elem_size(c.dtype);
@@ -31,9 +51,9 @@ WsLayout layout(const df_config& c) {
     auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
     L.status = take(kAlign);
     L.h = take(M * c.d_model * 4);
-    L.xd = take(M * c.d_model * es);
-    L.xo = take(M * c.d_model * es);
-    L.xf = take(moe ? 0 : M * (size_t)c.ffn * es);
+    L.xd = take(M * c.d_model * 4);
+    L.xo = take(M * c.d_model * 4);
+    L.xf = take(moe ? 0 : M * (size_t)c.ffn * 4);
     L.q = take(M * c.d_model * 4);
     L.part = take(dfk::attention_part_floats(c.batch, c.n_heads, c.max_seq, c.head_dim) * 4);
     L.logits = take(M * (size_t)c.vocab * 4);
@@ -43,8 +63,12 @@ WsLayout layout(const df_config& c) {
     L.offsets = take(moe ? (size_t)(c.n_experts + 1) * 4 : 0);
     L.perm = take(P * 4);
     L.inv = take(P * 4);
-    L.grows = take(P * 2 * (size_t)c.expert_ffn * es);
+    L.grows = take(P * 2 * (size_t)c.expert_ffn * 4);
     L.yrows = take(P * 2 * (size_t)c.d_model * 4);
+    size_t gp = 0, gb = 0;
+    gemv_scratch(c, &gp, &gb);
+    L.gpart = take(gp * 4);
+    L.gcount = take(gb * 4);
     L.total = o;
     return L;
 }
@@ -154,9 +178,9 @@ struct Step {
         const bool moe = c.n_experts > 0;
         int32_t* status = at<int32_t>(L.status);
         float* h = at<float>(L.h);
-        void* xd = ws + L.xd;
-        void* xo = ws + L.xo;
-        void* xf = ws + L.xf;
+        float* xd = at<float>(L.xd);
+        float* xo = at<float>(L.xo);
+        float* xf = at<float>(L.xf);
         float* q = at<float>(L.q);
         hipError_t e = dfk::embed_ln(c.dtype, w.tok_emb[0], w.tok_emb[1], w.pos_emb, tok, tok_stride, kv.len, B, d,
                                      c.max_seq, c.vocab, nflows, w.ln1, c.ln_eps, h, xd, status, s);
@@ -168,6 +192,7 @@ struct Step {
             char* vc = reinterpret_cast<char*>(kv.v) + l * kv_layer;
             dfk::GemvArgs g{};
             g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.H = c.n_heads; g.Dh = c.head_dim; g.S_max = c.max_seq;
+            g.part = at<float>(L.gpart); g.eps = c.ln_eps;
             // Q/K/V projection: Q coupling and primary K/V append fused
             g.x = xd; g.w = reinterpret_cast<const char*>(w.w_qkv) + (size_t)l * 3 * d * d * es;
             g.N = 3 * d; g.K = d; g.epi = dfk::EPI_QKV; g.cpl = w.cpl_a + (size_t)l * d; g.q_out = q;
@@ -180,20 +205,21 @@ struct Step {
             a.part = at<float>(L.part); a.o_rows = xo;
             timing_events(0, &a.ev_start, &a.ev_stop);
             if (dfk::attention(a, s) != hipSuccess) return DF_ERR_HIP;
-            // output projection + residual
+            // output projection + residual, then LN2 (fused in the split-K finish)
             g.x = xo; g.w = reinterpret_cast<const char*>(w.w_o) + (size_t)l * d * d * es;
-            g.N = d; g.K = d; g.epi = dfk::EPI_RESID; g.cpl = nullptr; g.h = h;
+            g.N = d; g.K = d; g.epi = dfk::EPI_RESID_LN; g.cpl = nullptr; g.h = h;
+            g.ln_gain = w.ln2 + (size_t)l * d; g.x_out = xd;
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
-            if (dfk::layer_norm_rows(c.dtype, h, w.ln2 + (size_t)l * d, c.ln_eps, B, d, nflows, xd, s) != hipSuccess)
-                return DF_ERR_HIP;
             const float* cb = w.cpl_b + (size_t)l * ffn;
             const float* cc = w.cpl_c + (size_t)l * d;
             if (!moe) {
                 g.x = xd; g.w = reinterpret_cast<const char*>(w.w_up) + (size_t)l * ffn * d * es;
                 g.N = (int)ffn; g.K = d; g.epi = dfk::EPI_GELU_B; g.cpl = cb; g.x_out = xf;
                 if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+                // down projection + c coupling + residual, then the next norm
                 g.x = xf; g.w = reinterpret_cast<const char*>(w.w_down) + (size_t)l * d * ffn * es;
-                g.N = d; g.K = (int)ffn; g.epi = dfk::EPI_RESID; g.cpl = cc; g.h = h;
+                g.N = d; g.K = (int)ffn; g.epi = dfk::EPI_RESID_LN; g.cpl = cc; g.h = h;
+                g.ln_gain = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf; g.x_out = xd;
                 if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             } else {
                 const int E = c.n_experts;
@@ -209,18 +235,20 @@ struct Step {
                 m.nflows = nflows; m.h = h;
                 m.ids_out = expert_ids ? expert_ids + (size_t)l * B * c.top_k : nullptr;
                 m.ids = at<int32_t>(L.ids); m.gates = at<float>(L.gates); m.offsets = at<int32_t>(L.offsets);
-                m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = ws + L.grows;
+                m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = at<float>(L.grows);
                 m.y_rows = at<float>(L.yrows);
                 if (dfk::moe(m, s) != hipSuccess) return DF_ERR_HIP;
+                const float* gn = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf;
+                if (dfk::layer_norm_rows(c.dtype, h, gn, c.ln_eps, B, d, nflows, xd, s) != hipSuccess)
+                    return DF_ERR_HIP;
             }
-            const float* gn = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf;
-            if (dfk::layer_norm_rows(c.dtype, h, gn, c.ln_eps, B, d, nflows, xd, s) != hipSuccess) return DF_ERR_HIP;
         }
         if (head) {
             float* lg = logits ? logits : at<float>(L.logits);
             dfk::GemvArgs g{};
             g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.x = xd; g.w = w.w_out; g.N = c.vocab; g.K = d;
             g.epi = dfk::EPI_STORE; g.out_f32 = lg;
+            g.part = at<float>(L.gpart);
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             if (dfk::mix_head(lg, B, c.vocab, nflows == 2, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
         }
@@ -320,6 +348,28 @@ int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t b
     a.o_f32 = d_o; a.lse = d_lse; a.o_rows = nullptr;
     timing_events(0, &a.ev_start, &a.ev_stop);
     return dfk::attention(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K) {
+    if ((dtype != DF_F32 && dtype != DF_BF16) || rows < 2 || (rows & 1) || N < 1 || K < 1) return 0;
+    if (dtype == DF_BF16 && (rows > 128 || K % 256)) return 0;
+    if (dtype == DF_F32 && (rows > 16 || K % 4)) return 0;
+    const dfk::GemvPlan pl = dfk::plan_gemv(dtype, N, K, rows);
+    return align_up(pl.part_floats * 4 + kAlign);
+}
+
+int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t rows, int32_t N, int32_t K,
+                    float* d_y, void* d_ws, size_t ws_bytes, void* stream) {
+    if (dtype != DF_F32 && dtype != DF_BF16) return DF_ERR_DTYPE;
+    if (!d_x || !d_w || !d_y || !d_ws) return DF_ERR_NULL;
+    const size_t need = df_stacked_gemv_workspace_bytes(dtype, rows, N, K);
+    if (need == 0) return DF_ERR_SHAPE;
+    if (!aligned16(d_x) || !aligned16(d_w) || !aligned16(d_y) || (uintptr_t)d_ws % kAlign) return DF_ERR_ALIGN;
+    if (ws_bytes < need) return DF_ERR_WORKSPACE;
+    dfk::GemvArgs g{};
+    g.dtype = dtype; g.x = d_x; g.w = d_w; g.N = N; g.K = K; g.B = rows / 2; g.nflows = 2;
+    g.epi = dfk::EPI_STORE; g.out_f32 = d_y; g.part = reinterpret_cast<float*>(d_ws);
+    return dfk::gemv(g, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
 int df_device_status(void* d_ws, void* stream, int32_t* status_out) {

@@ -3,13 +3,20 @@
 // coupled to Q1 through a_l, attends the primary K1/V1, so both flows are
 // served by one read of each K/V region).
 //
-// Split-K flash decode. Pass 1 (attn_partial): one wavefront per
-// (sequence, head, chunk of keys). Each 16-byte load of a key row is shared
-// by both queries; LPP lanes hold one key row (Dh/LPP elements each), so a
-// wave-wide load covers PPW consecutive positions. Every lane group keeps its
-// own online-softmax state (running max m, sum l, output o) in the log2
-// domain; groups merge once at the end of the chunk. Pass 2 (attn_combine)
-// merges the chunks of a (sequence, head) in chunk order: deterministic.
+// Split-K flash decode. The keys of every (sequence, head) pair are cut into
+// chunks of about equal length over the whole batch (C_b chunks for each head
+// of sequence b, C_b ~ n_b * items / total keys), so variable context lengths
+// still give equal work items. Pass 1 (attn_partial) runs one resident set of
+// wavefronts, each taking a fixed stride of items (about two per wave), so all
+// finish together. Each 16-byte load of a key
+// row is shared by both queries; LPP lanes hold one key row (Dh/LPP elements
+// each), so a wave-wide load covers PPW consecutive positions. Every lane
+// group keeps its own online-softmax state (running max m, sum l, output o)
+// in the log2 domain; groups merge once at the end of the chunk. Pass 2
+// (attn_combine) merges the chunks of a pair in chunk order: deterministic
+// (the item a wave happens to take does not change any result).
+#include <algorithm>
+
 #include "df_device.h"
 #include "df_internal.h"
 #include "../../include/dualflow.h"
@@ -23,10 +30,11 @@ struct PartParams {
     const float* q;
     const float* a;
     const int32_t* nkeys;
-    float* part_o;     // [B*H][n_chunks][2][Dh]
-    float* part_ml;    // [B*H][n_chunks][2][2]
+    float* part_o;     // [slots][2][Dh]
+    float* part_ml;    // [slots][4]
     size_t seq_stride; // elements between sequences in the cache
-    int B, H, S_max, nkeys_add, nflows, chunk, n_chunks;
+    int B, H, S_max, nkeys_add, nflows;
+    int target;        // wanted number of items over the batch
     float scale_log2;  // log2(e) / sqrt(Dh)
 };
 
@@ -47,136 +55,168 @@ __device__ __forceinline__ void unpack(const u32x4& r, float (&x)[EPL]) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr int kMinChunk = 64;   // keys per chunk at least
+
+// Chunking shared by both passes (pure integer function of the lengths).
+// n: keys of sequence b; total: sum over sequences of H*n. Returns C_b.
+__device__ __forceinline__ int chunks_of(int n, long long total, int target) {
+    if (n <= 0) return 0;
+    long long c = ((long long)n * target + total / 2) / (total > 0 ? total : 1);
+    const long long cmax = (n + kMinChunk - 1) / kMinChunk;
+    if (c < 1) c = 1;
+    if (c > cmax) c = cmax;
+    return (int)c;
+}
+
+__device__ __forceinline__ int keys_of(const int32_t* nkeys, int b, int add, int S_max) {
+    int n = nkeys[b] + add;
+    return n < 0 ? 0 : (n > S_max ? S_max : n);
+}
+
 template <typename T, int DH, int U>
 __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
     constexpr int LPP = DH / EPL;              // lanes per key row
     constexpr int PPW = 64 / LPP;              // key rows per wave-wide load
     const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int bh = item / p.n_chunks;
-    const int c = item - bh * p.n_chunks;
-    if (bh >= p.B * p.H) return;
-    const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-    int n = p.nkeys[b] + p.nkeys_add;
-    n = n > p.S_max ? p.S_max : n;
-    const int start = c * p.chunk;
-    if (start >= n) return;
-    const int end = min(start + p.chunk, n);
     const int g = lane / LPP, sub = lane - (lane / LPP) * LPP;
     const bool dual = p.nflows == 2;
 
-    float q1[EPL], q2[EPL];
-    {
-        const float* qp = p.q + ((size_t)(b * 2) * p.H + h) * DH + sub * EPL;
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) q1[e] = qp[e];
-        if (dual) {
-            const float* q2p = qp + (size_t)p.H * DH;
+    // Per-sequence chunk counts and item offsets (lane b holds sequence b).
+    const int my_n = lane < p.B ? keys_of(p.nkeys, lane, p.nkeys_add, p.S_max) : 0;
+    long long total = (long long)p.H * my_n;
+    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o, 64);
+    const int my_c = chunks_of(my_n, total, p.target);
+    int incl = p.H * my_c;                       // inclusive prefix over lanes
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    const int my_base = incl - p.H * my_c;
+    const int n_items = __shfl(incl, 63, 64);
+
+    // Items are of about equal length; wave w takes items w, w + G, w + 2G, ...
+    const int G = gridDim.x * 4;
+    for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < n_items; item += G) {
+        // sequence of this item: the last b whose base <= item
+        int b = 0;
+        for (int bb = 1; bb < p.B; ++bb)
+            if (__shfl(my_base, bb, 64) <= item) b = bb;
+        const int n = __shfl(my_n, b, 64), C = __shfl(my_c, b, 64), base = __shfl(my_base, b, 64);
+        const int rel = item - base;
+        const int h = rel / C, c = rel - h * C;
+        const int start = (int)(((long long)c * n) / C), end = (int)(((long long)(c + 1) * n) / C);
+
+        float q1[EPL], q2[EPL];
+        {
+            const float* qp = p.q + ((size_t)(b * 2) * p.H + h) * DH + sub * EPL;
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) q2[e] = q2p[e];
-            if (p.a) {
-                const float* ap = p.a + h * DH + sub * EPL;
+            for (int e = 0; e < EPL; ++e) q1[e] = qp[e];
+            if (dual) {
+                const float* q2p = qp + (size_t)p.H * DH;
                 #pragma unroll
-                for (int e = 0; e < EPL; ++e) q2[e] = fmaf(ap[e], q1[e], q2[e]);
+                for (int e = 0; e < EPL; ++e) q2[e] = q2p[e];
+                if (p.a) {
+                    const float* ap = p.a + h * DH + sub * EPL;
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) q2[e] = fmaf(ap[e], q1[e], q2[e]);
+                }
+            } else {
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) q2[e] = 0.f;
             }
-        } else {
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) q2[e] = 0.f;
+            for (int e = 0; e < EPL; ++e) { q1[e] *= p.scale_log2; q2[e] *= p.scale_log2; }
         }
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) { q1[e] *= p.scale_log2; q2[e] *= p.scale_log2; }
-    }
+        const size_t off = (size_t)b * p.seq_stride + (size_t)h * p.S_max * DH + sub * EPL;
+        const T* kp = reinterpret_cast<const T*>(p.k) + off;
+        const T* vp = reinterpret_cast<const T*>(p.v) + off;
 
-    const size_t base = (size_t)b * p.seq_stride + (size_t)h * p.S_max * DH + sub * EPL;
-    const T* kp = reinterpret_cast<const T*>(p.k) + base;
-    const T* vp = reinterpret_cast<const T*>(p.v) + base;
+        float m1 = -1e30f, l1 = 0.f, m2 = -1e30f, l2 = 0.f;
+        float o1[EPL], o2[EPL];
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) { o1[e] = 0.f; o2[e] = 0.f; }
 
-    float m1 = -1e30f, l1 = 0.f, m2 = -1e30f, l2 = 0.f;
-    float o1[EPL], o2[EPL];
-    #pragma unroll
-    for (int e = 0; e < EPL; ++e) { o1[e] = 0.f; o2[e] = 0.f; }
-
-    for (int j0 = start; j0 < end; j0 += PPW * U) {
-        u32x4 kr[U], vr[U];
-        #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int j = j0 + u * PPW + g;
-            j = j < end ? j : end - 1;
-            kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)j * DH));
-        }
-        #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int j = j0 + u * PPW + g;
-            j = j < end ? j : end - 1;
-            vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)j * DH));
-        }
-        float s1[U], s2[U];
-        #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kk[EPL];
-            unpack<T, EPL>(kr[u], kk);
-            float a1 = 0.f, a2 = 0.f;
+        for (int j0 = start; j0 < end; j0 += PPW * U) {
+            u32x4 kr[U], vr[U];
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) { a1 = fmaf(q1[e], kk[e], a1); a2 = fmaf(q2[e], kk[e], a2); }
-            a1 = df::group_sum<LPP>(a1);
-            if (dual) a2 = df::group_sum<LPP>(a2);
-            const bool valid = (j0 + u * PPW + g) < end;
-            s1[u] = valid ? a1 : -INFINITY;
-            s2[u] = valid ? a2 : -INFINITY;
-        }
-        float mb1 = s1[0], mb2 = s2[0];
-        #pragma unroll
-        for (int u = 1; u < U; ++u) { mb1 = fmaxf(mb1, s1[u]); mb2 = fmaxf(mb2, s2[u]); }
-        const float mn1 = fmaxf(m1, mb1), mn2 = fmaxf(m2, mb2);
-        const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
-        m1 = mn1; m2 = mn2;
-        l1 *= al1; l2 *= al2;
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) { o1[e] *= al1; o2[e] *= al2; }
-        #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float p1 = fast_exp2(s1[u] - mn1);
-            const float p2 = dual ? fast_exp2(s2[u] - mn2) : 0.f;
-            l1 += p1; l2 += p2;
-            float vv[EPL];
-            unpack<T, EPL>(vr[u], vv);
+            for (int u = 0; u < U; ++u) {
+                int j = j0 + u * PPW + g;
+                j = j < end ? j : end - 1;
+                kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)j * DH));
+            }
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) { o1[e] = fmaf(p1, vv[e], o1[e]); o2[e] = fmaf(p2, vv[e], o2[e]); }
+            for (int u = 0; u < U; ++u) {
+                int j = j0 + u * PPW + g;
+                j = j < end ? j : end - 1;
+                vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)j * DH));
+            }
+            float s1[U], s2[U];
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float kk[EPL];
+                unpack<T, EPL>(kr[u], kk);
+                float a1 = 0.f, a2 = 0.f;
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) { a1 = fmaf(q1[e], kk[e], a1); a2 = fmaf(q2[e], kk[e], a2); }
+                a1 = df::group_sum<LPP>(a1);
+                if (dual) a2 = df::group_sum<LPP>(a2);
+                const bool valid = (j0 + u * PPW + g) < end;
+                s1[u] = valid ? a1 : -INFINITY;
+                s2[u] = valid ? a2 : -INFINITY;
+            }
+            float mb1 = s1[0], mb2 = s2[0];
+            #pragma unroll
+            for (int u = 1; u < U; ++u) { mb1 = fmaxf(mb1, s1[u]); mb2 = fmaxf(mb2, s2[u]); }
+            const float mn1 = fmaxf(m1, mb1), mn2 = fmaxf(m2, mb2);
+            const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
+            m1 = mn1; m2 = mn2;
+            l1 *= al1; l2 *= al2;
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) { o1[e] *= al1; o2[e] *= al2; }
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p1 = fast_exp2(s1[u] - mn1);
+                const float p2 = dual ? fast_exp2(s2[u] - mn2) : 0.f;
+                l1 += p1; l2 += p2;
+                float vv[EPL];
+                unpack<T, EPL>(vr[u], vv);
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) { o1[e] = fmaf(p1, vv[e], o1[e]); o2[e] = fmaf(p2, vv[e], o2[e]); }
+            }
         }
-    }
 
-    // Merge the PPW lane groups (same dims, different key subsets).
-    #pragma unroll
-    for (int off = LPP; off < 64; off <<= 1) {
-        const float m1o = __shfl_xor(m1, off, 64), l1o = __shfl_xor(l1, off, 64);
-        const float m2o = __shfl_xor(m2, off, 64), l2o = __shfl_xor(l2, off, 64);
-        const float mn1 = fmaxf(m1, m1o), mn2 = fmaxf(m2, m2o);
-        const float sa1 = fast_exp2(m1 - mn1), sb1 = fast_exp2(m1o - mn1);
-        const float sa2 = fast_exp2(m2 - mn2), sb2 = fast_exp2(m2o - mn2);
-        l1 = l1 * sa1 + l1o * sb1;
-        l2 = l2 * sa2 + l2o * sb2;
+        // Merge the PPW lane groups (same dims, different key subsets).
         #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float x1 = __shfl_xor(o1[e], off, 64), x2 = __shfl_xor(o2[e], off, 64);
-            o1[e] = o1[e] * sa1 + x1 * sb1;
-            o2[e] = o2[e] * sa2 + x2 * sb2;
-        }
-        m1 = mn1; m2 = mn2;
-    }
-    const size_t slot = (size_t)bh * p.n_chunks + c;
-    if (g == 0) {
-        float* po = p.part_o + slot * 2 * DH + sub * EPL;
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) po[e] = o1[e];
-        if (dual) {
+        for (int off2 = LPP; off2 < 64; off2 <<= 1) {
+            const float m1o = __shfl_xor(m1, off2, 64), l1o = __shfl_xor(l1, off2, 64);
+            const float m2o = __shfl_xor(m2, off2, 64), l2o = __shfl_xor(l2, off2, 64);
+            const float mn1 = fmaxf(m1, m1o), mn2 = fmaxf(m2, m2o);
+            const float sa1 = fast_exp2(m1 - mn1), sb1 = fast_exp2(m1o - mn1);
+            const float sa2 = fast_exp2(m2 - mn2), sb2 = fast_exp2(m2o - mn2);
+            l1 = l1 * sa1 + l1o * sb1;
+            l2 = l2 * sa2 + l2o * sb2;
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) po[DH + e] = o2[e];
+            for (int e = 0; e < EPL; ++e) {
+                const float x1 = __shfl_xor(o1[e], off2, 64), x2 = __shfl_xor(o2[e], off2, 64);
+                o1[e] = o1[e] * sa1 + x1 * sb1;
+                o2[e] = o2[e] * sa2 + x2 * sb2;
+            }
+            m1 = mn1; m2 = mn2;
         }
-    }
-    if (lane == 0) {
-        float* pm = p.part_ml + slot * 4;
-        pm[0] = m1; pm[1] = l1; pm[2] = m2; pm[3] = l2;
+        if (g == 0) {
+            float* po = p.part_o + (size_t)item * 2 * DH + sub * EPL;
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) po[e] = o1[e];
+            if (dual) {
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) po[DH + e] = o2[e];
+            }
+        }
+        if (lane == 0) {
+            float* pm = p.part_ml + (size_t)item * 4;
+            pm[0] = m1; pm[1] = l1; pm[2] = m2; pm[3] = l2;
+        }
     }
 }
 
@@ -186,8 +226,8 @@ struct CombParams {
     const int32_t* nkeys;
     float* o_f32;
     float* lse;
-    void* o_rows;
-    int B, H, S_max, Dh, nkeys_add, nflows, chunk, n_chunks;
+    float* o_rows;
+    int B, H, S_max, Dh, nkeys_add, nflows, target;
 };
 
 template <typename T>
@@ -196,15 +236,20 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
     const int f = threadIdx.x / p.Dh, dim = threadIdx.x - f * p.Dh;
     if (f >= p.nflows) return;
-    int n = p.nkeys[b] + p.nkeys_add;
-    n = n > p.S_max ? p.S_max : n;
-    const int nc = (n + p.chunk - 1) / p.chunk;
-    const float* ml = p.part_ml + (size_t)bh * p.n_chunks * 4 + f * 2;
-    const float* po = p.part_o + (size_t)bh * p.n_chunks * 2 * p.Dh + f * p.Dh + dim;
+    long long total = 0;
+    for (int bb = 0; bb < p.B; ++bb) total += (long long)p.H * keys_of(p.nkeys, bb, p.nkeys_add, p.S_max);
+    int base = 0, C = 0;
+    for (int bb = 0; bb <= b; ++bb) {
+        const int c = chunks_of(keys_of(p.nkeys, bb, p.nkeys_add, p.S_max), total, p.target);
+        if (bb < b) base += p.H * c; else C = c;
+    }
+    const size_t first = (size_t)base + (size_t)h * C;
+    const float* ml = p.part_ml + first * 4 + f * 2;
+    const float* po = p.part_o + first * 2 * p.Dh + f * p.Dh + dim;
     float M = -1e30f;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[c * 4]);
+    for (int c = 0; c < C; ++c) M = fmaxf(M, ml[c * 4]);
     float L = 0.f, O = 0.f;
-    for (int c = 0; c < nc; ++c) {
+    for (int c = 0; c < C; ++c) {
         const float w = __builtin_amdgcn_exp2f(ml[c * 4] - M);
         L = fmaf(ml[c * 4 + 1], w, L);
         O = fmaf(po[(size_t)c * 2 * p.Dh], w, O);
@@ -212,49 +257,69 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     O = O / L;
     const size_t row = (size_t)(2 * b + f) * p.H * p.Dh + h * p.Dh + dim;
     if (p.o_f32) p.o_f32[row] = O;
-    if (p.o_rows) df::St<T>::st(reinterpret_cast<T*>(p.o_rows), row, O);
+    if (p.o_rows) p.o_rows[row] = O;
     if (p.lse && dim == 0) p.lse[(size_t)(2 * b + f) * p.H + h] = (M + __log2f(L)) * df::kLn2;
+}
+
+constexpr int kMaxTarget = 16384;   // items per launch at most (workspace bound)
+
+// Resident waves of attn_partial on the current device (cached).
+template <typename T, int DH, int U>
+int resident_waves() {
+    static int cached = 0;
+    if (cached) return cached;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&attn_partial<T, DH, U>),
+                                                      256, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+        per_cu = 2;
+    }
+    cached = cus * per_cu * 4;
+    return cached;
 }
 
 template <typename T, int DH>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     constexpr int U = 8;
-    const int chunk = attention_chunk(DH);
-    const int n_chunks = (a.S_max + chunk - 1) / chunk;
+    const int waves = resident_waves<T, DH, U>();
+    const int target = std::min(2 * waves, kMaxTarget - a.B * a.H);
     PartParams p;
     p.k = a.k; p.v = a.v; p.q = a.q; p.a = a.a; p.nkeys = a.nkeys;
-    p.part_o = a.part;
-    p.part_ml = a.part + (size_t)a.B * a.H * n_chunks * 2 * DH;
+    p.part_ml = a.part + 64;
+    p.part_o = p.part_ml + (size_t)kMaxTarget * 4;
     p.seq_stride = (size_t)a.H * a.S_max * DH;
     p.B = a.B; p.H = a.H; p.S_max = a.S_max; p.nkeys_add = a.nkeys_add; p.nflows = a.nflows;
-    p.chunk = chunk; p.n_chunks = n_chunks;
+    p.target = target;
     p.scale_log2 = df::kLog2e / sqrtf((float)DH);
-    const long items = (long)a.B * a.H * n_chunks;
-    const unsigned grid = (unsigned)((items + 3) / 4);
+    (void)hipGetLastError();
     if (a.ev_start) (void)hipEventRecord(a.ev_start, s);
-    hipLaunchKernelGGL((attn_partial<T, DH, U>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_partial<T, DH, U>), dim3(waves / 4), dim3(256), 0, s, p);
     if (a.ev_stop) (void)hipEventRecord(a.ev_stop, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     CombParams c;
     c.part_o = p.part_o; c.part_ml = p.part_ml; c.nkeys = a.nkeys; c.o_f32 = a.o_f32; c.lse = a.lse;
     c.o_rows = a.o_rows; c.B = a.B; c.H = a.H; c.S_max = a.S_max; c.Dh = DH; c.nkeys_add = a.nkeys_add;
-    c.nflows = a.nflows; c.chunk = chunk; c.n_chunks = n_chunks;
+    c.nflows = a.nflows; c.target = target;
     hipLaunchKernelGGL((attn_combine<T>), dim3(a.B * a.H), dim3(2 * DH), 0, s, c);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int attention_chunk(int Dh) { return Dh >= 128 ? 256 : 512; }
-
 size_t attention_part_floats(int B, int H, int S_max, int Dh) {
-    const int chunk = attention_chunk(Dh);
-    const size_t n_chunks = (size_t)((S_max + chunk - 1) / chunk);
-    return (size_t)B * H * n_chunks * (2 * Dh + 4);
+    (void)S_max;
+    // 64 spare floats, then ml [kMaxTarget][4], then o [kMaxTarget][2][Dh]
+    (void)B; (void)H;
+    return 64 + (size_t)kMaxTarget * (4 + 2 * Dh);
 }
 
 hipError_t attention(const AttnArgs& a, hipStream_t s) {
+    if (a.B > 64) return hipErrorInvalidValue;
     if (a.dtype == DF_BF16) {
         switch (a.Dh) {
             case 32: return launch<bf16_t, 32>(a, s);

@@ -20,14 +20,14 @@ struct AttnArgs {
     const int32_t* nkeys;     // keys attended by sequence b: nkeys[b] + nkeys_add
     int nkeys_add;
     int nflows;               // 2 = both flows, 1 = primary only
-    float* part;              // workspace, attention_part_floats() floats
+    float* part;              // workspace, attention_part_floats() floats; its first
+                              // two ints are work counters, zero between launches
     float* o_f32;             // [B][2][H][Dh] fp32 output or nullptr
     float* lse;               // [B][2][H] or nullptr
-    void* o_rows;             // [2B][H*Dh] output rounded to `dtype`, or nullptr
+    float* o_rows;            // [2B][H*Dh] fp32 output rows (projection input), or nullptr
     hipEvent_t ev_start;      // optional events around the partial pass
     hipEvent_t ev_stop;
 };
-int attention_chunk(int Dh);
 size_t attention_part_floats(int B, int H, int S_max, int Dh);
 hipError_t attention(const AttnArgs& a, hipStream_t s);
 
@@ -46,14 +46,14 @@ hipError_t kv_append(int dtype, void* k, void* v, int B, int H, int S_max, int D
 // len[b] += inc.
 hipError_t len_add(int32_t* len, int B, int inc, hipStream_t s);
 
-// h[2b+f] = E_f[tok[b*tok_stride]] + P[len[b]] (fp32), then x = rho(LN(h; g)).
+// h[2b+f] = E_f[tok[b*tok_stride]] + P[len[b]] (fp32), then x = LN(h; g) (fp32).
 // Token ids outside [0, V) are clamped and flagged (status bit 1).
 hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* pos_emb,
                     const int32_t* tok, int tok_stride, const int32_t* len, int B, int d, int S_max,
                     int V, int nflows, const float* g, float eps, float* h, void* x, int32_t* status,
                     hipStream_t s);
 
-// x[r] = rho(LN(h[r]; g)) for the stacked rows in use.
+// x[r] = LN(h[r]; g) (fp32) for the stacked rows in use.
 hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps, int B, int d,
                            int nflows, void* x, hipStream_t s);
 
@@ -64,13 +64,13 @@ hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps,
 enum EpiKind {
     EPI_STORE = 0,     // out_f32[m][n] = y
     EPI_QKV = 1,       // Q rows (+ a coupling) to q_out, primary K/V appended to the cache
-    EPI_GELU_B = 2,    // g = GELU(y), g2 += b*g1, rho(g) to x_out
-    EPI_RESID = 3,     // (optional c coupling) h[m][n] += y
+    EPI_GELU_B = 2,    // g = GELU(y), g2 += b*g1, g to x_out
+    EPI_RESID_LN = 3,  // (optional c coupling) h[m][n] += y, then x_out = LN(h; ln_gain)
 };
 
 struct GemvArgs {
     int dtype;
-    const void* x;        // [2B][K] stacked rows, storage dtype
+    const void* x;        // [2B][K] stacked rows, fp32
     const void* w;        // [N][K] storage dtype
     int N, K;
     int B;                // sequences
@@ -78,16 +78,24 @@ struct GemvArgs {
     int epi;
     // epilogue operands
     float* out_f32;       // EPI_STORE: [2B][N]
-    float* h;             // EPI_RESID: [2B][N]
-    void* x_out;          // EPI_GELU_B: [2B][N] storage dtype
-    const float* cpl;     // a (QKV), b (GELU_B), c (RESID) or nullptr
+    float* h;             // EPI_RESID_LN: [2B][N] residual
+    float* x_out;         // EPI_GELU_B, EPI_RESID_LN: [2B][N] fp32
+    const float* cpl;     // a (QKV), b (GELU_B), c (RESID_LN) or nullptr
     float* q_out;         // EPI_QKV: [2B][d] fp32
     void* kc;             // EPI_QKV: cache of this layer [B][H][S_max][Dh]
     void* vc;
     const int32_t* len;   // EPI_QKV: write position per sequence
     int H, Dh, S_max;
     int32_t* status;      // EPI_QKV: flag when a position is out of range
+    float* part;          // split-K partial sums (plan_gemv(...).part_floats floats)
+    const float* ln_gain; // EPI_RESID_LN: gain of the following norm
+    float eps;
 };
+struct GemvPlan {
+    int MT, ks, S, nblocks;
+    size_t lds, part_floats;
+};
+GemvPlan plan_gemv(int dtype, int N, int K, int M);
 hipError_t gemv(const GemvArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
@@ -95,7 +103,7 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s);
 // ---------------------------------------------------------------------------
 struct MoeArgs {
     int dtype;
-    const void* x;          // [2B][d] rho(LN2(h)) rows
+    const float* x;         // [2B][d] LN2(h) rows (fp32)
     const float* r;         // [2B][E] router logits (computed)
     const float* r1_given;  // [B][E] primary logits supplied, or nullptr
     const void* w_up;       // [E][Fe][d]
@@ -106,7 +114,7 @@ struct MoeArgs {
     float eps;
     const float* g_next;    // gain of the next norm
     float* h;               // [2B][d] residual (updated)
-    void* x_next;           // [2B][d] rho(LN(h; g_next))
+    float* x_next;          // [2B][d] LN(h; g_next)
     int32_t* ids_out;       // [B][k] or nullptr
     // workspace
     int32_t* ids;           // [B][k]
@@ -114,7 +122,7 @@ struct MoeArgs {
     int32_t* offsets;       // [E+1]
     int32_t* perm;          // [B*k]: sorted slot -> b*k + j
     int32_t* inv;           // [B*k]: b*k + j -> sorted slot
-    void* g_rows;           // [B*k][2][Fe] storage dtype
+    float* g_rows;          // [B*k][2][Fe] fp32
     float* y_rows;          // [B*k][2][d]
 };
 hipError_t moe(const MoeArgs& a, hipStream_t s);

@@ -27,8 +27,6 @@ namespace dfk {
 namespace {
 
 using tile::f32x4;
-using tile::RT;
-using tile::ROWS;
 
 struct GParams {
     const void* x;
@@ -40,7 +38,7 @@ struct GParams {
     int epi;
     float* out_f32;
     float* h;
-    void* x_out;
+    float* x_out;
     const float* cpl;
     float* q_out;
     void* kc;
@@ -48,6 +46,9 @@ struct GParams {
     const int32_t* len;
     int H, Dh, S_max;
     int32_t* status;
+    float* part;          // split-K partials [S][M][N]
+    const float* ln_gain; // EPI_RESID_LN: gain of the norm that follows
+    float eps;
 };
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
@@ -63,19 +64,13 @@ __device__ __forceinline__ void epilogue(const GParams& p, int n, int b, float y
             p.out_f32[r1] = y1;
             if (dual) p.out_f32[r2] = y2;
             break;
-        case EPI_RESID:
-            if (dual && p.cpl) y2 = fmaf(p.cpl[n], y1, y2);   // MLP-output coupling (c_l)
-            p.h[r1] += y1;
-            if (dual) p.h[r2] += y2;
-            break;
         case EPI_GELU_B: {
             const float g1 = gelu(y1);
-            T* xo = reinterpret_cast<T*>(p.x_out);
-            df::St<T>::st(xo, r1, g1);
+            p.x_out[r1] = g1;
             if (dual) {
                 float g2 = gelu(y2);
                 if (p.cpl) g2 = fmaf(p.cpl[n], g1, g2);          // MLP-intermediate coupling (b_l)
-                df::St<T>::st(xo, r2, g2);
+                p.x_out[r2] = g2;
             }
             break;
         }
@@ -103,39 +98,190 @@ __device__ __forceinline__ void epilogue(const GParams& p, int n, int b, float y
     }
 }
 
-template <int MT, int KU>
-__global__ __launch_bounds__(1024) void gemv_bf16(GParams p) {
-    extern __shared__ float red[];   // [NW][RT][MT][4][64]
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, NW = blockDim.x >> 6;
-    const int n0 = blockIdx.x * ROWS;
+typedef tile::u32x4 u32x4;
+typedef tile::bf16x8 bf16x8;
+
+constexpr int NWAVE = 8;         // waves per workgroup, 16 weight rows each
+constexpr int WG_ROWS = 16 * NWAVE;
+
+// Epilogue from MFMA registers: lane l holds D[4*(l/16) + r][l%16] of its
+// wave's 16 rows x 16 stacked rows (per m tile). With both flows, the aux
+// row 2b+1 sits in the neighbouring lane of the primary row 2b.
+template <int MT>
+__device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&acc)[MT], int n_base, int lane) {
     const int li = lane & 15, lg = lane >> 4;
-    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.w);
-    const bf16_t* X = reinterpret_cast<const bf16_t*>(p.x);
-    const bf16_t* wrow[RT];
-    #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int n = min(n0 + rt * 16 + li, p.N - 1);
-        wrow[rt] = W + (size_t)n * p.K + lg * 8;
-    }
-    const bf16_t* xrow[MT];
+    const bool dual = p.nflows == 2;
     #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = min(mt * 16 + li, p.M - 1);
-        xrow[mt] = X + (size_t)(m * p.row_step) * p.K + lg * 8;
+        #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = acc[mt][r];
+            const float partner = __shfl_xor(v, 1, 64);
+            const int n = n_base + 4 * lg + r;
+            const int m = mt * 16 + li;
+            if (n >= p.N || m >= p.M) continue;
+            if (dual) {
+                if ((m & 1) == 0) epilogue<bf16_t>(p, n, m >> 1, v, partner);
+            } else {
+                epilogue<bf16_t>(p, n, m, v, 0.f);
+            }
+        }
     }
-    f32x4 acc[RT][MT];
-    tile::zero<MT>(acc);
-    tile::stream_k<MT, KU>(wrow, xrow, MT, wv * p.kw, (wv + 1) * p.kw, acc);
-    tile::to_lds<MT>(red, wv, lane, acc);
+}
+
+// Y = X W^T for NWAVE*16 weight rows over one k-slice [s*ks, (s+1)*ks).
+// Activation rows are fp32; while the k-slice is staged in LDS each value is
+// split into bf16 hi = rne(x) and lo = rne(x - hi) (x - hi - lo is below
+// 2^-17 |x|), and both parts go through the matrix cores into the same fp32
+// accumulator. LDS rows are padded by 8 elements against bank conflicts and
+// shared by the waves; each wave streams its 16 weight rows from HBM with the
+// next KU chunks already in flight. With S = gridDim.y > 1 slices, every
+// workgroup writes its partial sums and the last one to finish (atomic
+// counter per row block) adds the S partials in slice order and runs the
+// epilogue: deterministic, no float atomics.
+template <int MT, int KU>
+__global__ __launch_bounds__(NWAVE * 64) void gemv_bf16(GParams p) {
+    extern __shared__ bf16_t xs[];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int blk = blockIdx.x, sl = blockIdx.y, S = gridDim.y;
+    const int n_base = blk * WG_ROWS + wv * 16;
+    const int ks = p.kw, ks0 = sl * ks;
+    const int XS = ks + 8;
+    bf16_t* xs_hi = xs;
+    bf16_t* xs_lo = xs + 16 * MT * XS;
+    const int li = lane & 15, lg = lane >> 4;
+    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.w);
+    const float* X = reinterpret_cast<const float*>(p.x);
+    const bf16_t* wp = W + (size_t)min(n_base + li, p.N - 1) * p.K + ks0 + lg * 8;
+
+    u32x4 a0[KU];
+    #pragma unroll
+    for (int ku = 0; ku < KU; ++ku) a0[ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + 32 * ku));
+
+    // Stage the activation k-slice (loads of a batch issued before any is used).
+    const int c4 = ks >> 2, n_items = 16 * MT * c4;
+    constexpr int SB = 8;
+    for (int i0 = threadIdx.x; i0 < n_items; i0 += SB * NWAVE * 64) {
+        float4 v[SB];
+        #pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int i = i0 + u * NWAVE * 64;
+            if (i < n_items) {
+                const int m = i / c4, c = i - m * c4;
+                const int mm = min(m, p.M - 1);
+                v[u] = *reinterpret_cast<const float4*>(X + (size_t)(mm * p.row_step) * p.K + ks0 + c * 4);
+            }
+        }
+        #pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int i = i0 + u * NWAVE * 64;
+            if (i < n_items) {
+                const int m = i / c4, c = i - m * c4;
+                const bf16_t h0 = df::f32_to_bf16(v[u].x), h1 = df::f32_to_bf16(v[u].y);
+                const bf16_t h2 = df::f32_to_bf16(v[u].z), h3 = df::f32_to_bf16(v[u].w);
+                const bf16_t l0 = df::f32_to_bf16(v[u].x - df::bf16_to_f32(h0));
+                const bf16_t l1 = df::f32_to_bf16(v[u].y - df::bf16_to_f32(h1));
+                const bf16_t l2 = df::f32_to_bf16(v[u].z - df::bf16_to_f32(h2));
+                const bf16_t l3 = df::f32_to_bf16(v[u].w - df::bf16_to_f32(h3));
+                uint2 hv, lv;
+                hv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                hv.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+                lv.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                lv.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+                *reinterpret_cast<uint2*>(xs_hi + m * XS + c * 4) = hv;
+                *reinterpret_cast<uint2*>(xs_lo + m * XS + c * 4) = lv;
+            }
+        }
+    }
     __syncthreads();
+
+    f32x4 acc[MT];
+    #pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int xoff = li * XS + lg * 8;
+    for (int kk = 0; kk < ks; kk += 32 * KU) {
+        const bool more = kk + 32 * KU < ks;
+        u32x4 a1[KU];
+        if (more) {
+            #pragma unroll
+            for (int ku = 0; ku < KU; ++ku)
+                a1[ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + kk + 32 * KU + 32 * ku));
+        }
+        #pragma unroll
+        for (int ku = 0; ku < KU; ++ku) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, a0[ku]);
+            #pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int o = xoff + mt * 16 * XS + kk + 32 * ku;
+                const u32x4 bh = *reinterpret_cast<const u32x4*>(xs_hi + o);
+                const u32x4 bl = *reinterpret_cast<const u32x4*>(xs_lo + o);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc[mt], 0, 0, 0);
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc[mt], 0, 0, 0);
+            }
+        }
+        if (more) {
+            #pragma unroll
+            for (int ku = 0; ku < KU; ++ku) a0[ku] = a1[ku];
+        }
+    }
+
+    if (S > 1 || p.epi == EPI_RESID_LN) {
+        // partial sums of this k-slice: part[sl][m][n]; a reduce kernel finishes
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = n_base + 4 * lg + r, m = mt * 16 + li;
+                if (n < p.N && m < p.M) p.part[((size_t)sl * p.M + m) * p.N + n] = acc[mt][r];
+            }
+        return;
+    }
+    epilogue_regs<MT>(p, acc, n_base, lane);
+}
+
+// Sum of the S k-slice partials of logical row m, column n (slice order;
+// loads issued eight at a time).
+__device__ __forceinline__ float sum_slices(const GParams& p, int S, int m, int n) {
+    const float* q = p.part + (size_t)m * p.N + n;
+    const size_t stride = (size_t)p.M * p.N;
+    float v = 0.f;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+        float t[8];
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = q[(size_t)(s + u) * stride];
+        #pragma unroll
+        for (int u = 0; u < 8; ++u) v += t[u];
+    }
+    for (; s < S; ++s) v += q[(size_t)s * stride];
+    return v;
+}
+
+// Split-K finish for the elementwise epilogues: thread per (sequence, column).
+__global__ __launch_bounds__(256) void gemv_reduce_epi(GParams p, int S) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = t / p.N, n = t - (t / p.N) * p.N;
+    if (b >= p.B) return;
     const bool dual = p.nflows == 2;
-    for (int t = threadIdx.x; t < ROWS * p.B; t += blockDim.x) {
-        const int nl = t % ROWS, b = t / ROWS;
-        const int n = n0 + nl;
-        if (n >= p.N) continue;
-        const float y1 = tile::lds_sum<MT>(red, NW, nl, dual ? 2 * b : b);
-        const float y2 = dual ? tile::lds_sum<MT>(red, NW, nl, 2 * b + 1) : 0.f;
-        epilogue<bf16_t>(p, n, b, y1, y2);
+    const float y1 = sum_slices(p, S, dual ? 2 * b : b, n);
+    const float y2 = dual ? sum_slices(p, S, 2 * b + 1, n) : 0.f;
+    epilogue<bf16_t>(p, n, b, y1, y2);
+}
+
+// Split-K finish with the residual add: thread per (sequence, column); the
+// aux output gets the c coupling (y2 += c * y1) when given; h += y. The
+// following LayerNorm runs as its own row kernel.
+__global__ __launch_bounds__(256) void gemv_reduce_resid(GParams p, int S) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = t / p.N, n = t - (t / p.N) * p.N;
+    if (b >= p.B) return;
+    const bool dual = p.nflows == 2;
+    const float y1 = sum_slices(p, S, dual ? 2 * b : b, n);
+    p.h[(size_t)(2 * b) * p.N + n] += y1;
+    if (dual) {
+        float y2 = sum_slices(p, S, 2 * b + 1, n);
+        if (p.cpl) y2 = fmaf(p.cpl[n], y1, y2);   // MLP-output coupling (c_l)
+        p.h[(size_t)(2 * b + 1) * p.N + n] += y2;
     }
 }
 
@@ -165,6 +311,12 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
     #pragma unroll
     for (int m = 0; m < 16; ++m)
         if (m < p.M) acc[m] = df::wave_sum(acc[m]);
+    if (p.epi == EPI_RESID_LN) {       // one "slice"; gemv_reduce_ln finishes
+        #pragma unroll
+        for (int m = 0; m < 16; ++m)
+            if (m < p.M && lane == m) p.part[(size_t)m * p.N + n] = acc[m];
+        return;
+    }
     const bool dual = p.nflows == 2;
     #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -177,23 +329,66 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
 }
 
 template <int MT>
-hipError_t launch_bf16(GParams& p, hipStream_t s) {
-    constexpr int KU = MT <= 2 ? 4 : 2;
-    const int nwg = (p.N + ROWS - 1) / ROWS;
-    const int nw = tile::pick_waves(nwg, p.K, MT, KU, 4096);
-    p.kw = p.K / nw;
-    const size_t lds = (size_t)nw * RT * MT * 256 * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_bf16<MT, KU>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((gemv_bf16<MT, KU>), dim3(nwg), dim3(64 * nw), lds, s, p);
+constexpr int ku_of() { return MT <= 2 ? 8 : (MT == 4 ? 4 : 2); }
+
+template <int MT>
+hipError_t launch_bf16(GParams& p, const GemvPlan& pl, hipStream_t s) {
+    constexpr int KU = ku_of<MT>();
+    p.kw = pl.ks;
+    hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&gemv_bf16<MT, KU>), pl.lds);
+    if (e != hipSuccess) return e;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemv_bf16<MT, KU>), dim3(pl.nblocks, pl.S), dim3(NWAVE * 64), pl.lds, s, p);
     return hipGetLastError();
 }
 
+hipError_t finish(GParams& p, int S, hipStream_t s) {
+    if (p.epi == EPI_RESID_LN) {
+        const long total = (long)p.B * p.N;
+        hipLaunchKernelGGL(gemv_reduce_resid, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p, S);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return layer_norm_rows(DF_F32, p.h, p.ln_gain, p.eps, p.B, p.N, p.nflows, p.x_out, s);
+    }
+    if (S > 1) {
+        const long total = (long)p.B * p.N;
+        hipLaunchKernelGGL(gemv_reduce_epi, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p, S);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
 }  // namespace
+
+GemvPlan plan_gemv(int dtype, int N, int K, int M) {
+    GemvPlan pl{};
+    if (dtype != DF_BF16) return pl;
+    int mt = (M + 15) / 16;
+    pl.MT = mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
+    pl.nblocks = (N + WG_ROWS - 1) / WG_ROWS;
+    // k-slice: a divisor of K, multiple of 32*KU, activation slice (hi and lo
+    // parts) in LDS small enough for two workgroups per CU; smaller slices
+    // until about two workgroups per CU are in the grid.
+    const int KU = pl.MT <= 2 ? 8 : (pl.MT == 4 ? 4 : 2);
+    const int step = 32 * KU;
+    auto lds_of = [&](int ks) { return (size_t)2 * 16 * pl.MT * (ks + 8) * 2; };
+    int best = step;
+    for (int ks = step; ks <= K && ks <= 512; ks += step)
+        if (K % ks == 0 && lds_of(ks) <= 78 * 1024) best = ks;
+    int ks = best;
+    while ((long)pl.nblocks * (K / ks) < 512) {
+        int nxt = 0;
+        for (int c = step; c < ks; c += step)
+            if (K % c == 0) nxt = c;
+        if (nxt == 0) break;
+        ks = nxt;
+    }
+    pl.ks = ks;
+    pl.S = K / ks;
+    pl.lds = lds_of(ks);
+    pl.part_floats = (size_t)pl.S * M * N;   // used when S > 1 or before a residual + norm
+    return pl;
+}
 
 hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     GParams p;
@@ -202,18 +397,30 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     p.row_step = a.nflows == 2 ? 1 : 2;
     p.epi = a.epi; p.out_f32 = a.out_f32; p.h = a.h; p.x_out = a.x_out; p.cpl = a.cpl; p.q_out = a.q_out;
     p.kc = a.kc; p.vc = a.vc; p.len = a.len; p.H = a.H; p.Dh = a.Dh; p.S_max = a.S_max; p.status = a.status;
+    p.part = a.part; p.ln_gain = a.ln_gain; p.eps = a.eps;
     p.kw = a.K;
     if (a.dtype == DF_F32) {
         if (p.M > 16) return hipErrorInvalidValue;
+        if (a.epi == EPI_RESID_LN && (!a.part || a.N > 4096)) return hipErrorInvalidValue;
+        (void)hipGetLastError();
         hipLaunchKernelGGL(gemv_f32, dim3((a.N + 3) / 4), dim3(256), 0, s, p);
-        return hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return finish(p, 1, s);
     }
-    const int mt = (p.M + 15) / 16;
-    if (mt <= 1) return launch_bf16<1>(p, s);
-    if (mt <= 2) return launch_bf16<2>(p, s);
-    if (mt <= 4) return launch_bf16<4>(p, s);
-    if (mt <= 8) return launch_bf16<8>(p, s);
-    return hipErrorInvalidValue;
+    if (p.M > 128 || (a.K % 256) != 0) return hipErrorInvalidValue;
+    const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M);
+    if ((pl.S > 1 || a.epi == EPI_RESID_LN) && !a.part) return hipErrorInvalidValue;
+    if (a.epi == EPI_RESID_LN && a.N > 4096) return hipErrorInvalidValue;
+    hipError_t e;
+    switch (pl.MT) {
+        case 1: e = launch_bf16<1>(p, pl, s); break;
+        case 2: e = launch_bf16<2>(p, pl, s); break;
+        case 4: e = launch_bf16<4>(p, pl, s); break;
+        default: e = launch_bf16<8>(p, pl, s); break;
+    }
+    if (e != hipSuccess) return e;
+    return finish(p, pl.S, s);
 }
 
 }  // namespace dfk

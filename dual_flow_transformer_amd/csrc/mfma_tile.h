@@ -22,13 +22,33 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int RT = 2;           // 16-row weight tiles per workgroup
 constexpr int ROWS = 16 * RT;   // weight rows per workgroup
 
+// Eight fp32 activations as two bf16 octets, hi = rne(x), lo = rne(x - hi):
+// hi + lo equals x to within 2^-17 |x|.
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
+    const float4 v0 = *reinterpret_cast<const float4*>(x);
+    const float4 v1 = *reinterpret_cast<const float4*>(x + 4);
+    const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t h[4], l[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16_t h0 = df::f32_to_bf16(f[2 * i]), h1 = df::f32_to_bf16(f[2 * i + 1]);
+        const bf16_t l0 = df::f32_to_bf16(f[2 * i] - df::bf16_to_f32(h0));
+        const bf16_t l1 = df::f32_to_bf16(f[2 * i + 1] - df::bf16_to_f32(h1));
+        h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    hi = (u32x4){h[0], h[1], h[2], h[3]};
+    lo = (u32x4){l[0], l[1], l[2], l[3]};
+}
+
 // Stream k in [kbeg, kend) (multiple of 32*KU) through MFMAs for RT weight
-// tiles against the first `mtiles` activation tiles (wave-uniform).
+// tiles against the first `mtiles` activation tiles (wave-uniform). The fp32
+// activation rows enter as bf16 hi and lo parts into the same accumulator.
 template <int MT, int KU>
-__device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const bf16_t* const (&xrow)[MT],
+__device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const float* const (&xrow)[MT],
                                          int mtiles, int kbeg, int kend, f32x4 (&acc)[RT][MT]) {
     for (int k = kbeg; k < kend; k += 32 * KU) {
-        u32x4 a[RT][KU], bx[MT][KU];
+        u32x4 a[RT][KU], bh[MT][KU], bl[MT][KU];
         #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             #pragma unroll
@@ -38,8 +58,7 @@ __device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const 
         for (int mt = 0; mt < MT; ++mt)
             if (mt < mtiles) {
                 #pragma unroll
-                for (int ku = 0; ku < KU; ++ku)
-                    bx[mt][ku] = *reinterpret_cast<const u32x4*>(xrow[mt] + k + 32 * ku);
+                for (int ku = 0; ku < KU; ++ku) split8(xrow[mt] + k + 32 * ku, bh[mt][ku], bl[mt][ku]);
             }
         #pragma unroll
         for (int ku = 0; ku < KU; ++ku)
@@ -47,10 +66,13 @@ __device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const 
             for (int rt = 0; rt < RT; ++rt)
                 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    if (mt < mtiles)
+                    if (mt < mtiles) {
+                        const bf16x8 av = __builtin_bit_cast(bf16x8, a[rt][ku]);
                         acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[rt][ku]), __builtin_bit_cast(bf16x8, bx[mt][ku]),
-                            acc[rt][mt], 0, 0, 0);
+                            av, __builtin_bit_cast(bf16x8, bh[mt][ku]), acc[rt][mt], 0, 0, 0);
+                        acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av, __builtin_bit_cast(bf16x8, bl[mt][ku]), acc[rt][mt], 0, 0, 0);
+                    }
     }
 }
 
@@ -82,6 +104,12 @@ __device__ __forceinline__ float lds_sum(const float* red, int NW, int nl, int m
     float s = 0.f;
     for (int w = 0; w < NW; ++w) s += red[(size_t)w * RT * MT * 256 + idx];
     return s;
+}
+
+// Allow `bytes` of dynamic LDS for kernel `fn` (needed above 64 KiB).
+inline hipError_t allow_lds(const void* fn, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 inline int floor_pow2(int x) {

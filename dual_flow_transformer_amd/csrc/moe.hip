@@ -100,13 +100,13 @@ __global__ __launch_bounds__(256) void moe_route(const float* r, const float* r1
 }
 
 struct ExpParams {
-    const bf16_t* x;       // up: [2B][d] rows; down: g_rows [P][2][Fe]
+    const float* x;        // up: [2B][d] rows; down: g_rows [P][2][Fe] (fp32)
     const bf16_t* w;       // [E][N][K]
     int N, K, k, nflows, kw;
     const int32_t* offsets;
     const int32_t* perm;
     const float* cpl_b;
-    bf16_t* g_out;         // up: [P][2][Fe]
+    float* g_out;          // up: [P][2][Fe]
     float* y_out;          // down: [P][2][d]
     bool up;
 };
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
     // Several passes when one expert holds more than MT*16 stacked rows.
     for (int mbase = 0; mbase < M; mbase += MT * 16) {
         const int mt_here = min((M - mbase + 15) / 16, mtiles);
-        const bf16_t* xrow[MT];
+        const float* xrow[MT];
         #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = min(mbase + mt * 16 + li, M - 1);
@@ -160,11 +160,11 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
             const int s = off + mbase / p.nflows + q;
             if (p.up) {
                 const float g1 = 0.5f * y1 * (1.0f + erff(y1 * 0.70710678118654752f));
-                p.g_out[((size_t)s * 2) * p.N + n] = df::f32_to_bf16(g1);
+                p.g_out[((size_t)s * 2) * p.N + n] = g1;
                 if (p.nflows == 2) {
                     float g2 = 0.5f * y2 * (1.0f + erff(y2 * 0.70710678118654752f));
                     g2 = fmaf(p.cpl_b[n], g1, g2);      // intermediate coupling b_l, per expert
-                    p.g_out[((size_t)s * 2 + 1) * p.N + n] = df::f32_to_bf16(g2);
+                    p.g_out[((size_t)s * 2 + 1) * p.N + n] = g2;
                 }
             } else {
                 p.y_out[((size_t)s * 2) * p.N + n] = y1;
@@ -195,17 +195,13 @@ __global__ __launch_bounds__(256) void moe_combine(const float* y_rows, const fl
 
 template <int MT>
 hipError_t launch_expert(ExpParams& p, int E, hipStream_t s) {
-    constexpr int KU = MT <= 2 ? 4 : 2;
+    constexpr int KU = 2;
     const int nwg = (p.N + ROWS - 1) / ROWS;
     const int nw = tile::pick_waves(nwg * E, p.K, MT, KU, 8192);
     p.kw = p.K / nw;
     const size_t lds = (size_t)nw * RT * MT * 256 * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_expert<MT, KU>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
-    }
+    hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&moe_expert<MT, KU>), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((moe_expert<MT, KU>), dim3(nwg, E), dim3(64 * nw), lds, s, p);
     return hipGetLastError();
 }
@@ -214,19 +210,20 @@ hipError_t launch_expert(ExpParams& p, int E, hipStream_t s) {
 
 hipError_t moe(const MoeArgs& a, hipStream_t s) {
     if (a.k > kMaxK || a.B > 64 || a.E > 1024 || a.dtype != DF_BF16) return hipErrorInvalidValue;
+    (void)hipGetLastError();
     hipLaunchKernelGGL(moe_route, dim3(1), dim3(256), 0, s, a.r, a.r1_given, a.B, a.E, a.k, a.nflows, a.ids,
                        a.gates, a.ids_out, a.offsets, a.perm, a.inv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ExpParams up;
-    up.x = reinterpret_cast<const bf16_t*>(a.x);
+    up.x = a.x;
     up.w = reinterpret_cast<const bf16_t*>(a.w_up);
     up.N = a.Fe; up.K = a.d; up.k = a.k; up.nflows = a.nflows; up.offsets = a.offsets; up.perm = a.perm;
-    up.cpl_b = a.cpl_b; up.g_out = reinterpret_cast<bf16_t*>(a.g_rows); up.y_out = nullptr; up.up = true;
+    up.cpl_b = a.cpl_b; up.g_out = a.g_rows; up.y_out = nullptr; up.up = true;
     e = launch_expert<2>(up, a.E, s);
     if (e != hipSuccess) return e;
     ExpParams dn = up;
-    dn.x = reinterpret_cast<const bf16_t*>(a.g_rows);
+    dn.x = a.g_rows;
     dn.w = reinterpret_cast<const bf16_t*>(a.w_down);
     dn.N = a.d; dn.K = a.Fe; dn.g_out = nullptr; dn.y_out = a.y_rows; dn.up = false;
     e = launch_expert<2>(dn, a.E, s);

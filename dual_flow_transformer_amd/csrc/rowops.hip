@@ -11,9 +11,9 @@ namespace {
 constexpr int kRowThreads = 256;
 constexpr int kMaxPerThread = 16;   // d <= 4096
 
-// LayerNorm of one row held in registers (x[e] is element tid + e*256).
-template <typename T>
-__device__ void ln_store(const float (&x)[kMaxPerThread], int d, const float* g, float eps, T* out,
+// LayerNorm of one row held in registers (x[e] is element tid + e*256);
+// the normalised row is written in fp32 (projection inputs are not rounded).
+__device__ void ln_store(const float (&x)[kMaxPerThread], int d, const float* g, float eps, float* out,
                          float* red) {
     const int tid = threadIdx.x;
     float s = 0.f;
@@ -34,14 +34,14 @@ __device__ void ln_store(const float (&x)[kMaxPerThread], int d, const float* g,
     #pragma unroll
     for (int e = 0; e < kMaxPerThread; ++e) {
         const int i = tid + e * kRowThreads;
-        if (i < d) df::St<T>::st(out, i, (x[e] - mean) * rstd * g[i]);
+        if (i < d) out[i] = (x[e] - mean) * rstd * g[i];
     }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
     const T* emb0, const T* emb1, const T* pos_emb, const int32_t* tok, int tok_stride,
-    const int32_t* len, int d, int S_max, int V, int nflows, const float* g, float eps, float* h, T* x,
+    const int32_t* len, int d, int S_max, int V, int nflows, const float* g, float eps, float* h, float* x,
     int32_t* status) {
     __shared__ float red[16];
     const int b = blockIdx.x;
@@ -66,13 +66,12 @@ __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
                 h[row + i] = xv[k];
             }
         }
-        ln_store<T>(xv, d, g, eps, x + row, red);
+        ln_store(xv, d, g, eps, x + row, red);
     }
 }
 
-template <typename T>
 __global__ __launch_bounds__(kRowThreads) void ln_rows_kernel(const float* h, const float* g, float eps,
-                                                              int d, int nflows, T* x) {
+                                                              int d, int nflows, float* x) {
     __shared__ float red[16];
     const int b = blockIdx.x;
     for (int f = 0; f < nflows; ++f) {
@@ -83,7 +82,7 @@ __global__ __launch_bounds__(kRowThreads) void ln_rows_kernel(const float* h, co
             const int i = threadIdx.x + k * kRowThreads;
             xv[k] = i < d ? h[row + i] : 0.f;
         }
-        ln_store<T>(xv, d, g, eps, x + row, red);
+        ln_store(xv, d, g, eps, x + row, red);
     }
 }
 
@@ -171,6 +170,7 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int
 
 hipError_t mix_head(const float* logits, int B, int V, int aux_on, float* p_mix, float* alpha,
                     int32_t* next_tok, hipStream_t s) {
+    (void)hipGetLastError();
     hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, logits, V, aux_on, p_mix, alpha, next_tok);
     return hipGetLastError();
 }
@@ -178,6 +178,7 @@ hipError_t mix_head(const float* logits, int B, int V, int aux_on, float* p_mix,
 hipError_t kv_append(int dtype, void* k, void* v, int B, int H, int S_max, int Dh, const int32_t* pos,
                      const float* dk, const float* dv, int32_t* status, hipStream_t s) {
     const int threads = Dh < 64 ? 64 : Dh;
+    (void)hipGetLastError();
     if (dtype == DF_BF16)
         hipLaunchKernelGGL(kv_append_kernel<bf16_t>, dim3(B * H), dim3(threads), 0, s, (bf16_t*)k, (bf16_t*)v,
                            H, S_max, Dh, pos, dk, dv, status);
@@ -188,6 +189,7 @@ hipError_t kv_append(int dtype, void* k, void* v, int B, int H, int S_max, int D
 }
 
 hipError_t len_add(int32_t* len, int B, int inc, hipStream_t s) {
+    (void)hipGetLastError();
     hipLaunchKernelGGL(len_add_kernel, dim3((B + 63) / 64), dim3(64), 0, s, len, B, inc);
     return hipGetLastError();
 }
@@ -195,10 +197,11 @@ hipError_t len_add(int32_t* len, int B, int inc, hipStream_t s) {
 hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* pos_emb, const int32_t* tok,
                     int tok_stride, const int32_t* len, int B, int d, int S_max, int V, int nflows, const float* g,
                     float eps, float* h, void* x, int32_t* status, hipStream_t s) {
+    (void)hipGetLastError();
     if (dtype == DF_BF16)
         hipLaunchKernelGGL(embed_ln_kernel<bf16_t>, dim3(B), dim3(kRowThreads), 0, s, (const bf16_t*)emb0,
                            (const bf16_t*)emb1, (const bf16_t*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
-                           g, eps, h, (bf16_t*)x, status);
+                           g, eps, h, (float*)x, status);
     else
         hipLaunchKernelGGL(embed_ln_kernel<float>, dim3(B), dim3(kRowThreads), 0, s, (const float*)emb0,
                            (const float*)emb1, (const float*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
@@ -208,12 +211,9 @@ hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* p
 
 hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps, int B, int d, int nflows,
                            void* x, hipStream_t s) {
-    if (dtype == DF_BF16)
-        hipLaunchKernelGGL(ln_rows_kernel<bf16_t>, dim3(B), dim3(kRowThreads), 0, s, h, g, eps, d, nflows,
-                           (bf16_t*)x);
-    else
-        hipLaunchKernelGGL(ln_rows_kernel<float>, dim3(B), dim3(kRowThreads), 0, s, h, g, eps, d, nflows,
-                           (float*)x);
+    (void)dtype;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ln_rows_kernel, dim3(B), dim3(kRowThreads), 0, s, h, g, eps, d, nflows, (float*)x);
     return hipGetLastError();
 }
 

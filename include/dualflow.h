@@ -31,9 +31,11 @@
  *    launches nothing. DF_ERR_HIP reports a launch error (the HIP error is
  *    left for the caller to read with hipGetLastError).
  *  - Storage dtype (weights, embeddings, K/V): DF_F32 or DF_BF16. Coupling
- *    vectors and LayerNorm gains are always fp32. Arithmetic is fp32 with
- *    fp32 accumulation; with DF_BF16 every projection input is rounded to
- *    bf16 (nearest-even), as are appended K/V entries.
+ *    vectors and LayerNorm gains are always fp32. Activations are fp32 and
+ *    accumulation is fp32; appended K/V entries are rounded to the storage
+ *    dtype (nearest-even). With DF_BF16 the projections run on bf16 matrix
+ *    cores, each fp32 activation entering as a pair of bf16 parts whose sum
+ *    is within 2^-17 of it.
  *  - Stacked rows: row 2b is the primary flow of sequence b, row 2b+1 its
  *    aux flow ([B][2][...] layouts below).
  *  - Results are deterministic: no atomics take part in any reduction.
@@ -170,7 +172,9 @@ int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t aux
  *  d_a: [n_heads*head_dim] or NULL: if given Q2 = Q2raw + a * Q1.
  *  d_o: [batch][2][n_heads][head_dim] fp32 outputs; d_lse: [batch][2][n_heads]
  *  natural-log sum of exp of the scaled scores. Scores are q.k/sqrt(head_dim).
- *  d_len[b] must lie in [1, max_seq]. */
+ *  d_len[b] must lie in [1, max_seq]; batch <= 64.
+ *  d_ws: df_attention_workspace_bytes bytes, zero-filled before its first
+ *  use (it holds work counters that every call leaves at zero). */
 int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch,
                       int32_t n_heads, int32_t max_seq, int32_t head_dim, const int32_t* d_len,
                       const float* d_q, const float* d_a, float* d_o, float* d_lse,
@@ -178,6 +182,21 @@ int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t b
 
 /* Workspace bytes df_attention_dual needs for these sizes. */
 size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_seq, int32_t head_dim);
+
+/* The stacked-row projection alone (the building block of every shared
+ * weight in the step, gist.science/es/paper/2608.12385, "Arquitectura
+ * Central": both flows use the same matrices):
+ * y[m][n] = sum_k x[m][k] w[n][k] for m < rows.
+ *  d_x: fp32 [rows][K]; d_w: [N][K] in `dtype`; d_y: fp32 [rows][N].
+ *  rows even (primary/aux row pairs), rows <= 128 (DF_F32: rows <= 16);
+ *  DF_BF16: K a multiple of 256. With DF_BF16 each x element enters the
+ *  bf16 matrix cores as two bf16 parts whose sum is within 2^-17 of it.
+ *  d_ws: df_stacked_gemv_workspace_bytes bytes (split-K partial sums). */
+int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t rows, int32_t N, int32_t K,
+                    float* d_y, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of df_stacked_gemv for these sizes (0 if unsupported). */
+size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K);
 
 /* Reads and clears the device status word kept in a decode workspace
  * (bit 0: a K/V write was skipped because len >= max_seq; bit 1: a token

@@ -37,9 +37,11 @@ before the 1/sqrt(Dh) scale; b_l after the GELU; c_l on the MLP output before
 the residual add; alpha = min(1, max(0.5, sum p1^2)); greedy argmax with
 ties to the lowest index; top-k ordered by descending logit with ties to the
 lower expert index, gates are the softmax over the k selected logits of each
-flow. Storage rounding rho (to the storage dtype, round-to-nearest-even) is
-applied to every projection input, to appended K/V and nowhere else;
-couplings read the primary's unrounded values.
+flow. Weights, embeddings and the K/V cache are stored in the storage dtype;
+activations are not rounded: the only rounding rho (to the storage dtype,
+nearest-even) in a step is that of the appended K/V entries. (Rounding every
+projection input to bf16 as well makes full-depth logits move by ~4e-2 under
+fp32-level perturbations, so no two implementations could agree to 2e-2.)
 """
 from __future__ import annotations
 
@@ -55,15 +57,27 @@ from scipy.special import erf
 # --------------------------------------------------------------------------
 
 
-def decode_bf16(u16: np.ndarray) -> np.ndarray:
-    """bf16 bit patterns (uint16) -> float64 values (exact)."""
-    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+def decode_bf16(u16: np.ndarray, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 values (exact): the bits are the
+    upper half of the float32 with the same value. Converted in blocks to keep
+    the temporaries small; `out` (same shape, float64) may be reused."""
+    u = np.ascontiguousarray(u16, dtype=np.uint16)
+    if out is None or out.shape != u.shape:
+        out = np.empty(u.shape, dtype=np.float64)
+    uf, of = u.reshape(-1), out.reshape(-1)
+    n = 1 << 22
+    for i in range(0, uf.size, n):
+        of[i:i + n] = (uf[i:i + n].astype(np.uint32) << 16).view(np.float32)
+    return out
 
 
-def to_f64(raw: np.ndarray) -> np.ndarray:
+def to_f64(raw: np.ndarray, out: Optional[np.ndarray] = None) -> np.ndarray:
     """Decode a stored tensor (uint16 = bf16 bits, or float32) into float64."""
     if raw.dtype == np.uint16:
-        return decode_bf16(raw)
+        return decode_bf16(raw, out)
+    if out is not None and out.shape == raw.shape:
+        out[...] = raw
+        return out
     return np.asarray(raw, dtype=np.float64)
 
 
@@ -182,8 +196,15 @@ class Model:
         n_params = c.L * (4 * c.d * c.d + 2 * c.d * (c.E * c.Fe if c.moe else c.F))
         self.keep = keep_layers if keep_layers is not None else n_params < 64_000_000
         self._layers: Dict[int, dict] = {}
+        self._scratch: Dict[str, np.ndarray] = {}   # decode buffers reused layer to layer
         self._out = None
         self._lnf = None
+
+    def _dec(self, key: str, raw: np.ndarray) -> np.ndarray:
+        if self.keep:
+            return to_f64(raw)
+        self._scratch[key] = to_f64(raw, self._scratch.get(key))
+        return self._scratch[key]
 
     def emb(self, flow: int, tokens) -> np.ndarray:
         return to_f64(self.src.tok_emb_rows(flow, tokens))
@@ -198,19 +219,19 @@ class Model:
         p = {
             "ln1": s.ln_gain("ln1", l).astype(np.float64),
             "ln2": s.ln_gain("ln2", l).astype(np.float64),
-            "w_qkv": to_f64(s.w_qkv(l)),
-            "w_o": to_f64(s.w_o(l)),
+            "w_qkv": self._dec("w_qkv", s.w_qkv(l)),
+            "w_o": self._dec("w_o", s.w_o(l)),
             "a": s.coupling("a", l).astype(np.float64),
             "b": s.coupling("b", l).astype(np.float64),
             "c": s.coupling("c", l).astype(np.float64),
         }
         if c.moe:
-            p["w_router"] = to_f64(s.w_router(l))
-            p["w_eup"] = [to_f64(s.w_exp_up(l, e)) for e in range(c.E)]
-            p["w_edown"] = [to_f64(s.w_exp_down(l, e)) for e in range(c.E)]
+            p["w_router"] = self._dec("w_router", s.w_router(l))
+            p["w_eup"] = [self._dec(f"w_eup{e}", s.w_exp_up(l, e)) for e in range(c.E)]
+            p["w_edown"] = [self._dec(f"w_edown{e}", s.w_exp_down(l, e)) for e in range(c.E)]
         else:
-            p["w_up"] = to_f64(s.w_up(l))
-            p["w_down"] = to_f64(s.w_down(l))
+            p["w_up"] = self._dec("w_up", s.w_up(l))
+            p["w_down"] = self._dec("w_down", s.w_down(l))
         if self.keep:
             self._layers[l] = p
         return p
@@ -253,12 +274,19 @@ class Cache:
         self._k: Dict[int, np.ndarray] = {}
         self._v: Dict[int, np.ndarray] = {}
         self.appended: Dict[tuple, tuple] = {}   # (l, seq, pos) -> (k [H,Dh], v [H,Dh])
+        self._spare = None
 
     def _fill(self, l: int):
         c = self.cfg
         nb = len(self.seqs)
-        k = np.zeros((nb, c.H, c.S_max, c.Dh))
-        v = np.zeros((nb, c.H, c.S_max, c.Dh))
+        if self.lazy and self._spare is not None:
+            k, v = self._spare          # buffers of a released layer, reused
+            self._spare = None
+            k[...] = 0.0
+            v[...] = 0.0
+        else:
+            k = np.zeros((nb, c.H, c.S_max, c.Dh))
+            v = np.zeros((nb, c.H, c.S_max, c.Dh))
         if c.ctx > 0:
             for i, b in enumerate(self.seqs):
                 k[i, :, :c.ctx] = to_f64(self.src.kv_block("k", l, b, c.ctx))
@@ -276,9 +304,8 @@ class Cache:
         return self._k[l], self._v[l]
 
     def release(self, l: int):
-        if self.lazy:
-            self._k.pop(l, None)
-            self._v.pop(l, None)
+        if self.lazy and l in self._k:
+            self._spare = (self._k.pop(l), self._v.pop(l))
 
     def write(self, l: int, i: int, pos: int, k_hd: np.ndarray, v_hd: np.ndarray):
         K, V = self.layer(l)
@@ -351,12 +378,12 @@ def attend(q: np.ndarray, K_bh: np.ndarray, V_bh: np.ndarray, pos: int) -> np.nd
 def _mlp_dense(p: dict, v: np.ndarray, flows: int, dtype: str, tr: Optional[dict] = None):
     """Dense MLP of both flows with the two MLP couplings ([ES] Mecanismos Clave,
     light coupling): g2 = GELU(z2) + b * GELU(z1) (b_l on the post-activation
-    intermediate), then y2 = rho(g2) W2^T + c * y1 (c_l on the MLP output,
-    before the residual add). Primary rows never read aux values."""
+    intermediate), then y2 = g2 W2^T + c * y1 (c_l on the MLP output, before
+    the residual add). Primary rows never read aux values."""
     g = [gelu(_matvec(p["w_up"], v[f])) for f in range(flows)]
     if flows == 2:
         g[1] = couple_mid(g[1], p["b"], g[0])
-    y = [_matvec(p["w_down"], round_to(g[f], dtype)) for f in range(flows)]
+    y = [_matvec(p["w_down"], g[f]) for f in range(flows)]
     if flows == 2:
         y[1] = couple_out(y[1], p["c"], y[0])
     if tr is not None:
@@ -385,7 +412,7 @@ def _mlp_moe(p: dict, v: np.ndarray, flows: int, dtype: str, k: int,
         if flows == 2:
             g[1] = couple_mid(g[1], p["b"], g[0])
         for f in range(flows):
-            y[f] = y[f] + gates[f][j] * _matvec(p["w_edown"][e], round_to(g[f], dtype))
+            y[f] = y[f] + gates[f][j] * _matvec(p["w_edown"][e], g[f])
     if flows == 2:
         y[1] = couple_out(y[1], p["c"], y[0])
     if tr is not None:
@@ -398,11 +425,11 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
     """One grouped decode step for every sequence held by ``cache``.
 
     tokens[i]: token id of sequence cache.seqs[i] at position pos = lens[i].
-    Per layer: u = rho(LN1(h)); primary [Q1 K1 V1] = u1 Wqkv^T; aux Q2 =
+    Per layer: u = LN1(h); primary [Q1 K1 V1] = u1 Wqkv^T; aux Q2 =
     u2 Wq^T + a * Q1 (aux forms a query only and never writes K/V); the cache
     receives rho(K1), rho(V1) at pos; both queries attend positions 0..pos of
-    the primary cache; h += rho(O) Wo^T; v = rho(LN2(h)); MLP (dense or MoE)
-    with b/c couplings; h += y. Then the final LN, the shared LM head and the
+    the primary cache; h += O Wo^T; v = LN2(h); MLP (dense or MoE) with b/c
+    couplings; h += y. Then the final LN, the shared LM head and the
     mixture head. ([ES] Arquitectura Central and Mecanismos Clave; the aux
     flow joins the primary on the shared weights once per step, [ES] Costes.)
 
@@ -431,7 +458,7 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
         g_in = p["ln1"] if g_prev is None else g_prev
         for i in range(nb):
             lt = {} if trace else None
-            u = [round_to(layer_norm(h[i, f], g_in, c.eps), dt) for f in range(flows)]
+            u = [layer_norm(h[i, f], g_in, c.eps) for f in range(flows)]
             q, k_new, v_new = qkv_rows(p, u, c)
             cache.write(l, i, int(pos[i]), k_new, v_new)
             o = np.zeros((flows, c.d))
@@ -440,10 +467,10 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
                 for f in range(flows):
                     o[f, sl] = attend(q[f][sl], K[i, hh], V[i, hh], int(pos[i]))
             for f in range(flows):
-                h[i, f] = h[i, f] + _matvec(p["w_o"], round_to(o[f], dt))
+                h[i, f] = h[i, f] + _matvec(p["w_o"], o[f])
             if trace:
                 lt["h_mid"] = h[i].copy()
-            v = np.stack([round_to(layer_norm(h[i, f], p["ln2"], c.eps), dt) for f in range(flows)])
+            v = np.stack([layer_norm(h[i, f], p["ln2"], c.eps) for f in range(flows)])
             if c.moe:
                 r1 = None if router_logits is None else router_logits[l][i]
                 y, ids, gates = _mlp_moe(p, v, flows, dt, c.top_k, r1, lt)
@@ -468,7 +495,7 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
     nxt = np.zeros(nb, dtype=np.int64)
     for i in range(nb):
         for f in range(flows):
-            logits[i, f] = _matvec(W_out, round_to(layer_norm(h[i, f], model.lnf(), c.eps), dt))
+            logits[i, f] = _matvec(W_out, layer_norm(h[i, f], model.lnf(), c.eps))
         p_mix[i], alpha[i], nxt[i] = mix_head(logits[i, 0], logits[i, 1] if flows == 2 else None)
     cache.lens = cache.lens + 1
     res = StepResult(logits, p_mix, alpha, nxt,
@@ -503,7 +530,7 @@ def prefill_primary(model: Model, cache: Cache, prompt: np.ndarray):
             p = model.layer(l)
             K, V = cache.layer(l)
             g = p["ln1"] if g_in is None else g_in
-            u = round_to(layer_norm(h, g, c.eps), dt)
+            u = layer_norm(h, g, c.eps)
             qkv = u @ p["w_qkv"].T
             Q = qkv[:, :c.d]
             K[i, :, p0:p0 + T] = round_to(qkv[:, c.d:2 * c.d], dt).reshape(T, c.H, c.Dh).transpose(1, 0, 2)
@@ -516,18 +543,18 @@ def prefill_primary(model: Model, cache: Cache, prompt: np.ndarray):
                 for hh in range(c.H):
                     sl = slice(hh * c.Dh, (hh + 1) * c.Dh)
                     O[t, sl], _ = attention_one(Q[t, sl], K[i, hh, :n], V[i, hh, :n])
-            h = h + round_to(O, dt) @ p["w_o"].T
-            v = round_to(layer_norm(h, p["ln2"], c.eps), dt)
+            h = h + O @ p["w_o"].T
+            v = layer_norm(h, p["ln2"], c.eps)
             if c.moe:
                 y = np.zeros_like(h)
                 for t in range(T):
                     yy, _, _ = _mlp_moe(p, v[t:t + 1], 1, dt, c.top_k, None)
                     y[t] = yy[0]
             else:
-                y = round_to(gelu(v @ p["w_up"].T), dt) @ p["w_down"].T
+                y = gelu(v @ p["w_up"].T) @ p["w_down"].T
             h = h + y
             g_in = model.ln_next(l)
-        out[i] = round_to(layer_norm(h, model.lnf(), c.eps), dt) @ model.w_out().T
+        out[i] = layer_norm(h, model.lnf(), c.eps) @ model.w_out().T
     cache.lens = cache.lens + T
     return out
 

@@ -354,7 +354,7 @@ def pin_mid_coupling(cfg):
     independent of b) the aux intermediate with b = 1 equals the aux
     intermediate with b = 0 plus the primary intermediate; with the aux
     embedding tied and b = 1 the aux MLP output is exactly twice the primary
-    one (b acts after the GELU on the unrounded primary activation)."""
+    one (b acts after the GELU, on the primary activation as computed)."""
     if cfg.moe:
         return
     r0, _ = _traced(cfg, {})
@@ -435,8 +435,7 @@ def pin_moe_all_experts_is_full_mixture():
         logits = p["w_router"] @ v[f]
         w = np.exp(logits - logits.max())
         w /= w.sum()
-        want = sum(w[e] * (p["w_edown"][e] @ odf.round_to(odf.gelu(p["w_eup"][e] @ v[f]), "bf16"))
-                   for e in range(cfg.E))
+        want = sum(w[e] * (p["w_edown"][e] @ odf.gelu(p["w_eup"][e] @ v[f])) for e in range(cfg.E))
         assert np.max(np.abs(y[f] - want)) < 1e-12
 
 

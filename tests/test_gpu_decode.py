@@ -25,6 +25,7 @@ SMALL_F32 = Config("gpu_small_f32", L=2, d=128, H=2, Dh=64, F=256, V=300, B=2, c
 SMALL_MOE = Config("gpu_small_moe", L=2, d=256, H=2, Dh=128, F=0, V=512, B=8, ctx=40, S_max=64, dtype="bf16",
                    moe=True, E=16, top_k=4, Fe=256, router_override=True, seed=23, sigma_w=0.05, sigma_ln=0.1)
 LOGIT_TOL, PMIX_TOL = 2e-2, 1e-3
+KV_ABS = 5e-4      # fp32 projection error feeding an appended K/V entry (see test_gpu_fullsize)
 
 
 def _compare_step(cfg, gm: DecodeModel, r: odf.StepResult, aux_on=True):
@@ -65,7 +66,7 @@ def _check_writes(gm, cfg, lens0, cache: odf.Cache, sentinel):
                 got = bits_to_f64(t[l, b, :, lens0[b]], cfg.dtype)
                 ref = cache.appended[(l, b, int(lens0[b]))][0 if name == "k" else 1]
                 ulp = 2.0 ** -7 if cfg.dtype == "bf16" else 2.0 ** -20
-                assert np.all(np.abs(got - ref) <= ulp * np.abs(ref) + 1e-6), f"{name} values l={l} b={b}"
+                assert np.all(np.abs(got - ref) <= ulp * np.abs(ref) + KV_ABS), f"{name} values l={l} b={b}"
 
 
 @pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_F32], ids=lambda c: c.name)

@@ -1,0 +1,62 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times, against the oracle on sampled sequences (sequences are independent,
+so the oracle recomputes a few of them through every layer).
+
+Bars: logits within 2e-2 and p_mix within 1e-3 max-abs; MoE expert ids of
+the sampled sequences bit-exact; each layer's K/V written exactly at
+position len (the next position stays untouched). Appended values: within one
+bf16 ulp of the oracle's plus KV_ABS, the worst-case error of the fp32
+projection feeding them (each activation enters the bf16 matrix cores as
+hi + lo parts within 2^-17 of it: 2^-17 * sum_k |w_k u_k| <= 5e-4 here)."""
+import numpy as np
+import pytest
+import torch
+
+from dual_flow_transformer_amd.runtime import DecodeModel
+from gpu_util import argmax_agrees, bits_to_f64, max_abs, say
+from oracle import dualflow as odf
+from synth.workloads import PRESETS, Inputs
+
+pytestmark = pytest.mark.gpu
+KV_REL, KV_ABS = 2.0 ** -7, 5e-4
+
+
+@pytest.mark.parametrize("name,seqs", [("c3", [0, 15]), ("c4", [0, 41]), ("c5", [0])])
+def test_full_size_sampled(name, seqs):
+    cfg = PRESETS[name]
+    say(f"full-size {cfg.name}: GPU step, oracle on sequences {seqs}")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    tok = src.step_tokens(0)
+    rl = gm.router_logits(0) if cfg.moe else None
+    gm.decode_step(gm.tokens(tok), router_logits=rl)
+    torch.cuda.synchronize()
+    assert gm.status() == 0
+    lg = gm.logits.cpu().numpy()[seqs]
+    pm = gm.p_mix.cpu().numpy()[seqs]
+    al = gm.alpha.cpu().numpy()[seqs]
+    nt = gm.next_tok.cpu().numpy()[seqs]
+    ids = gm.expert_ids.cpu().numpy()[:, seqs] if cfg.moe else None
+    kw = {l: gm.k[l, seqs, :, cfg.ctx:cfg.ctx + 2].cpu() for l in range(cfg.L)}
+    vw = {l: gm.v[l, seqs, :, cfg.ctx:cfg.ctx + 2].cpu() for l in range(cfg.L)}
+    del gm
+    torch.cuda.empty_cache()
+    say("  oracle ...")
+    m = odf.Model(src, keep_layers=False)
+    cache = odf.Cache(cfg, seqs, src, lazy=True)
+    r = odf.decode_step(m, cache, tok[seqs], aux_on=True,
+                        router_logits=None if rl is None else rl.cpu().numpy()[:, seqs])
+    el, ep = max_abs(lg, r.logits), max_abs(pm, r.p_mix)
+    say(f"  logits max|d|={el:.3e} p_mix max|d|={ep:.3e} alpha {al} vs {r.alpha}")
+    assert el < 2e-2 and ep < 1e-3 and max_abs(al, r.alpha) < 1e-3
+    for i in range(len(seqs)):
+        assert argmax_agrees(pm[i], r.p_mix[i], nt[i], margin=2e-3)
+    if cfg.moe:
+        assert np.array_equal(ids, r.ids), "expert ids differ"
+    for l in range(cfg.L):
+        for i, b in enumerate(seqs):
+            for t, which in ((kw[l], 0), (vw[l], 1)):
+                got = bits_to_f64(t[i, :, 0], cfg.dtype)
+                ref = cache.appended[(l, b, cfg.ctx)][which]
+                assert np.all(np.abs(got - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, b, which)
+                assert np.all(t[i, :, 1].numpy() == 0), "write beyond position len"

@@ -58,12 +58,12 @@ def test_mix_head_confident_primary():
     """A peaked primary distribution: collision probability above 0.5."""
     V = 4096
     l = np.zeros((1, 2, V), np.float32)
-    l[0, 0, 17] = 9.0
+    l[0, 0, 17] = 12.0
     l[0, 1] = synth.normal((V,), 3, synth.stream_id("mixc"), 1.0, "f32")
     p, a, t = _mix(l, 1)
     rp, ra, rt = odf.mix_head(l[0, 0], l[0, 1])
     assert ra > 0.5 and abs(a[0] - ra) < 1e-5 and t[0] == rt == 17
-    assert max_abs(p[0], rp) < 1e-6
+    assert np.all(np.abs(p[0] - rp) <= 1e-6 + 1e-5 * rp)      # fp32 relative error on the large entry
 
 
 @pytest.mark.parametrize("dtype", [_abi.DF_BF16, _abi.DF_F32])
@@ -81,8 +81,8 @@ def test_kv_append_positions_and_values(dtype):
     dk = synth.normal((B, H, Dh), 9, synth.stream_id("kva"), 3.0, "f32")
     dv = synth.normal((B, H, Dh), 9, synth.stream_id("kvb"), 3.0, "f32")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    rc = _abi.df_kv_append(cfg, kv, 1, torch.from_numpy(pos).cuda().data_ptr(), torch.from_numpy(dk).cuda().data_ptr(),
-                           torch.from_numpy(dv).cuda().data_ptr(), st.data_ptr(),
+    dpos, ddk, ddv = torch.from_numpy(pos).cuda(), torch.from_numpy(dk).cuda(), torch.from_numpy(dv).cuda()
+    rc = _abi.df_kv_append(cfg, kv, 1, dpos.data_ptr(), ddk.data_ptr(), ddv.data_ptr(), st.data_ptr(),
                            torch.cuda.current_stream().cuda_stream)
     assert rc == 0
     torch.cuda.synchronize()
@@ -101,8 +101,7 @@ def test_kv_append_positions_and_values(dtype):
     # out-of-range positions: nothing written, status flagged
     bad = torch.from_numpy(np.array([S, -1, 3], np.int32)).cuda()
     before = K.clone()
-    rc = _abi.df_kv_append(cfg, kv, 0, bad.data_ptr(), torch.from_numpy(dk).cuda().data_ptr(),
-                           torch.from_numpy(dv).cuda().data_ptr(), st.data_ptr(),
+    rc = _abi.df_kv_append(cfg, kv, 0, bad.data_ptr(), ddk.data_ptr(), ddv.data_ptr(), st.data_ptr(),
                            torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0 and int(st.item()) == 1
