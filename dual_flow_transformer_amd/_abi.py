@@ -27,7 +27,8 @@ DF_BF16 = 1
 
 EXPORTS = ["df_workspace_bytes", "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
            "df_attention_dual", "df_attention_workspace_bytes", "df_device_status", "df_status_str",
-           "df_timing_enable", "df_timing_read", "df_stacked_gemv", "df_stacked_gemv_workspace_bytes"]
+           "df_timing_enable", "df_timing_read", "df_stacked_gemv", "df_stacked_gemv_workspace_bytes",
+           "df_pack_weights"]
 
 
 class df_config(ctypes.Structure):
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.df_stacked_gemv.argtypes = [i32, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         L.df_stacked_gemv_workspace_bytes.restype = sz
         L.df_stacked_gemv_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.df_pack_weights.restype = ctypes.c_int
+        L.df_pack_weights.argtypes = [i32, vp, vp, ctypes.c_int64, i32, i32, vp]
         L.df_timing_enable.restype = ctypes.c_int
         L.df_timing_enable.argtypes = [i32]
         L.df_timing_read.restype = ctypes.c_int
@@ -157,6 +160,10 @@ def df_stacked_gemv(dtype, d_x, d_w, rows, N, K, d_y, d_ws, ws_bytes, stream=0) 
 
 def df_stacked_gemv_workspace_bytes(dtype, rows, N, K) -> int:
     return int(lib().df_stacked_gemv_workspace_bytes(int(dtype), int(rows), int(N), int(K)))
+
+
+def df_pack_weights(dtype, d_src, d_dst, n_mats, rows, cols, stream=0) -> int:
+    return lib().df_pack_weights(int(dtype), d_src, d_dst, int(n_mats), int(rows), int(cols), stream)
 
 
 def df_timing_enable(kclass: int = 0) -> int:

@@ -352,9 +352,10 @@ int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t b
 
 size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K) {
     if ((dtype != DF_F32 && dtype != DF_BF16) || rows < 2 || (rows & 1) || N < 1 || K < 1) return 0;
-    if (dtype == DF_BF16 && (rows > 128 || K % 256)) return 0;
+    if (dtype == DF_BF16 && (rows > 128 || K % 256 || N % 16)) return 0;
     if (dtype == DF_F32 && (rows > 16 || K % 4)) return 0;
     const dfk::GemvPlan pl = dfk::plan_gemv(dtype, N, K, rows);
+    if (dtype == DF_BF16 && pl.MT == 0) return 0;
     return align_up(pl.part_floats * 4 + kAlign);
 }
 
@@ -370,6 +371,22 @@ int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t ro
     g.dtype = dtype; g.x = d_x; g.w = d_w; g.N = N; g.K = K; g.B = rows / 2; g.nflows = 2;
     g.epi = dfk::EPI_STORE; g.out_f32 = d_y; g.part = reinterpret_cast<float*>(d_ws);
     return dfk::gemv(g, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+int df_pack_weights(int32_t dtype, const void* d_src, void* d_dst, int64_t n_mats, int32_t rows, int32_t cols,
+                    void* stream) {
+    if (dtype != DF_BF16) return DF_ERR_DTYPE;
+    if (!d_src || !d_dst) return DF_ERR_NULL;
+    if (n_mats < 1 || n_mats > 65535 || rows < 16 || cols < 32 || rows % 16 || cols % 32) return DF_ERR_SHAPE;
+    if (!aligned16(d_src) || !aligned16(d_dst)) return DF_ERR_ALIGN;
+    const size_t bytes = (size_t)n_mats * rows * cols * 2;
+    const char* a = reinterpret_cast<const char*>(d_src);
+    const char* b = reinterpret_cast<const char*>(d_dst);
+    if (a < b + bytes && b < a + bytes) return DF_ERR_ARG;   // overlapping buffers
+    return dfk::pack_weights(d_src, d_dst, (long)n_mats, rows, cols, reinterpret_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? DF_OK
+               : DF_ERR_HIP;
 }
 
 int df_device_status(void* d_ws, void* stream, int32_t* status_out) {

@@ -71,7 +71,7 @@ enum EpiKind {
 struct GemvArgs {
     int dtype;
     const void* x;        // [2B][K] stacked rows, fp32
-    const void* w;        // [N][K] storage dtype
+    const void* w;        // bf16: [N][K] in the 16x32 fragment layout; fp32: row-major [N][K]
     int N, K;
     int B;                // sequences
     int nflows;           // 2 or 1 (1: only rows 2b are read and written)
@@ -92,7 +92,10 @@ struct GemvArgs {
     float eps;
 };
 struct GemvPlan {
-    int MT, ks, S, nblocks;
+    int MT;               // 16-row activation tiles (0: shape not supported)
+    int variant;          // kernel shape
+    int ks, S;            // k-slice width and count
+    int grid, nblocks;    // workgroups; row groups per slice
     size_t lds, part_floats;
 };
 GemvPlan plan_gemv(int dtype, int N, int K, int M);
@@ -106,8 +109,8 @@ struct MoeArgs {
     const float* x;         // [2B][d] LN2(h) rows (fp32)
     const float* r;         // [2B][E] router logits (computed)
     const float* r1_given;  // [B][E] primary logits supplied, or nullptr
-    const void* w_up;       // [E][Fe][d]
-    const void* w_down;     // [E][d][Fe]
+    const void* w_up;       // [E][Fe][d]  (fragment layout per expert)
+    const void* w_down;     // [E][d][Fe]  (fragment layout per expert)
     const float* cpl_b;     // [Fe]
     const float* cpl_c;     // [d]
     int B, d, E, k, Fe, nflows;
@@ -126,5 +129,10 @@ struct MoeArgs {
     float* y_rows;          // [B*k][2][d]
 };
 hipError_t moe(const MoeArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Row-major bf16 [n_mats][rows][cols] to the 16x32 fragment layout.
+// ---------------------------------------------------------------------------
+hipError_t pack_weights(const void* src, void* dst, long n_mats, int rows, int cols, hipStream_t s);
 
 }  // namespace dfk

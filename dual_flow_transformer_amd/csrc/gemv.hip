@@ -8,13 +8,12 @@
 // Y[m][n] = sum_k X[m][k] W[n][k] over the M = 2B stacked rows
 // (row 2b = primary, 2b+1 = aux of sequence b).
 //
-// bf16 path (v_mfma_f32_16x16x32_bf16): a workgroup owns 32 weight rows
-// (two 16-row A tiles) and splits K across its waves; each lane streams
-// 16-byte pieces of weight rows (A operand: row = lane%16, k-group =
-// lane/16) and of activation rows (B operand: column = stacked row).
-// The per-wave partial sums meet in LDS in a fixed order, then one fused
-// epilogue per output element: plain store, Q coupling + K/V append, GELU +
-// b coupling, or c coupling + residual add. fp32 path (fp32 storage): one
+// bf16 path: v_mfma_f32_16x16x32_bf16 with the weights as the A operand,
+// read from the 16x32 fragment layout (mfma_tile.h), the activation rows as
+// the B operand from LDS; split over k-slices, persistent over row tiles;
+// partial sums are finished by a reduce kernel with one of the epilogues:
+// plain store, Q coupling + K/V append, GELU + b coupling, or c coupling +
+// residual add (then LayerNorm). fp32 path (fp32 storage, row-major): one
 // wave per weight row, lanes split K, wave reduction, same epilogues.
 #include <algorithm>
 
@@ -28,13 +27,15 @@ namespace {
 
 using tile::f32x4;
 
+constexpr int kCUs = 256;   // compute units of the MI355X
+
 struct GParams {
     const void* x;
     const void* w;
     int N, K;
     int M;          // logical rows: 2B (dual) or B (primary only)
     int row_step;   // physical stacked row of logical row m is m * row_step
-    int nflows, B, kw;
+    int nflows, B;
     int epi;
     float* out_f32;
     float* h;
@@ -46,6 +47,7 @@ struct GParams {
     const int32_t* len;
     int H, Dh, S_max;
     int32_t* status;
+    int S;                // k-slices
     float* part;          // split-K partials [S][M][N]
     const float* ln_gain; // EPI_RESID_LN: gain of the norm that follows
     float eps;
@@ -101,12 +103,9 @@ __device__ __forceinline__ void epilogue(const GParams& p, int n, int b, float y
 typedef tile::u32x4 u32x4;
 typedef tile::bf16x8 bf16x8;
 
-constexpr int NWAVE = 8;         // waves per workgroup, 16 weight rows each
-constexpr int WG_ROWS = 16 * NWAVE;
-
 // Epilogue from MFMA registers: lane l holds D[4*(l/16) + r][l%16] of its
-// wave's 16 rows x 16 stacked rows (per m tile). With both flows, the aux
-// row 2b+1 sits in the neighbouring lane of the primary row 2b.
+// wave's 16 weight rows x 16 stacked rows (per m tile). With both flows, the
+// aux row 2b+1 sits in the neighbouring lane of the primary row 2b.
 template <int MT>
 __device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&acc)[MT], int n_base, int lane) {
     const int li = lane & 15, lg = lane >> 4;
@@ -129,114 +128,147 @@ __device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&ac
     }
 }
 
-// Y = X W^T for NWAVE*16 weight rows over one k-slice [s*ks, (s+1)*ks).
-// Activation rows are fp32; while the k-slice is staged in LDS each value is
+// Y = X W^T over one k-slice of KS columns, persistent over row tiles.
+//
+// Workgroup g works on slice s = g % S for a contiguous range of row tiles
+// (16*RT weight rows each); its waves take the tiles of that range in turn.
+// The activation slice is staged once per workgroup: each fp32 value is
 // split into bf16 hi = rne(x) and lo = rne(x - hi) (x - hi - lo is below
-// 2^-17 |x|), and both parts go through the matrix cores into the same fp32
-// accumulator. LDS rows are padded by 8 elements against bank conflicts and
-// shared by the waves; each wave streams its 16 weight rows from HBM with the
-// next KU chunks already in flight. With S = gridDim.y > 1 slices, every
-// workgroup writes its partial sums and the last one to finish (atomic
-// counter per row block) adds the S partials in slice order and runs the
-// epilogue: deterministic, no float atomics.
-template <int MT, int KU>
-__global__ __launch_bounds__(NWAVE * 64) void gemv_bf16(GParams p) {
+// 2^-17 |x|) and both parts go through the matrix cores into the same fp32
+// accumulator. Weights are read in the 16x32 fragment layout, so every
+// wave-wide load is one contiguous 1 KiB piece, and a wave's tile slice is
+// one contiguous run; the next KU fragments per tile are always in flight,
+// across tile boundaries too. Loads are issued without branches (an
+// iteration past the end reads a fixed hot address) so the compiler's wait
+// counts stay exact. With S > 1 each tile's partial sums go to
+// part[s][m][n] and a reduce kernel finishes in slice order; with S == 1
+// the epilogue runs from the registers.
+template <int MT, int RT, int KU, int NW, int KS>
+__global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     extern __shared__ bf16_t xs[];
+    constexpr int TR = 16 * RT, XS = KS + 8, IPT = KS / (32 * KU);
+    constexpr int C4 = KS / 4, NI = 16 * MT * C4, XB = (NI + NW * 64 - 1) / (NW * 64);
+    static_assert(KS % (32 * KU) == 0, "k-slice");
+    static_assert(XB <= 16, "activation staging registers");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int blk = blockIdx.x, sl = blockIdx.y, S = gridDim.y;
-    const int n_base = blk * WG_ROWS + wv * 16;
-    const int ks = p.kw, ks0 = sl * ks;
-    const int XS = ks + 8;
-    bf16_t* xs_hi = xs;
-    bf16_t* xs_lo = xs + 16 * MT * XS;
     const int li = lane & 15, lg = lane >> 4;
+    const int S = p.S;
+    const int s = blockIdx.x % S, grp = blockIdx.x / S, ngrp = gridDim.x / S;
+    const int n_tiles = (p.N + TR - 1) / TR;
+    const int t_lo = (int)((long)grp * n_tiles / ngrp), t_hi = (int)((long)(grp + 1) * n_tiles / ngrp);
+    const int my_tiles = t_hi - t_lo > wv ? (t_hi - t_lo - wv + NW - 1) / NW : 0;
+    const int n_it = my_tiles * IPT;
+    const int ks0 = s * KS, KB = p.K / 32, NT16 = p.N / 16;
     const bf16_t* W = reinterpret_cast<const bf16_t*>(p.w);
     const float* X = reinterpret_cast<const float*>(p.x);
-    const bf16_t* wp = W + (size_t)min(n_base + li, p.N - 1) * p.K + ks0 + lg * 8;
+    const bf16_t* dummy = reinterpret_cast<const bf16_t*>(X);
+    bf16_t* xh = xs;
+    bf16_t* xl = xs + 16 * MT * XS;
 
-    u32x4 a0[KU];
+    auto load = [&](int it, u32x4 (&a)[RT][KU]) {
+        const bool real = it < n_it;
+        const int j = it / IPT, kb = it - j * IPT;
+        const int tile = t_lo + wv + j * NW;
+        #pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int t16 = min(tile * RT + rt, NT16 - 1);
+            const bf16_t* q = W + (((size_t)t16 * KB + ks0 / 32 + kb * KU) * 64 + lane) * 8;
+            q = real ? q : dummy;
+            #pragma unroll
+            for (int ku = 0; ku < KU; ++ku)
+                a[rt][ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + (real ? 512 * ku : 0)));
+        }
+    };
+
+    // activation loads first, then the first weight fragments, then the split
+    float4 xv[XB];
     #pragma unroll
-    for (int ku = 0; ku < KU; ++ku) a0[ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + 32 * ku));
-
-    // Stage the activation k-slice (loads of a batch issued before any is used).
-    const int c4 = ks >> 2, n_items = 16 * MT * c4;
-    constexpr int SB = 8;
-    for (int i0 = threadIdx.x; i0 < n_items; i0 += SB * NWAVE * 64) {
-        float4 v[SB];
-        #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const int i = i0 + u * NWAVE * 64;
-            if (i < n_items) {
-                const int m = i / c4, c = i - m * c4;
-                const int mm = min(m, p.M - 1);
-                v[u] = *reinterpret_cast<const float4*>(X + (size_t)(mm * p.row_step) * p.K + ks0 + c * 4);
-            }
-        }
-        #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const int i = i0 + u * NWAVE * 64;
-            if (i < n_items) {
-                const int m = i / c4, c = i - m * c4;
-                const bf16_t h0 = df::f32_to_bf16(v[u].x), h1 = df::f32_to_bf16(v[u].y);
-                const bf16_t h2 = df::f32_to_bf16(v[u].z), h3 = df::f32_to_bf16(v[u].w);
-                const bf16_t l0 = df::f32_to_bf16(v[u].x - df::bf16_to_f32(h0));
-                const bf16_t l1 = df::f32_to_bf16(v[u].y - df::bf16_to_f32(h1));
-                const bf16_t l2 = df::f32_to_bf16(v[u].z - df::bf16_to_f32(h2));
-                const bf16_t l3 = df::f32_to_bf16(v[u].w - df::bf16_to_f32(h3));
-                uint2 hv, lv;
-                hv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                hv.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-                lv.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
-                lv.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
-                *reinterpret_cast<uint2*>(xs_hi + m * XS + c * 4) = hv;
-                *reinterpret_cast<uint2*>(xs_lo + m * XS + c * 4) = lv;
-            }
-        }
+    for (int u = 0; u < XB; ++u) {
+        const int i = min((int)threadIdx.x + u * NW * 64, NI - 1);
+        const int m = i / C4, c = i - m * C4;
+        xv[u] = *reinterpret_cast<const float4*>(X + (size_t)(min(m, p.M - 1) * p.row_step) * p.K + ks0 + c * 4);
+    }
+    u32x4 a0[RT][KU], a1[RT][KU];
+    load(0, a0);
+    #pragma unroll
+    for (int u = 0; u < XB; ++u) {
+        const int i = threadIdx.x + u * NW * 64;
+        if (i >= NI) break;
+        const int m = i / C4, c = i - m * C4;
+        const float4 v = xv[u];
+        const bf16_t h0 = df::f32_to_bf16(v.x), h1 = df::f32_to_bf16(v.y);
+        const bf16_t h2 = df::f32_to_bf16(v.z), h3 = df::f32_to_bf16(v.w);
+        const bf16_t l0 = df::f32_to_bf16(v.x - df::bf16_to_f32(h0));
+        const bf16_t l1 = df::f32_to_bf16(v.y - df::bf16_to_f32(h1));
+        const bf16_t l2 = df::f32_to_bf16(v.z - df::bf16_to_f32(h2));
+        const bf16_t l3 = df::f32_to_bf16(v.w - df::bf16_to_f32(h3));
+        uint2 hv, lv;
+        hv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        hv.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+        lv.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        lv.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+        *reinterpret_cast<uint2*>(xh + m * XS + c * 4) = hv;
+        *reinterpret_cast<uint2*>(xl + m * XS + c * 4) = lv;
     }
     __syncthreads();
 
-    f32x4 acc[MT];
+    f32x4 acc[RT][MT];
     #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int xoff = li * XS + lg * 8;
-    for (int kk = 0; kk < ks; kk += 32 * KU) {
-        const bool more = kk + 32 * KU < ks;
-        u32x4 a1[KU];
-        if (more) {
-            #pragma unroll
-            for (int ku = 0; ku < KU; ++ku)
-                a1[ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + kk + 32 * KU + 32 * ku));
-        }
+    for (int rt = 0; rt < RT; ++rt)
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int xo = li * XS + lg * 8;
+
+    auto step = [&](int it, u32x4 (&cur)[RT][KU], u32x4 (&nxt)[RT][KU]) {
+        load(it + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        const int j = it / IPT, kb = it - j * IPT;
+        const int kk = kb * 32 * KU;
         #pragma unroll
         for (int ku = 0; ku < KU; ++ku) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, a0[ku]);
+            bf16x8 bh[MT], bl[MT];
             #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int o = xoff + mt * 16 * XS + kk + 32 * ku;
-                const u32x4 bh = *reinterpret_cast<const u32x4*>(xs_hi + o);
-                const u32x4 bl = *reinterpret_cast<const u32x4*>(xs_lo + o);
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bh), acc[mt], 0, 0, 0);
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl), acc[mt], 0, 0, 0);
+                const int o = xo + mt * 16 * XS + kk + 32 * ku;
+                bh[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xh + o));
+                bl[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + o));
+            }
+            #pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, cur[rt][ku]);
+                #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[mt], acc[rt][mt], 0, 0, 0);
+                    acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[mt], acc[rt][mt], 0, 0, 0);
+                }
             }
         }
-        if (more) {
+        if (kb == IPT - 1) {   // tile done
+            const int tile = t_lo + wv + j * NW;
             #pragma unroll
-            for (int ku = 0; ku < KU; ++ku) a0[ku] = a1[ku];
-        }
-    }
-
-    if (S > 1 || p.epi == EPI_RESID_LN) {
-        // partial sums of this k-slice: part[sl][m][n]; a reduce kernel finishes
-        #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = n_base + 4 * lg + r, m = mt * 16 + li;
-                if (n < p.N && m < p.M) p.part[((size_t)sl * p.M + m) * p.N + n] = acc[mt][r];
+            for (int rt = 0; rt < RT; ++rt) {
+                const int nb = tile * TR + rt * 16;
+                if (S > 1 || p.epi == EPI_RESID_LN) {
+                    #pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const int m = mt * 16 + li, n0 = nb + 4 * lg;
+                        if (n0 < p.N && m < p.M)
+                            *reinterpret_cast<f32x4*>(p.part + ((size_t)s * p.M + m) * p.N + n0) = acc[rt][mt];
+                    }
+                } else {
+                    epilogue_regs<MT>(p, acc[rt], nb, lane);
+                }
+                #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
-        return;
+        }
+    };
+    int it = 0;
+    for (; it + 1 < n_it; it += 2) {
+        step(it, a0, a1);
+        step(it + 1, a1, a0);
     }
-    epilogue_regs<MT>(p, acc, n_base, lane);
+    if (it < n_it) step(it, a0, a1);
 }
 
 // Sum of the S k-slice partials of logical row m, column n (slice order;
@@ -328,18 +360,39 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
     }
 }
 
-template <int MT>
-constexpr int ku_of() { return MT <= 2 ? 8 : (MT == 4 ? 4 : 2); }
+// Kernel shapes: A = 16-row tiles, 8 waves, 8 fragments in flight per tile
+// (4 with 64 or more stacked rows); B = 32-row tiles, 4 waves, 4 fragments
+// per tile (matrices with fewer than 8192 rows).
+enum Variant { VAR_A = 0, VAR_B = 1 };
 
-template <int MT>
-hipError_t launch_bf16(GParams& p, const GemvPlan& pl, hipStream_t s) {
-    constexpr int KU = ku_of<MT>();
-    p.kw = pl.ks;
-    hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&gemv_bf16<MT, KU>), pl.lds);
+template <int MT, int RT, int KU, int NW, int KS>
+hipError_t launch_one(GParams& p, const GemvPlan& pl, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&gemv_bf16<MT, RT, KU, NW, KS>);
+    hipError_t e = tile::allow_lds(fn, pl.lds);
     if (e != hipSuccess) return e;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemv_bf16<MT, KU>), dim3(pl.nblocks, pl.S), dim3(NWAVE * 64), pl.lds, s, p);
+    hipLaunchKernelGGL((gemv_bf16<MT, RT, KU, NW, KS>), dim3(pl.grid), dim3(NW * 64), pl.lds, s, p);
     return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_mt(GParams& p, const GemvPlan& pl, hipStream_t s) {
+    if (pl.variant == VAR_B) {
+        if constexpr (MT <= 2) {
+            if (pl.ks == 512) return launch_one<MT, 2, 4, 4, 512>(p, pl, s);
+            if (pl.ks == 256) return launch_one<MT, 2, 4, 4, 256>(p, pl, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    constexpr int KU = MT >= 4 ? 4 : 8;   // register budget of the wider activation tiles
+    if constexpr (MT <= 2) {
+        if (pl.ks == 1024) return launch_one<MT, 1, KU, 8, 1024>(p, pl, s);
+    }
+    if constexpr (MT <= 4) {
+        if (pl.ks == 512) return launch_one<MT, 1, KU, 8, 512>(p, pl, s);
+    }
+    if (pl.ks == 256) return launch_one<MT, 1, KU, 8, 256>(p, pl, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t finish(GParams& p, int S, hipStream_t s) {
@@ -362,30 +415,26 @@ hipError_t finish(GParams& p, int S, hipStream_t s) {
 
 GemvPlan plan_gemv(int dtype, int N, int K, int M) {
     GemvPlan pl{};
-    if (dtype != DF_BF16) return pl;
-    int mt = (M + 15) / 16;
+    if (dtype != DF_BF16 || M < 1 || M > 128 || N < 16 || N % 16 || K < 256 || K % 256) return pl;
+    const int mt = (M + 15) / 16;
     pl.MT = mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
-    pl.nblocks = (N + WG_ROWS - 1) / WG_ROWS;
-    // k-slice: a divisor of K, multiple of 32*KU, activation slice (hi and lo
-    // parts) in LDS small enough for two workgroups per CU; smaller slices
-    // until about two workgroups per CU are in the grid.
-    const int KU = pl.MT <= 2 ? 8 : (pl.MT == 4 ? 4 : 2);
-    const int step = 32 * KU;
-    auto lds_of = [&](int ks) { return (size_t)2 * 16 * pl.MT * (ks + 8) * 2; };
-    int best = step;
-    for (int ks = step; ks <= K && ks <= 512; ks += step)
-        if (K % ks == 0 && lds_of(ks) <= 78 * 1024) best = ks;
-    int ks = best;
-    while ((long)pl.nblocks * (K / ks) < 512) {
-        int nxt = 0;
-        for (int c = step; c < ks; c += step)
-            if (K % c == 0) nxt = c;
-        if (nxt == 0) break;
-        ks = nxt;
-    }
+    pl.variant = (pl.MT <= 2 && N < 8192) ? VAR_B : VAR_A;
+    const int ks_max = pl.variant == VAR_B ? 512 : (pl.MT <= 2 ? 1024 : pl.MT == 4 ? 512 : 256);
+    int ks = 256;
+    for (int c = ks_max; c >= 256; c /= 2)
+        if (K % c == 0) { ks = c; break; }
     pl.ks = ks;
     pl.S = K / ks;
-    pl.lds = lds_of(ks);
+    pl.lds = (size_t)2 * 16 * pl.MT * (ks + 8) * 2;
+    // one or two resident workgroups per CU (LDS permitting), split over the
+    // k-slices; no more row groups than row tiles
+    const int wg_per_cu = pl.lds <= 80 * 1024 ? 2 : 1;
+    const int rt = pl.variant == VAR_B ? 2 : 1;
+    const int n_tiles = (N + 16 * rt - 1) / (16 * rt);
+    int ngrp = std::max(1, kCUs * wg_per_cu / pl.S);
+    ngrp = std::min(ngrp, n_tiles);
+    pl.grid = ngrp * pl.S;
+    pl.nblocks = ngrp;
     pl.part_floats = (size_t)pl.S * M * N;   // used when S > 1 or before a residual + norm
     return pl;
 }
@@ -398,7 +447,6 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     p.epi = a.epi; p.out_f32 = a.out_f32; p.h = a.h; p.x_out = a.x_out; p.cpl = a.cpl; p.q_out = a.q_out;
     p.kc = a.kc; p.vc = a.vc; p.len = a.len; p.H = a.H; p.Dh = a.Dh; p.S_max = a.S_max; p.status = a.status;
     p.part = a.part; p.ln_gain = a.ln_gain; p.eps = a.eps;
-    p.kw = a.K;
     if (a.dtype == DF_F32) {
         if (p.M > 16) return hipErrorInvalidValue;
         if (a.epi == EPI_RESID_LN && (!a.part || a.N > 4096)) return hipErrorInvalidValue;
@@ -408,16 +456,17 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         return finish(p, 1, s);
     }
-    if (p.M > 128 || (a.K % 256) != 0) return hipErrorInvalidValue;
     const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M);
+    if (pl.MT == 0) return hipErrorInvalidValue;
+    p.S = pl.S;
     if ((pl.S > 1 || a.epi == EPI_RESID_LN) && !a.part) return hipErrorInvalidValue;
     if (a.epi == EPI_RESID_LN && a.N > 4096) return hipErrorInvalidValue;
     hipError_t e;
     switch (pl.MT) {
-        case 1: e = launch_bf16<1>(p, pl, s); break;
-        case 2: e = launch_bf16<2>(p, pl, s); break;
-        case 4: e = launch_bf16<4>(p, pl, s); break;
-        default: e = launch_bf16<8>(p, pl, s); break;
+        case 1: e = launch_mt<1>(p, pl, s); break;
+        case 2: e = launch_mt<2>(p, pl, s); break;
+        case 4: e = launch_mt<4>(p, pl, s); break;
+        default: e = launch_mt<8>(p, pl, s); break;
     }
     if (e != hipSuccess) return e;
     return finish(p, pl.S, s);

@@ -5,9 +5,16 @@
 // Operand layout of one 16x16x32 product D = A B (A: 16 x 32, B: 32 x 16):
 // lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16] as
 // eight bf16 each, and receives D[4*(l/16) + r][l%16] in register r.
-// Here A is a 16-row tile of a weight matrix (each lane loads 16
-// contiguous bytes of one weight row) and B the transposed activation rows,
-// so D[i][j] = partial sum of weight row i with stacked row j.
+// Here A is a 16-row tile of a weight matrix and B the transposed
+// activation rows, so D[i][j] = partial sum of weight row i with stacked
+// row j.
+//
+// Weight fragment layout (bf16 [N][K], N % 16 == 0, K % 32 == 0): the A
+// operand of 16-row tile t and 32-column block kb is stored as 64
+// consecutive 16-byte pieces in lane order,
+//   element (n, k) at ((n/16 * K/32 + k/32) * 64 + ((k%32)/8) * 16 + n%16) * 8 + k%8,
+// so a wave-wide load of one operand is one contiguous 1 KiB piece and the
+// k-blocks of a tile follow each other.
 #pragma once
 
 #include "df_device.h"
@@ -41,9 +48,15 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
     lo = (u32x4){l[0], l[1], l[2], l[3]};
 }
 
+// Lane's base of 16-row tile t16 in the fragment layout (k-block 0).
+__device__ __forceinline__ const bf16_t* frag_tile(const bf16_t* w, int t16, int K, int lane) {
+    return w + ((size_t)t16 * (K / 32) * 64 + lane) * 8;
+}
+
 // Stream k in [kbeg, kend) (multiple of 32*KU) through MFMAs for RT weight
-// tiles against the first `mtiles` activation tiles (wave-uniform). The fp32
-// activation rows enter as bf16 hi and lo parts into the same accumulator.
+// tiles (lane bases from frag_tile) against the first `mtiles` activation
+// tiles (wave-uniform). The fp32 activation rows enter as bf16 hi and lo
+// parts into the same accumulator.
 template <int MT, int KU>
 __device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const float* const (&xrow)[MT],
                                          int mtiles, int kbeg, int kend, f32x4 (&acc)[RT][MT]) {
@@ -53,7 +66,8 @@ __device__ __forceinline__ void stream_k(const bf16_t* const (&wrow)[RT], const 
         for (int rt = 0; rt < RT; ++rt)
             #pragma unroll
             for (int ku = 0; ku < KU; ++ku)
-                a[rt][ku] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[rt] + k + 32 * ku));
+                a[rt][ku] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(wrow[rt] + (size_t)(k / 32 + ku) * 512));
         #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             if (mt < mtiles) {

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void moe_route(const float* r, const float* r1
 
 struct ExpParams {
     const float* x;        // up: [2B][d] rows; down: g_rows [P][2][Fe] (fp32)
-    const bf16_t* w;       // [E][N][K]
+    const bf16_t* w;       // [E][N][K], each expert matrix in the fragment layout
     int N, K, k, nflows, kw;
     const int32_t* offsets;
     const int32_t* perm;
@@ -126,10 +126,7 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
     const bf16_t* W = p.w + (size_t)e * p.N * p.K;
     const bf16_t* wrow[RT];
     #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int n = min(n0 + rt * 16 + li, p.N - 1);
-        wrow[rt] = W + (size_t)n * p.K + lg * 8;
-    }
+    for (int rt = 0; rt < RT; ++rt) wrow[rt] = tile::frag_tile(W, min(n0 / 16 + rt, p.N / 16 - 1), p.K, lane);
     // Several passes when one expert holds more than MT*16 stacked rows.
     for (int mbase = 0; mbase < M; mbase += MT * 16) {
         const int mt_here = min((M - mbase + 15) / 16, mtiles);

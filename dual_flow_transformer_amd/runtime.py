@@ -28,7 +28,10 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 class DecodeModel:
-    """Weights, K/V cache, workspace and outputs of one workload on a GPU."""
+    """Weights, K/V cache, workspace and outputs of one workload on a GPU.
+
+    bf16 projection matrices are generated row-major and then repacked on the
+    device into the fragment layout the library reads (df_pack_weights)."""
 
     def __init__(self, cfg: Config, device: str = "cuda", fill: str = "device", src: Optional[Inputs] = None,
                  max_seq: Optional[int] = None):
@@ -150,6 +153,17 @@ class DecodeModel:
             self._up(self.w_out, s.w_out())
         else:
             raise ValueError(mode)
+        if self.bf16:   # bf16 projection matrices go to the matrix-core fragment layout
+            self._pack(self.w_qkv, c.L, 3 * c.d, c.d)
+            self._pack(self.w_o, c.L, c.d, c.d)
+            if c.moe:
+                self._pack(self.w_router, c.L, c.E, c.d)
+                self._pack(self.w_eup, c.L * c.E, c.Fe, c.d)
+                self._pack(self.w_edown, c.L * c.E, c.d, c.Fe)
+            else:
+                self._pack(self.w_up, c.L, c.F, c.d)
+                self._pack(self.w_down, c.L, c.d, c.F)
+            self._pack(self.w_out, 1, c.V, c.d)
         # small fp32 parameters always come from the host generator
         for l in range(c.L):
             self.ln1[l] = torch.from_numpy(s.ln_gain("ln1", l))
@@ -159,6 +173,15 @@ class DecodeModel:
             self.cpl_c[l] = torch.from_numpy(s.coupling("c", l))
         self.lnf.copy_(torch.from_numpy(s.ln_gain("lnf", 0)))
         torch.cuda.synchronize(self.dev)
+
+    def _pack(self, t: torch.Tensor, n_mats: int, rows: int, cols: int):
+        """Row-major bf16 matrices in `t` to the fragment layout, in place
+        (through a temporary copy)."""
+        src = t.clone()
+        _abi.check(_abi.df_pack_weights(_abi.DF_BF16, src.data_ptr(), t.data_ptr(), n_mats, rows, cols, _stream()),
+                   "df_pack_weights")
+        torch.cuda.synchronize(self.dev)
+        del src
 
     def tokens(self, arr) -> torch.Tensor:
         return torch.as_tensor(np.asarray(arr, dtype=np.int32), device=self.dev)

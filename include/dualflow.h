@@ -85,8 +85,12 @@ typedef struct df_config {
     float ln_eps;        /* LayerNorm epsilon */
 } df_config;
 
-/* Parameters, all device pointers, row-major, layer-major stacks.
- * Projection matrices are [out][in] (a GEMV reads whole rows). */
+/* Parameters, all device pointers, layer-major stacks. Embeddings and
+ * position tables are row-major. Projection matrices are [out][in]
+ * (w[n][k] multiplies input k into output n): with DF_F32 row-major, with
+ * DF_BF16 in the 16x32 fragment layout of df_pack_weights, each matrix of a
+ * stack packed on its own (the layout every wave-wide weight load of the
+ * bf16 matrix cores reads as one contiguous 1 KiB piece). */
 typedef struct df_weights {
     const void* tok_emb[2];    /* [vocab][d]: primary (0), aux (1) */
     const void* pos_emb;       /* [max_seq][d], shared by both flows */
@@ -187,16 +191,29 @@ size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_
  * weight in the step, gist.science/es/paper/2608.12385, "Arquitectura
  * Central": both flows use the same matrices):
  * y[m][n] = sum_k x[m][k] w[n][k] for m < rows.
- *  d_x: fp32 [rows][K]; d_w: [N][K] in `dtype`; d_y: fp32 [rows][N].
+ *  d_x: fp32 [rows][K]; d_w: [N][K] in `dtype` (DF_F32 row-major, DF_BF16
+ *  in the fragment layout of df_pack_weights); d_y: fp32 [rows][N].
  *  rows even (primary/aux row pairs), rows <= 128 (DF_F32: rows <= 16);
- *  DF_BF16: K a multiple of 256. With DF_BF16 each x element enters the
- *  bf16 matrix cores as two bf16 parts whose sum is within 2^-17 of it.
+ *  DF_BF16: K a multiple of 256, N a multiple of 16. With DF_BF16 each x
+ *  element enters the bf16 matrix cores as two bf16 parts whose sum is
+ *  within 2^-17 of it.
  *  d_ws: df_stacked_gemv_workspace_bytes bytes (split-K partial sums). */
 int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t rows, int32_t N, int32_t K,
                     float* d_y, void* d_ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes of df_stacked_gemv for these sizes (0 if unsupported). */
 size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K);
+
+/* Repacks n_mats row-major bf16 matrices [rows][cols] (consecutive in
+ * d_src) into the 16x32 fragment layout at d_dst (same size, no overlap):
+ * element (n, k) of a matrix goes to
+ *   ((n/16 * cols/32 + k/32) * 64 + ((k%32)/8) * 16 + n%16) * 8 + k%8,
+ * i.e. each 16-row x 32-column block becomes 64 groups of 8 consecutive k
+ * in the order the bf16 matrix-core A operand takes them (group
+ * (k%32)/8 * 16 + n%16 belongs to lane of that number). DF_BF16 only;
+ * rows % 16 == 0, cols % 32 == 0. Asynchronous on `stream`. */
+int df_pack_weights(int32_t dtype, const void* d_src, void* d_dst, int64_t n_mats, int32_t rows, int32_t cols,
+                    void* stream);
 
 /* Reads and clears the device status word kept in a decode workspace
  * (bit 0: a K/V write was skipped because len >= max_seq; bit 1: a token

@@ -122,3 +122,20 @@ def test_status_strings():
     assert _abi.df_status_str(0) == "ok"
     assert "workspace" in _abi.df_status_str(_abi.DF_ERR_WORKSPACE)
     assert _abi.df_status_str(12345) == "unknown status code"
+
+
+def test_pack_and_gemv_reject_bad_arguments():
+    p = lambda **kw: _abi.df_pack_weights(kw.get("dt", _abi.DF_BF16), kw.get("src", 0x100000),
+                                          kw.get("dst", 0x900000), kw.get("n", 2), kw.get("rows", 32),
+                                          kw.get("cols", 64))
+    assert p(dt=_abi.DF_F32) == _abi.DF_ERR_DTYPE
+    assert p(src=None) == _abi.DF_ERR_NULL
+    assert p(rows=24) == _abi.DF_ERR_SHAPE
+    assert p(cols=48) == _abi.DF_ERR_SHAPE
+    assert p(n=0) == _abi.DF_ERR_SHAPE
+    assert p(dst=0x900008) == _abi.DF_ERR_ALIGN
+    assert p(dst=0x100000 + 2 * 32 * 64 * 2 - 16) == _abi.DF_ERR_ARG     # overlaps the source
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 24, 4096) == 0   # N % 16
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 4096, 4000) == 0  # K % 256
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 3, 4096, 4096) == 0   # odd rows
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 4096, 4096) > 0
