@@ -19,7 +19,7 @@ size_t elem_size(int dtype) { return dtype == DF_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets from the workspace base).
 struct WsLayout {
     size_t status, h, xd, xo, xf, q, part, logits, r, ids, gates, offsets, perm, inv, grows, yrows, gpart, gcount,
-        total;
+        stats, total;
 };
 
 // Largest split-K partial buffer and row-block count over the model's GEMVs.
@@ -69,6 +69,7 @@ WsLayout layout(const df_config& c) {
     gemv_scratch(c, &gp, &gb);
     L.gpart = take(gp * 4);
     L.gcount = take(gb * 4);
+    L.stats = take(M * dfk::stat_segs(c.d_model) * 2 * 4);
     L.total = o;
     return L;
 }
@@ -187,14 +188,33 @@ struct Step {
         if (e != hipSuccess) return DF_ERR_HIP;
         const size_t kv_layer = (size_t)B * c.n_heads * c.max_seq * c.head_dim * es;
         const size_t ffn = moe ? (size_t)c.expert_ffn : (size_t)c.ffn;
+        // LayerNorms: a residual update leaves per-segment statistics of h;
+        // with bf16 storage the next projection normalises h on the fly from
+        // them, otherwise ln_apply writes the normalised rows to xd first.
+        const bool fused = c.dtype == DF_BF16;
+        float* stats = at<float>(L.stats);
+        bool pending = false;   // h has fresh statistics whose norm has not been applied
+        auto set_x = [&](dfk::GemvArgs& g, const float* gain) {
+            if (pending && fused) { g.x = h; g.x_stats = stats; g.x_gain = gain; }
+            else { g.x = xd; g.x_stats = nullptr; g.x_gain = nullptr; }
+        };
+        auto apply_norm = [&](const float* gain) -> bool {   // h -> xd when it is not fused
+            if (!pending || fused) return true;
+            pending = false;
+            return dfk::ln_apply(h, stats, gain, c.ln_eps, B, d, nflows, xd, s) == hipSuccess;
+        };
         for (int l = 0; l < L_; ++l) {
             char* kc = reinterpret_cast<char*>(kv.k) + l * kv_layer;
             char* vc = reinterpret_cast<char*>(kv.v) + l * kv_layer;
+            const float* g_ln1 = w.ln1 + (size_t)l * d;
+            const float* g_ln2 = w.ln2 + (size_t)l * d;
+            const float* g_next = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf;
             dfk::GemvArgs g{};
             g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.H = c.n_heads; g.Dh = c.head_dim; g.S_max = c.max_seq;
             g.part = at<float>(L.gpart); g.eps = c.ln_eps;
-            // Q/K/V projection: Q coupling and primary K/V append fused
-            g.x = xd; g.w = reinterpret_cast<const char*>(w.w_qkv) + (size_t)l * 3 * d * d * es;
+            // Q/K/V projection of LN1(h): Q coupling and primary K/V append fused
+            set_x(g, g_ln1);
+            g.w = reinterpret_cast<const char*>(w.w_qkv) + (size_t)l * 3 * d * d * es;
             g.N = 3 * d; g.K = d; g.epi = dfk::EPI_QKV; g.cpl = w.cpl_a + (size_t)l * d; g.q_out = q;
             g.kc = kc; g.vc = vc; g.len = kv.len; g.status = status;
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
@@ -205,25 +225,35 @@ struct Step {
             a.part = at<float>(L.part); a.o_rows = xo;
             timing_events(0, &a.ev_start, &a.ev_stop);
             if (dfk::attention(a, s) != hipSuccess) return DF_ERR_HIP;
-            // output projection + residual, then LN2 (fused in the split-K finish)
-            g.x = xo; g.w = reinterpret_cast<const char*>(w.w_o) + (size_t)l * d * d * es;
-            g.N = d; g.K = d; g.epi = dfk::EPI_RESID_LN; g.cpl = nullptr; g.h = h;
-            g.ln_gain = w.ln2 + (size_t)l * d; g.x_out = xd;
+            // output projection + residual (statistics for LN2)
+            g.x = xo; g.x_stats = nullptr; g.x_gain = nullptr;
+            g.w = reinterpret_cast<const char*>(w.w_o) + (size_t)l * d * d * es;
+            g.N = d; g.K = d; g.epi = dfk::EPI_RESID; g.cpl = nullptr; g.h = h; g.stats_out = stats;
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+            pending = true;
             const float* cb = w.cpl_b + (size_t)l * ffn;
             const float* cc = w.cpl_c + (size_t)l * d;
             if (!moe) {
-                g.x = xd; g.w = reinterpret_cast<const char*>(w.w_up) + (size_t)l * ffn * d * es;
+                if (!apply_norm(g_ln2)) return DF_ERR_HIP;
+                set_x(g, g_ln2);
+                g.w = reinterpret_cast<const char*>(w.w_up) + (size_t)l * ffn * d * es;
                 g.N = (int)ffn; g.K = d; g.epi = dfk::EPI_GELU_B; g.cpl = cb; g.x_out = xf;
                 if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
-                // down projection + c coupling + residual, then the next norm
-                g.x = xf; g.w = reinterpret_cast<const char*>(w.w_down) + (size_t)l * d * ffn * es;
-                g.N = d; g.K = (int)ffn; g.epi = dfk::EPI_RESID_LN; g.cpl = cc; g.h = h;
-                g.ln_gain = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf; g.x_out = xd;
+                pending = false;
+                // down projection + c coupling + residual (statistics for the next norm)
+                g.x = xf; g.x_stats = nullptr; g.x_gain = nullptr;
+                g.w = reinterpret_cast<const char*>(w.w_down) + (size_t)l * d * ffn * es;
+                g.N = d; g.K = (int)ffn; g.epi = dfk::EPI_RESID; g.cpl = cc; g.h = h; g.stats_out = stats;
                 if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
+                pending = true;
+                if (!apply_norm(g_next)) return DF_ERR_HIP;
             } else {
+                // router and experts read LN2(h) rows
+                if (dfk::ln_apply(h, stats, g_ln2, c.ln_eps, B, d, nflows, xd, s) != hipSuccess) return DF_ERR_HIP;
+                pending = false;
                 const int E = c.n_experts;
-                g.x = xd; g.w = reinterpret_cast<const char*>(w.w_router) + (size_t)l * E * d * es;
+                g.x = xd; g.x_stats = nullptr; g.x_gain = nullptr;
+                g.w = reinterpret_cast<const char*>(w.w_router) + (size_t)l * E * d * es;
                 g.N = E; g.K = d; g.epi = dfk::EPI_STORE; g.out_f32 = at<float>(L.r);
                 if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
                 dfk::MoeArgs m{};
@@ -238,17 +268,17 @@ struct Step {
                 m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = at<float>(L.grows);
                 m.y_rows = at<float>(L.yrows);
                 if (dfk::moe(m, s) != hipSuccess) return DF_ERR_HIP;
-                const float* gn = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf;
-                if (dfk::layer_norm_rows(c.dtype, h, gn, c.ln_eps, B, d, nflows, xd, s) != hipSuccess)
+                if (dfk::layer_norm_rows(c.dtype, h, g_next, c.ln_eps, B, d, nflows, xd, s) != hipSuccess)
                     return DF_ERR_HIP;
             }
         }
         if (head) {
             float* lg = logits ? logits : at<float>(L.logits);
             dfk::GemvArgs g{};
-            g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.x = xd; g.w = w.w_out; g.N = c.vocab; g.K = d;
-            g.epi = dfk::EPI_STORE; g.out_f32 = lg;
+            g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.w = w.w_out; g.N = c.vocab; g.K = d;
+            g.epi = dfk::EPI_STORE; g.out_f32 = lg; g.eps = c.ln_eps;
             g.part = at<float>(L.gpart);
+            set_x(g, w.lnf);   // final norm
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             if (dfk::mix_head(lg, B, c.vocab, nflows == 2, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
         }

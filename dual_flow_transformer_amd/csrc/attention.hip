@@ -13,7 +13,7 @@
 // each), so a wave-wide load covers PPW consecutive positions. Every lane
 // group keeps its own online-softmax state (running max m, sum l, output o)
 // in the log2 domain; groups merge once at the end of the chunk. Pass 2
-// (attn_combine) merges the chunks of a pair in chunk order: deterministic
+// (attn_combine) merges the chunks of a pair in a fixed order: deterministic
 // (the item a wave happens to take does not change any result).
 #include <algorithm>
 
@@ -32,6 +32,7 @@ struct PartParams {
     const int32_t* nkeys;
     float* part_o;     // [slots][2][Dh]
     float* part_ml;    // [slots][4]
+    int32_t* chunk_tab; // [B][2]: first item and chunk count of sequence b
     size_t seq_stride; // elements between sequences in the cache
     int B, H, S_max, nkeys_add, nflows;
     int target;        // wanted number of items over the batch
@@ -94,6 +95,10 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     }
     const int my_base = incl - p.H * my_c;
     const int n_items = __shfl(incl, 63, 64);
+    if (blockIdx.x == 0 && threadIdx.x < p.B) {   // the chunking, for the combine pass
+        p.chunk_tab[2 * threadIdx.x] = my_base;
+        p.chunk_tab[2 * threadIdx.x + 1] = my_c;
+    }
 
     // Items are of about equal length; wave w takes items w, w + G, w + 2G, ...
     const int G = gridDim.x * 4;
@@ -223,45 +228,81 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
 struct CombParams {
     const float* part_o;
     const float* part_ml;
-    const int32_t* nkeys;
+    const int32_t* chunk_tab;
     float* o_f32;
     float* lse;
     float* o_rows;
-    int B, H, S_max, Dh, nkeys_add, nflows, target;
+    int H, nflows;
 };
 
-template <typename T>
+// One workgroup per (sequence, head): thread (cg, f, d4) merges chunks
+// cg, cg + NG, ... of flow f for dims 4*d4 .. 4*d4 + 3 (all loads of a thread
+// are independent, so they are in flight together), then the NG chunk
+// groups merge in a fixed order through LDS: deterministic.
+template <int DH>
 __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
+    constexpr int D4 = DH / 4, PER = 2 * D4, NG = 256 / PER;   // chunk groups
+    __shared__ float s_m[NG][2], s_l[NG][2];
+    __shared__ float4 s_o[NG][2][D4];
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-    const int f = threadIdx.x / p.Dh, dim = threadIdx.x - f * p.Dh;
-    if (f >= p.nflows) return;
-    long long total = 0;
-    for (int bb = 0; bb < p.B; ++bb) total += (long long)p.H * keys_of(p.nkeys, bb, p.nkeys_add, p.S_max);
-    int base = 0, C = 0;
-    for (int bb = 0; bb <= b; ++bb) {
-        const int c = chunks_of(keys_of(p.nkeys, bb, p.nkeys_add, p.S_max), total, p.target);
-        if (bb < b) base += p.H * c; else C = c;
-    }
+    const int cg = threadIdx.x / PER, r = threadIdx.x - cg * PER;
+    const int f = r / D4, d4 = r - f * D4;
+    const int base = p.chunk_tab[2 * b], C = p.chunk_tab[2 * b + 1];
     const size_t first = (size_t)base + (size_t)h * C;
-    const float* ml = p.part_ml + first * 4 + f * 2;
-    const float* po = p.part_o + first * 2 * p.Dh + f * p.Dh + dim;
-    float M = -1e30f;
-    for (int c = 0; c < C; ++c) M = fmaxf(M, ml[c * 4]);
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < C; ++c) {
-        const float w = __builtin_amdgcn_exp2f(ml[c * 4] - M);
-        L = fmaf(ml[c * 4 + 1], w, L);
-        O = fmaf(po[(size_t)c * 2 * p.Dh], w, O);
+    float m = -1e30f, l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (f < p.nflows) {
+        for (int c0 = cg; c0 < C; c0 += 4 * NG) {
+            float mc[4], lc[4];
+            float4 oc[4];
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = min(c0 + u * NG, C - 1);
+                mc[u] = p.part_ml[(first + c) * 4 + 2 * f];
+                lc[u] = p.part_ml[(first + c) * 4 + 2 * f + 1];
+                oc[u] = *reinterpret_cast<const float4*>(p.part_o + ((first + c) * 2 + f) * DH + 4 * d4);
+            }
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (c0 + u * NG >= C) break;
+                const float mn = fmaxf(m, mc[u]);
+                const float sa = __builtin_amdgcn_exp2f(m - mn), sb = __builtin_amdgcn_exp2f(mc[u] - mn);
+                l = l * sa + lc[u] * sb;
+                o.x = o.x * sa + oc[u].x * sb;
+                o.y = o.y * sa + oc[u].y * sb;
+                o.z = o.z * sa + oc[u].z * sb;
+                o.w = o.w * sa + oc[u].w * sb;
+                m = mn;
+            }
+        }
     }
-    O = O / L;
-    const size_t row = (size_t)(2 * b + f) * p.H * p.Dh + h * p.Dh + dim;
-    if (p.o_f32) p.o_f32[row] = O;
-    if (p.o_rows) p.o_rows[row] = O;
-    if (p.lse && dim == 0) p.lse[(size_t)(2 * b + f) * p.H + h] = (M + __log2f(L)) * df::kLn2;
+    if (d4 == 0) { s_m[cg][f] = m; s_l[cg][f] = l; }
+    s_o[cg][f][d4] = o;
+    __syncthreads();
+    if (cg != 0 || f >= p.nflows) return;
+    for (int g = 1; g < NG; ++g) {
+        const float mo = s_m[g][f], lo = s_l[g][f];
+        const float4 oo = s_o[g][f][d4];
+        const float mn = fmaxf(m, mo);
+        const float sa = __builtin_amdgcn_exp2f(m - mn), sb = __builtin_amdgcn_exp2f(mo - mn);
+        l = l * sa + lo * sb;
+        o.x = o.x * sa + oo.x * sb;
+        o.y = o.y * sa + oo.y * sb;
+        o.z = o.z * sa + oo.z * sb;
+        o.w = o.w * sa + oo.w * sb;
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+    const size_t row = (size_t)(2 * b + f) * p.H * DH + (size_t)h * DH + 4 * d4;
+    if (p.o_f32) *reinterpret_cast<float4*>(p.o_f32 + row) = o;
+    if (p.o_rows) *reinterpret_cast<float4*>(p.o_rows + row) = o;
+    if (p.lse && d4 == 0) p.lse[(size_t)(2 * b + f) * p.H + h] = (m + __log2f(l)) * df::kLn2;
 }
 
 constexpr int kMaxTarget = 16384;   // items per launch at most (workspace bound)
+constexpr int kTabFloats = 256;     // chunk table [64][2] ints, padded
 
 // Resident waves of attn_partial on the current device (cached).
 template <typename T, int DH, int U>
@@ -289,7 +330,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     const int target = std::min(2 * waves, kMaxTarget - a.B * a.H);
     PartParams p;
     p.k = a.k; p.v = a.v; p.q = a.q; p.a = a.a; p.nkeys = a.nkeys;
-    p.part_ml = a.part + 64;
+    p.chunk_tab = reinterpret_cast<int32_t*>(a.part);
+    p.part_ml = a.part + kTabFloats;
     p.part_o = p.part_ml + (size_t)kMaxTarget * 4;
     p.seq_stride = (size_t)a.H * a.S_max * DH;
     p.B = a.B; p.H = a.H; p.S_max = a.S_max; p.nkeys_add = a.nkeys_add; p.nflows = a.nflows;
@@ -302,10 +344,9 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     CombParams c;
-    c.part_o = p.part_o; c.part_ml = p.part_ml; c.nkeys = a.nkeys; c.o_f32 = a.o_f32; c.lse = a.lse;
-    c.o_rows = a.o_rows; c.B = a.B; c.H = a.H; c.S_max = a.S_max; c.Dh = DH; c.nkeys_add = a.nkeys_add;
-    c.nflows = a.nflows; c.target = target;
-    hipLaunchKernelGGL((attn_combine<T>), dim3(a.B * a.H), dim3(2 * DH), 0, s, c);
+    c.part_o = p.part_o; c.part_ml = p.part_ml; c.chunk_tab = p.chunk_tab; c.o_f32 = a.o_f32; c.lse = a.lse;
+    c.o_rows = a.o_rows; c.H = a.H; c.nflows = a.nflows;
+    hipLaunchKernelGGL((attn_combine<DH>), dim3(a.B * a.H), dim3(256), 0, s, c);
     return hipGetLastError();
 }
 
@@ -313,9 +354,9 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
 
 size_t attention_part_floats(int B, int H, int S_max, int Dh) {
     (void)S_max;
-    // 64 spare floats, then ml [kMaxTarget][4], then o [kMaxTarget][2][Dh]
+    // chunk table, then ml [kMaxTarget][4], then o [kMaxTarget][2][Dh]
     (void)B; (void)H;
-    return 64 + (size_t)kMaxTarget * (4 + 2 * Dh);
+    return kTabFloats + (size_t)kMaxTarget * (4 + 2 * Dh);
 }
 
 hipError_t attention(const AttnArgs& a, hipStream_t s) {

@@ -91,4 +91,20 @@ __device__ __forceinline__ float block_max(float x, float* red) {
     return t;
 }
 
+// Mean and 1/sqrt(var + eps) of a row of d values from the (mean, M2) pairs
+// of its nseg consecutive segments of seg_len values (the last one possibly
+// shorter), by Chan et al.'s pairwise combination of partial moments.
+__device__ __forceinline__ float2 row_norm_from_segments(const float2* st, int nseg, int seg_len, int d,
+                                                         float eps) {
+    float mean = 0.f;
+    for (int i = 0; i < nseg; ++i) mean += (float)min(seg_len, d - i * seg_len) * st[i].x;
+    mean /= (float)d;
+    float m2 = 0.f;
+    for (int i = 0; i < nseg; ++i) {
+        const float dm = st[i].x - mean;
+        m2 += st[i].y + (float)min(seg_len, d - i * seg_len) * dm * dm;
+    }
+    return make_float2(mean, 1.0f / sqrtf(m2 / (float)d + eps));
+}
+
 }  // namespace df

@@ -20,8 +20,8 @@ struct AttnArgs {
     const int32_t* nkeys;     // keys attended by sequence b: nkeys[b] + nkeys_add
     int nkeys_add;
     int nflows;               // 2 = both flows, 1 = primary only
-    float* part;              // workspace, attention_part_floats() floats; its first
-                              // two ints are work counters, zero between launches
+    float* part;              // workspace, attention_part_floats() floats (chunk table and
+                              // per-chunk partial results of this call)
     float* o_f32;             // [B][2][H][Dh] fp32 output or nullptr
     float* lse;               // [B][2][H] or nullptr
     float* o_rows;            // [2B][H*Dh] fp32 output rows (projection input), or nullptr
@@ -57,6 +57,17 @@ hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* p
 hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps, int B, int d,
                            int nflows, void* x, hipStream_t s);
 
+// Residual rows are summarised per segment of kStatSeg columns as (mean, M2)
+// pairs, stats[(r * nseg + seg) * 2 + {0, 1}] for stacked row r, nseg =
+// ceil(d / kStatSeg); a LayerNorm then needs no further pass over the row.
+constexpr int kStatSeg = 256;
+constexpr int kMaxSeg = 16;   // d <= 4096
+__host__ __device__ inline int stat_segs(int d) { return (d + kStatSeg - 1) / kStatSeg; }
+
+// x[r] = LN(h[r]; g) (fp32) from the per-segment statistics of h.
+hipError_t ln_apply(const float* h, const float* stats, const float* g, float eps, int B, int d, int nflows,
+                    float* x, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Stacked-row GEMV: Y[m][n] = sum_k X[m][k] W[n][k], m over the stacked rows
 // in use, with a fused epilogue.
@@ -65,12 +76,14 @@ enum EpiKind {
     EPI_STORE = 0,     // out_f32[m][n] = y
     EPI_QKV = 1,       // Q rows (+ a coupling) to q_out, primary K/V appended to the cache
     EPI_GELU_B = 2,    // g = GELU(y), g2 += b*g1, g to x_out
-    EPI_RESID_LN = 3,  // (optional c coupling) h[m][n] += y, then x_out = LN(h; ln_gain)
+    EPI_RESID = 3,     // (optional c coupling) h[m][n] += y; per-segment statistics of h to stats_out
 };
 
 struct GemvArgs {
     int dtype;
-    const void* x;        // [2B][K] stacked rows, fp32
+    const void* x;        // [2B][K] stacked rows, fp32 (with x_stats: residual rows to normalise)
+    const float* x_stats; // bf16 only: per-segment statistics of x; the rows enter as LN(x; x_gain)
+    const float* x_gain;
     const void* w;        // bf16: [N][K] in the 16x32 fragment layout; fp32: row-major [N][K]
     int N, K;
     int B;                // sequences
@@ -78,8 +91,9 @@ struct GemvArgs {
     int epi;
     // epilogue operands
     float* out_f32;       // EPI_STORE: [2B][N]
-    float* h;             // EPI_RESID_LN: [2B][N] residual
-    float* x_out;         // EPI_GELU_B, EPI_RESID_LN: [2B][N] fp32
+    float* h;             // EPI_RESID: [2B][N] residual
+    float* stats_out;     // EPI_RESID: per-segment statistics of the updated rows
+    float* x_out;         // EPI_GELU_B: [2B][N] fp32
     const float* cpl;     // a (QKV), b (GELU_B), c (RESID_LN) or nullptr
     float* q_out;         // EPI_QKV: [2B][d] fp32
     void* kc;             // EPI_QKV: cache of this layer [B][H][S_max][Dh]
@@ -88,15 +102,14 @@ struct GemvArgs {
     int H, Dh, S_max;
     int32_t* status;      // EPI_QKV: flag when a position is out of range
     float* part;          // split-K partial sums (plan_gemv(...).part_floats floats)
-    const float* ln_gain; // EPI_RESID_LN: gain of the following norm
-    float eps;
+    float eps;            // LayerNorm epsilon (x_stats)
 };
 struct GemvPlan {
     int MT;               // 16-row activation tiles (0: shape not supported)
     int variant;          // kernel shape
     int ks, S;            // k-slice width and count
     int grid, nblocks;    // workgroups; row groups per slice
-    size_t lds, part_floats;
+    size_t lds, part_floats;   // dynamic LDS bytes; partial-sum floats
 };
 GemvPlan plan_gemv(int dtype, int N, int K, int M);
 hipError_t gemv(const GemvArgs& a, hipStream_t s);

@@ -39,6 +39,7 @@ struct GParams {
     int epi;
     float* out_f32;
     float* h;
+    float* stats_out;
     float* x_out;
     const float* cpl;
     float* q_out;
@@ -49,7 +50,8 @@ struct GParams {
     int32_t* status;
     int S;                // k-slices
     float* part;          // split-K partials [S][M][N]
-    const float* ln_gain; // EPI_RESID_LN: gain of the norm that follows
+    const float* x_stats; // activation rows normalised on the fly (see GemvArgs)
+    const float* x_gain;
     float eps;
 };
 
@@ -180,7 +182,26 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
         }
     };
 
-    // activation loads first, then the first weight fragments, then the split
+    // Loads first: with a LayerNorm on the fly the gains of the slice and the
+    // per-segment statistics of the rows (so the row statistics can be
+    // combined while the rest is in flight), then the activation rows, then
+    // the first weight fragments; then the normalisation and the hi/lo split.
+    __shared__ float s_gain[KS];
+    __shared__ float s_mean[16 * MT], s_rstd[16 * MT];
+    constexpr int SPT = (16 * MT * kMaxSeg + NW * 64 - 1) / (NW * 64);
+    const bool norm = p.x_stats != nullptr;
+    const int nseg = stat_segs(p.K), n_st = p.M * nseg;
+    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    float2 sv[SPT];
+    if (norm) {
+        if ((int)threadIdx.x < KS / 4) gv = *reinterpret_cast<const float4*>(p.x_gain + ks0 + 4 * threadIdx.x);
+        #pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int e = min((int)threadIdx.x + u * NW * 64, n_st - 1);
+            const int m = e / nseg, seg = e - m * nseg;
+            sv[u] = *reinterpret_cast<const float2*>(p.x_stats + ((size_t)(m * p.row_step) * nseg + seg) * 2);
+        }
+    }
     float4 xv[XB];
     #pragma unroll
     for (int u = 0; u < XB; ++u) {
@@ -190,12 +211,40 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     }
     u32x4 a0[RT][KU], a1[RT][KU];
     load(0, a0);
+    if (norm) {
+        // row statistics (Chan's combination of the segments), in the LDS
+        // area of the activation slice, which is free until the split
+        float2* s_seg = reinterpret_cast<float2*>(xs);
+        if ((int)threadIdx.x < KS / 4) *reinterpret_cast<float4*>(s_gain + 4 * threadIdx.x) = gv;
+        #pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int e = threadIdx.x + u * NW * 64;
+            if (e < n_st) s_seg[e] = sv[u];
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < p.M) {
+            const int m = threadIdx.x;
+            const float2 mr = df::row_norm_from_segments(s_seg + m * nseg, nseg, kStatSeg, p.K, p.eps);
+            s_mean[m] = mr.x;
+            s_rstd[m] = mr.y;
+        }
+        __syncthreads();
+    }
     #pragma unroll
     for (int u = 0; u < XB; ++u) {
         const int i = threadIdx.x + u * NW * 64;
         if (i >= NI) break;
         const int m = i / C4, c = i - m * C4;
-        const float4 v = xv[u];
+        float4 v = xv[u];
+        if (norm) {
+            const int mm = min(m, p.M - 1);
+            const float mean = s_mean[mm], rstd = s_rstd[mm];
+            const float4 g = *reinterpret_cast<const float4*>(s_gain + 4 * c);
+            v.x = (v.x - mean) * rstd * g.x;
+            v.y = (v.y - mean) * rstd * g.y;
+            v.z = (v.z - mean) * rstd * g.z;
+            v.w = (v.w - mean) * rstd * g.w;
+        }
         const bf16_t h0 = df::f32_to_bf16(v.x), h1 = df::f32_to_bf16(v.y);
         const bf16_t h2 = df::f32_to_bf16(v.z), h3 = df::f32_to_bf16(v.w);
         const bf16_t l0 = df::f32_to_bf16(v.x - df::bf16_to_f32(h0));
@@ -248,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
             #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const int nb = tile * TR + rt * 16;
-                if (S > 1 || p.epi == EPI_RESID_LN) {
+                if (S > 1 || p.epi == EPI_RESID) {
                     #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const int m = mt * 16 + li, n0 = nb + 4 * lg;
@@ -271,22 +320,27 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     if (it < n_it) step(it, a0, a1);
 }
 
-// Sum of the S k-slice partials of logical row m, column n (slice order;
-// loads issued eight at a time).
-__device__ __forceinline__ float sum_slices(const GParams& p, int S, int m, int n) {
-    const float* q = p.part + (size_t)m * p.N + n;
+// Sums of the S k-slice partials of logical rows m1 and m2 (m2 < 0: none),
+// column n, in slice order; sixteen loads in flight at a time.
+__device__ __forceinline__ void sum_slices(const GParams& p, int S, int m1, int m2, int n, float& y1, float& y2) {
+    const float* q1 = p.part + (size_t)m1 * p.N + n;
+    const float* q2 = p.part + (size_t)(m2 < 0 ? m1 : m2) * p.N + n;
     const size_t stride = (size_t)p.M * p.N;
-    float v = 0.f;
+    float v1 = 0.f, v2 = 0.f;
     int s = 0;
     for (; s + 8 <= S; s += 8) {
-        float t[8];
+        float t1[8], t2[8];
         #pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = q[(size_t)(s + u) * stride];
+        for (int u = 0; u < 8; ++u) {
+            t1[u] = q1[(size_t)(s + u) * stride];
+            t2[u] = q2[(size_t)(s + u) * stride];
+        }
         #pragma unroll
-        for (int u = 0; u < 8; ++u) v += t[u];
+        for (int u = 0; u < 8; ++u) { v1 += t1[u]; v2 += t2[u]; }
     }
-    for (; s < S; ++s) v += q[(size_t)s * stride];
-    return v;
+    for (; s < S; ++s) { v1 += q1[(size_t)s * stride]; v2 += q2[(size_t)s * stride]; }
+    y1 = v1;
+    y2 = m2 < 0 ? 0.f : v2;
 }
 
 // Split-K finish for the elementwise epilogues: thread per (sequence, column).
@@ -295,25 +349,62 @@ __global__ __launch_bounds__(256) void gemv_reduce_epi(GParams p, int S) {
     const int b = t / p.N, n = t - (t / p.N) * p.N;
     if (b >= p.B) return;
     const bool dual = p.nflows == 2;
-    const float y1 = sum_slices(p, S, dual ? 2 * b : b, n);
-    const float y2 = dual ? sum_slices(p, S, 2 * b + 1, n) : 0.f;
+    float y1, y2;
+    sum_slices(p, S, dual ? 2 * b : b, dual ? 2 * b + 1 : -1, n, y1, y2);
     epilogue<bf16_t>(p, n, b, y1, y2);
 }
 
-// Split-K finish with the residual add: thread per (sequence, column); the
-// aux output gets the c coupling (y2 += c * y1) when given; h += y. The
-// following LayerNorm runs as its own row kernel.
-__global__ __launch_bounds__(256) void gemv_reduce_resid(GParams p, int S) {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    const int b = t / p.N, n = t - (t / p.N) * p.N;
-    if (b >= p.B) return;
+// Split-K finish with the residual add: block (segment, sequence), thread
+// per column; the aux output gets the c coupling (y2 += c * y1) when given;
+// h += y; then the (mean, M2) of each updated row over the block's
+// kStatSeg columns go to stats_out, from which the next projection (or
+// ln_apply) normalises the rows without another pass.
+__global__ __launch_bounds__(kStatSeg) void gemv_reduce_resid(GParams p, int S) {
+    __shared__ float2 red[kStatSeg / 64];
+    const int seg = blockIdx.x, b = blockIdx.y, nseg = gridDim.x;
+    const int n = seg * kStatSeg + threadIdx.x;
+    const bool ok = n < p.N;
     const bool dual = p.nflows == 2;
-    const float y1 = sum_slices(p, S, dual ? 2 * b : b, n);
-    p.h[(size_t)(2 * b) * p.N + n] += y1;
-    if (dual) {
-        float y2 = sum_slices(p, S, 2 * b + 1, n);
-        if (p.cpl) y2 = fmaf(p.cpl[n], y1, y2);   // MLP-output coupling (c_l)
-        p.h[(size_t)(2 * b + 1) * p.N + n] += y2;
+    float v1 = 0.f, v2 = 0.f;
+    if (ok) {
+        float y1, y2;
+        sum_slices(p, S, dual ? 2 * b : b, dual ? 2 * b + 1 : -1, n, y1, y2);
+        float* h1 = p.h + (size_t)(2 * b) * p.N + n;
+        v1 = *h1 + y1;
+        *h1 = v1;
+        if (dual) {
+            if (p.cpl) y2 = fmaf(p.cpl[n], y1, y2);   // MLP-output coupling (c_l)
+            float* h2 = p.h + (size_t)(2 * b + 1) * p.N + n;
+            v2 = *h2 + y2;
+            *h2 = v2;
+        }
+    }
+    if (!p.stats_out) return;
+    // both rows at once: block sums of (v1, v2), then of the squared deviations
+    auto bsum2 = [&](float a, float c) {
+        a = df::wave_sum(a);
+        c = df::wave_sum(c);
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(a, c);
+        __syncthreads();
+        float2 t = red[0];
+        #pragma unroll
+        for (int i = 1; i < kStatSeg / 64; ++i) { t.x += red[i].x; t.y += red[i].y; }
+        return t;
+    };
+    const float cnt = (float)min(kStatSeg, p.N - seg * kStatSeg);
+    const float2 sm = bsum2(v1, v2);
+    const float mean1 = sm.x / cnt, mean2 = sm.y / cnt;
+    const float d1 = ok ? v1 - mean1 : 0.f, d2 = ok ? v2 - mean2 : 0.f;
+    const float2 m2 = bsum2(d1 * d1, d2 * d2);
+    if (threadIdx.x == 0) {
+        float* st = p.stats_out + ((size_t)(2 * b) * nseg + seg) * 2;
+        st[0] = mean1;
+        st[1] = m2.x;
+        if (dual) {
+            st[(size_t)nseg * 2] = mean2;
+            st[(size_t)nseg * 2 + 1] = m2.y;
+        }
     }
 }
 
@@ -343,7 +434,7 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
     #pragma unroll
     for (int m = 0; m < 16; ++m)
         if (m < p.M) acc[m] = df::wave_sum(acc[m]);
-    if (p.epi == EPI_RESID_LN) {       // one "slice"; gemv_reduce_ln finishes
+    if (p.epi == EPI_RESID) {          // one "slice"; gemv_reduce_resid finishes
         #pragma unroll
         for (int m = 0; m < 16; ++m)
             if (m < p.M && lane == m) p.part[(size_t)m * p.N + n] = acc[m];
@@ -361,7 +452,7 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
 }
 
 // Kernel shapes: A = 16-row tiles, 8 waves, 8 fragments in flight per tile
-// (4 with 64 or more stacked rows); B = 32-row tiles, 4 waves, 4 fragments
+// (4 with 64 stacked rows, 2 with 128); B = 32-row tiles, 4 waves, 4 fragments
 // per tile (matrices with fewer than 8192 rows).
 enum Variant { VAR_A = 0, VAR_B = 1 };
 
@@ -384,7 +475,7 @@ hipError_t launch_mt(GParams& p, const GemvPlan& pl, hipStream_t s) {
         }
         return hipErrorInvalidValue;
     }
-    constexpr int KU = MT >= 4 ? 4 : 8;   // register budget of the wider activation tiles
+    constexpr int KU = MT >= 8 ? 2 : MT >= 4 ? 4 : 8;   // register budget of the wider activation tiles
     if constexpr (MT <= 2) {
         if (pl.ks == 1024) return launch_one<MT, 1, KU, 8, 1024>(p, pl, s);
     }
@@ -396,12 +487,9 @@ hipError_t launch_mt(GParams& p, const GemvPlan& pl, hipStream_t s) {
 }
 
 hipError_t finish(GParams& p, int S, hipStream_t s) {
-    if (p.epi == EPI_RESID_LN) {
-        const long total = (long)p.B * p.N;
-        hipLaunchKernelGGL(gemv_reduce_resid, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p, S);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return layer_norm_rows(DF_F32, p.h, p.ln_gain, p.eps, p.B, p.N, p.nflows, p.x_out, s);
+    if (p.epi == EPI_RESID) {
+        hipLaunchKernelGGL(gemv_reduce_resid, dim3(stat_segs(p.N), p.B), dim3(kStatSeg), 0, s, p, S);
+        return hipGetLastError();
     }
     if (S > 1) {
         const long total = (long)p.B * p.N;
@@ -428,7 +516,8 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M) {
     pl.lds = (size_t)2 * 16 * pl.MT * (ks + 8) * 2;
     // one or two resident workgroups per CU (LDS permitting), split over the
     // k-slices; no more row groups than row tiles
-    const int wg_per_cu = pl.lds <= 80 * 1024 ? 2 : 1;
+    const size_t lds_static = (size_t)ks * 4 + 2 * 16 * pl.MT * 4;   // gains, row mean and rstd
+    const int wg_per_cu = pl.lds + lds_static <= 80 * 1024 ? 2 : 1;
     const int rt = pl.variant == VAR_B ? 2 : 1;
     const int n_tiles = (N + 16 * rt - 1) / (16 * rt);
     int ngrp = std::max(1, kCUs * wg_per_cu / pl.S);
@@ -444,12 +533,14 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     p.x = a.x; p.w = a.w; p.N = a.N; p.K = a.K; p.nflows = a.nflows; p.B = a.B;
     p.M = a.nflows == 2 ? 2 * a.B : a.B;
     p.row_step = a.nflows == 2 ? 1 : 2;
-    p.epi = a.epi; p.out_f32 = a.out_f32; p.h = a.h; p.x_out = a.x_out; p.cpl = a.cpl; p.q_out = a.q_out;
+    p.epi = a.epi; p.out_f32 = a.out_f32; p.h = a.h; p.stats_out = a.stats_out; p.x_out = a.x_out; p.cpl = a.cpl;
+    p.q_out = a.q_out; p.x_stats = a.x_stats; p.x_gain = a.x_gain;
     p.kc = a.kc; p.vc = a.vc; p.len = a.len; p.H = a.H; p.Dh = a.Dh; p.S_max = a.S_max; p.status = a.status;
-    p.part = a.part; p.ln_gain = a.ln_gain; p.eps = a.eps;
+    p.part = a.part; p.eps = a.eps;
     if (a.dtype == DF_F32) {
         if (p.M > 16) return hipErrorInvalidValue;
-        if (a.epi == EPI_RESID_LN && (!a.part || a.N > 4096)) return hipErrorInvalidValue;
+        if (a.x_stats) return hipErrorInvalidValue;   // fp32 rows are normalised by ln_apply
+        if (a.epi == EPI_RESID && (!a.part || a.N > 4096)) return hipErrorInvalidValue;
         (void)hipGetLastError();
         hipLaunchKernelGGL(gemv_f32, dim3((a.N + 3) / 4), dim3(256), 0, s, p);
         hipError_t e = hipGetLastError();
@@ -459,8 +550,9 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M);
     if (pl.MT == 0) return hipErrorInvalidValue;
     p.S = pl.S;
-    if ((pl.S > 1 || a.epi == EPI_RESID_LN) && !a.part) return hipErrorInvalidValue;
-    if (a.epi == EPI_RESID_LN && a.N > 4096) return hipErrorInvalidValue;
+    if ((pl.S > 1 || a.epi == EPI_RESID) && !a.part) return hipErrorInvalidValue;
+    if (a.epi == EPI_RESID && a.N > 4096) return hipErrorInvalidValue;
+    if (a.x_stats && (!a.x_gain || a.K > kMaxSeg * kStatSeg)) return hipErrorInvalidValue;
     hipError_t e;
     switch (pl.MT) {
         case 1: e = launch_mt<1>(p, pl, s); break;

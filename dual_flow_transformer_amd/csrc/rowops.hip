@@ -86,6 +86,26 @@ __global__ __launch_bounds__(kRowThreads) void ln_rows_kernel(const float* h, co
     }
 }
 
+// x[r] = LN(h[r]; g) from the per-segment statistics of h: block (segment,
+// sequence), thread per column, both flows.
+__global__ __launch_bounds__(kStatSeg) void ln_apply_kernel(const float* h, const float* stats, const float* g,
+                                                            float eps, int d, int nflows, float* x) {
+    __shared__ float2 s_mr[2];
+    const int seg = blockIdx.x, b = blockIdx.y, nseg = stat_segs(d);
+    if ((int)threadIdx.x < nflows) {
+        const int r = 2 * b + threadIdx.x;
+        s_mr[threadIdx.x] = df::row_norm_from_segments(reinterpret_cast<const float2*>(stats) + (size_t)r * nseg,
+                                                       nseg, kStatSeg, d, eps);
+    }
+    __syncthreads();
+    const int n = seg * kStatSeg + threadIdx.x;
+    if (n >= d) return;
+    for (int f = 0; f < nflows; ++f) {
+        const size_t i = (size_t)(2 * b + f) * d + n;
+        x[i] = (h[i] - s_mr[f].x) * s_mr[f].y * g[n];
+    }
+}
+
 template <typename T>
 __global__ void kv_append_kernel(T* k, T* v, int H, int S_max, int Dh, const int32_t* pos,
                                  const float* dk, const float* dv, int32_t* status) {
@@ -206,6 +226,13 @@ hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* p
         hipLaunchKernelGGL(embed_ln_kernel<float>, dim3(B), dim3(kRowThreads), 0, s, (const float*)emb0,
                            (const float*)emb1, (const float*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
                            g, eps, h, (float*)x, status);
+    return hipGetLastError();
+}
+
+hipError_t ln_apply(const float* h, const float* stats, const float* g, float eps, int B, int d, int nflows,
+                    float* x, hipStream_t s) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ln_apply_kernel, dim3(stat_segs(d), B), dim3(kStatSeg), 0, s, h, stats, g, eps, d, nflows, x);
     return hipGetLastError();
 }
 

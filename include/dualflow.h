@@ -177,8 +177,8 @@ int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t aux
  *  d_o: [batch][2][n_heads][head_dim] fp32 outputs; d_lse: [batch][2][n_heads]
  *  natural-log sum of exp of the scaled scores. Scores are q.k/sqrt(head_dim).
  *  d_len[b] must lie in [1, max_seq]; batch <= 64.
- *  d_ws: df_attention_workspace_bytes bytes, zero-filled before its first
- *  use (it holds work counters that every call leaves at zero). */
+ *  d_ws: df_attention_workspace_bytes bytes (the call's chunk table and
+ *  per-chunk partial results; no initial contents needed). */
 int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch,
                       int32_t n_heads, int32_t max_seq, int32_t head_dim, const int32_t* d_len,
                       const float* d_q, const float* d_a, float* d_o, float* d_lse,
