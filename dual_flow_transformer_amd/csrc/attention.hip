@@ -7,8 +7,9 @@
 // chunks of about equal length over the whole batch (C_b chunks for each head
 // of sequence b, C_b ~ n_b * items / total keys), so variable context lengths
 // still give equal work items. Pass 1 (attn_partial) runs one resident set of
-// wavefronts, each taking a fixed stride of items (about two per wave), so all
-// finish together. Each 16-byte load of a key
+// wavefronts, each taking a fixed stride of items (one per wave: fewer, longer
+// items cost less setup and fewer partial results than several short ones),
+// so all finish together. Each 16-byte load of a key
 // row is shared by both queries; LPP lanes hold one key row (Dh/LPP elements
 // each), so a wave-wide load covers PPW consecutive positions. Every lane
 // group keeps its own online-softmax state (running max m, sum l, output o)
@@ -58,11 +59,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr int kMinChunk = 64;   // keys per chunk at least
 
-// Chunking shared by both passes (pure integer function of the lengths).
-// n: keys of sequence b; total: sum over sequences of H*n. Returns C_b.
+// Chunking (pure integer function of the lengths). n: keys of sequence b;
+// total: sum over sequences of H*n. Returns C_b = floor(n * target / total),
+// at least 1, so the items of a launch never exceed `target` (one per
+// resident wave) unless a sequence is too short to go below one chunk.
 __device__ __forceinline__ int chunks_of(int n, long long total, int target) {
     if (n <= 0) return 0;
-    long long c = ((long long)n * target + total / 2) / (total > 0 ? total : 1);
+    long long c = ((long long)n * target) / (total > 0 ? total : 1);
     const long long cmax = (n + kMinChunk - 1) / kMinChunk;
     if (c < 1) c = 1;
     if (c > cmax) c = cmax;
@@ -327,7 +330,7 @@ template <typename T, int DH>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     constexpr int U = 8;
     const int waves = resident_waves<T, DH, U>();
-    const int target = std::min(2 * waves, kMaxTarget - a.B * a.H);
+    const int target = std::min(waves, kMaxTarget - a.B * a.H);
     PartParams p;
     p.k = a.k; p.v = a.v; p.q = a.q; p.a = a.a; p.nkeys = a.nkeys;
     p.chunk_tab = reinterpret_cast<int32_t*>(a.part);

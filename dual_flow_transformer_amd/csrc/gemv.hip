@@ -139,13 +139,14 @@ __device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&ac
 // 2^-17 |x|) and both parts go through the matrix cores into the same fp32
 // accumulator. Weights are read in the 16x32 fragment layout, so every
 // wave-wide load is one contiguous 1 KiB piece, and a wave's tile slice is
-// one contiguous run; the next KU fragments per tile are always in flight,
-// across tile boundaries too. Loads are issued without branches (an
+// one contiguous run; the next NBUF - 1 batches of KU fragments per tile
+// are always in flight (from before the activation staging on, and across
+// tile boundaries). Loads are issued without branches (an
 // iteration past the end reads a fixed hot address) so the compiler's wait
 // counts stay exact. With S > 1 each tile's partial sums go to
 // part[s][m][n] and a reduce kernel finishes in slice order; with S == 1
 // the epilogue runs from the registers.
-template <int MT, int RT, int KU, int NW, int KS>
+template <int MT, int RT, int KU, int NW, int KS, int NBUF>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     extern __shared__ bf16_t xs[];
     constexpr int TR = 16 * RT, XS = KS + 8, IPT = KS / (32 * KU);
@@ -209,8 +210,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
         const int m = i / C4, c = i - m * C4;
         xv[u] = *reinterpret_cast<const float4*>(X + (size_t)(min(m, p.M - 1) * p.row_step) * p.K + ks0 + c * 4);
     }
-    u32x4 a0[RT][KU], a1[RT][KU];
+    static_assert(NBUF == 2 || NBUF == 3, "fragment buffers");
+    u32x4 a0[RT][KU], a1[RT][KU], a2[NBUF == 3 ? RT : 1][NBUF == 3 ? KU : 1];
     load(0, a0);
+    if constexpr (NBUF == 3) load(1, a1);
     if (norm) {
         // row statistics (Chan's combination of the segments), in the LDS
         // area of the activation slice, which is free until the split
@@ -268,8 +271,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
         for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const int xo = li * XS + lg * 8;
 
+    // NBUF fragment buffers in rotation: NBUF - 1 batches are in flight while
+    // one is consumed
     auto step = [&](int it, u32x4 (&cur)[RT][KU], u32x4 (&nxt)[RT][KU]) {
-        load(it + 1, nxt);
+        load(it + NBUF - 1, nxt);
         __builtin_amdgcn_sched_barrier(0);
         const int j = it / IPT, kb = it - j * IPT;
         const int kk = kb * 32 * KU;
@@ -313,11 +318,21 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
         }
     };
     int it = 0;
-    for (; it + 1 < n_it; it += 2) {
-        step(it, a0, a1);
-        step(it + 1, a1, a0);
+    if constexpr (NBUF == 3) {
+        for (; it + 2 < n_it; it += 3) {
+            step(it, a0, a2);
+            step(it + 1, a1, a0);
+            step(it + 2, a2, a1);
+        }
+        if (it < n_it) step(it, a0, a2);
+        if (it + 1 < n_it) step(it + 1, a1, a0);
+    } else {
+        for (; it + 1 < n_it; it += 2) {
+            step(it, a0, a1);
+            step(it + 1, a1, a0);
+        }
+        if (it < n_it) step(it, a0, a1);
     }
-    if (it < n_it) step(it, a0, a1);
 }
 
 // Sums of the S k-slice partials of logical rows m1 and m2 (m2 < 0: none),
@@ -451,18 +466,19 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
     }
 }
 
-// Kernel shapes: A = 16-row tiles, 8 waves, 8 fragments in flight per tile
-// (4 with 64 stacked rows, 2 with 128); B = 32-row tiles, 4 waves, 4 fragments
-// per tile (matrices with fewer than 8192 rows).
+// Kernel shapes: A = 16-row tiles, 8 waves, batches of 8 fragments (4 with 64
+// stacked rows, 2 with 128), two batches ahead (one with 128 rows);
+// B = 32-row tiles, 4 waves, batches of 4 fragments per tile, one batch ahead
+// (matrices with fewer than 8192 rows; two waves per SIMD need the registers).
 enum Variant { VAR_A = 0, VAR_B = 1 };
 
-template <int MT, int RT, int KU, int NW, int KS>
+template <int MT, int RT, int KU, int NW, int KS, int NBUF>
 hipError_t launch_one(GParams& p, const GemvPlan& pl, hipStream_t s) {
-    const void* fn = reinterpret_cast<const void*>(&gemv_bf16<MT, RT, KU, NW, KS>);
+    const void* fn = reinterpret_cast<const void*>(&gemv_bf16<MT, RT, KU, NW, KS, NBUF>);
     hipError_t e = tile::allow_lds(fn, pl.lds);
     if (e != hipSuccess) return e;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemv_bf16<MT, RT, KU, NW, KS>), dim3(pl.grid), dim3(NW * 64), pl.lds, s, p);
+    hipLaunchKernelGGL((gemv_bf16<MT, RT, KU, NW, KS, NBUF>), dim3(pl.grid), dim3(NW * 64), pl.lds, s, p);
     return hipGetLastError();
 }
 
@@ -470,19 +486,20 @@ template <int MT>
 hipError_t launch_mt(GParams& p, const GemvPlan& pl, hipStream_t s) {
     if (pl.variant == VAR_B) {
         if constexpr (MT <= 2) {
-            if (pl.ks == 512) return launch_one<MT, 2, 4, 4, 512>(p, pl, s);
-            if (pl.ks == 256) return launch_one<MT, 2, 4, 4, 256>(p, pl, s);
+            if (pl.ks == 512) return launch_one<MT, 2, 4, 4, 512, 2>(p, pl, s);
+            if (pl.ks == 256) return launch_one<MT, 2, 4, 4, 256, 2>(p, pl, s);
         }
         return hipErrorInvalidValue;
     }
     constexpr int KU = MT >= 8 ? 2 : MT >= 4 ? 4 : 8;   // register budget of the wider activation tiles
+    constexpr int NB = MT >= 8 ? 2 : 3;
     if constexpr (MT <= 2) {
-        if (pl.ks == 1024) return launch_one<MT, 1, KU, 8, 1024>(p, pl, s);
+        if (pl.ks == 1024) return launch_one<MT, 1, KU, 8, 1024, NB>(p, pl, s);
     }
     if constexpr (MT <= 4) {
-        if (pl.ks == 512) return launch_one<MT, 1, KU, 8, 512>(p, pl, s);
+        if (pl.ks == 512) return launch_one<MT, 1, KU, 8, 512, NB>(p, pl, s);
     }
-    if (pl.ks == 256) return launch_one<MT, 1, KU, 8, 256>(p, pl, s);
+    if (pl.ks == 256) return launch_one<MT, 1, KU, 8, 256, NB>(p, pl, s);
     return hipErrorInvalidValue;
 }
 
