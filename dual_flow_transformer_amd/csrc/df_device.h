@@ -17,11 +17,23 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// Two fp32 -> packed bf16 pair (a in the low half), round to nearest even.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four fp32 values split into bf16 hi = rne(x) and lo = rne(x - hi) parts
+// (packed pairs); hi + lo is within 2^-17 |x| of x.
+__device__ __forceinline__ void split_hi_lo(const float4& v, uint2& hi, uint2& lo) {
+    hi.x = pack_bf16x2(v.x, v.y);
+    hi.y = pack_bf16x2(v.z, v.w);
+    lo.x = pack_bf16x2(v.x - bf16_lo(hi.x), v.y - bf16_hi(hi.x));
+    lo.y = pack_bf16x2(v.z - bf16_lo(hi.y), v.w - bf16_hi(hi.y));
 }
 
 // Storage-type traits: load as fp32, store with rounding to the storage type.

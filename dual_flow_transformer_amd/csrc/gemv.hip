@@ -189,18 +189,20 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     // the first weight fragments; then the normalisation and the hi/lo split.
     __shared__ float s_gain[KS];
     __shared__ float s_mean[16 * MT], s_rstd[16 * MT];
+    // statistics: 16 lanes per row, lane j holds segment j (kMaxSeg == 16)
     constexpr int SPT = (16 * MT * kMaxSeg + NW * 64 - 1) / (NW * 64);
+    static_assert(kMaxSeg == 16, "one 16-lane group per row");
     const bool norm = p.x_stats != nullptr;
-    const int nseg = stat_segs(p.K), n_st = p.M * nseg;
+    const int nseg = stat_segs(p.K);
     float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
     float2 sv[SPT];
     if (norm) {
         if ((int)threadIdx.x < KS / 4) gv = *reinterpret_cast<const float4*>(p.x_gain + ks0 + 4 * threadIdx.x);
         #pragma unroll
         for (int u = 0; u < SPT; ++u) {
-            const int e = min((int)threadIdx.x + u * NW * 64, n_st - 1);
-            const int m = e / nseg, seg = e - m * nseg;
-            sv[u] = *reinterpret_cast<const float2*>(p.x_stats + ((size_t)(m * p.row_step) * nseg + seg) * 2);
+            const int e = threadIdx.x + u * NW * 64;
+            const int m = min(e >> 4, p.M - 1), j = min(e & 15, nseg - 1);
+            sv[u] = *reinterpret_cast<const float2*>(p.x_stats + ((size_t)(m * p.row_step) * nseg + j) * 2);
         }
     }
     float4 xv[XB];
@@ -215,21 +217,22 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     load(0, a0);
     if constexpr (NBUF == 3) load(1, a1);
     if (norm) {
-        // row statistics (Chan's combination of the segments), in the LDS
-        // area of the activation slice, which is free until the split
-        float2* s_seg = reinterpret_cast<float2*>(xs);
+        // row mean and rstd by Chan's combination of the segments' (mean, M2),
+        // reduced over each 16-lane group
         if ((int)threadIdx.x < KS / 4) *reinterpret_cast<float4*>(s_gain + 4 * threadIdx.x) = gv;
         #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int e = threadIdx.x + u * NW * 64;
-            if (e < n_st) s_seg[e] = sv[u];
-        }
-        __syncthreads();
-        if ((int)threadIdx.x < p.M) {
-            const int m = threadIdx.x;
-            const float2 mr = df::row_norm_from_segments(s_seg + m * nseg, nseg, kStatSeg, p.K, p.eps);
-            s_mean[m] = mr.x;
-            s_rstd[m] = mr.y;
+            const int m = e >> 4, j = e & 15;
+            const bool valid = j < nseg;
+            const float cnt = valid ? (float)min(kStatSeg, p.K - j * kStatSeg) : 0.f;
+            const float mean = df::group_sum<16>(cnt * sv[u].x) / (float)p.K;
+            const float dm = sv[u].x - mean;
+            const float m2 = df::group_sum<16>(valid ? fmaf(cnt * dm, dm, sv[u].y) : 0.f);
+            if (j == 0 && m < 16 * MT) {
+                s_mean[m] = mean;
+                s_rstd[m] = 1.0f / sqrtf(m2 / (float)p.K + p.eps);
+            }
         }
         __syncthreads();
     }
@@ -240,25 +243,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
         const int m = i / C4, c = i - m * C4;
         float4 v = xv[u];
         if (norm) {
-            const int mm = min(m, p.M - 1);
-            const float mean = s_mean[mm], rstd = s_rstd[mm];
+            const float mean = s_mean[m], rstd = s_rstd[m];
             const float4 g = *reinterpret_cast<const float4*>(s_gain + 4 * c);
             v.x = (v.x - mean) * rstd * g.x;
             v.y = (v.y - mean) * rstd * g.y;
             v.z = (v.z - mean) * rstd * g.z;
             v.w = (v.w - mean) * rstd * g.w;
         }
-        const bf16_t h0 = df::f32_to_bf16(v.x), h1 = df::f32_to_bf16(v.y);
-        const bf16_t h2 = df::f32_to_bf16(v.z), h3 = df::f32_to_bf16(v.w);
-        const bf16_t l0 = df::f32_to_bf16(v.x - df::bf16_to_f32(h0));
-        const bf16_t l1 = df::f32_to_bf16(v.y - df::bf16_to_f32(h1));
-        const bf16_t l2 = df::f32_to_bf16(v.z - df::bf16_to_f32(h2));
-        const bf16_t l3 = df::f32_to_bf16(v.w - df::bf16_to_f32(h3));
         uint2 hv, lv;
-        hv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        hv.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-        lv.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        lv.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+        df::split_hi_lo(v, hv, lv);
         *reinterpret_cast<uint2*>(xh + m * XS + c * 4) = hv;
         *reinterpret_cast<uint2*>(xl + m * XS + c * 4) = lv;
     }
