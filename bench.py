@@ -31,10 +31,10 @@ PEAK_HBM_GBS = 8000.0
 # write). Reported only while the kernel sources are the ones they were measured on.
 COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "02294f4b98ad57aba2da25298b1a35bc686eea73ea154011e6bda99cb1681534",
-    "attention_traffic_bytes_per_launch": 2.1564e9,
-    "library_sources_sha256": "6f5ccdd5123edc15af5483b8d20949d46a489a8ce44d106bf1658587085f0023",
-    "step_traffic_bytes": {"dual": 87.456e9, "primary_only": 84.728e9},
+    "attention_source_sha256": "4140c1ef04b656a90ad4e2cace72ce53214a667ef07bf0258373feedd5521a7d",
+    "attention_traffic_bytes_per_launch": 2.1524e9,
+    "library_sources_sha256": "b935a3c7ed15e071b646e00936122e74d9939f0e36d5d981a7030cb266c4e333",
+    "step_traffic_bytes": {"dual": 84.842e9, "primary_only": 83.382e9},
 }
 
 
