@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"],
+                    help="c5 (default) / c3 / c4: full decode step; c2: the shared-K/V attention kernel alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-primary-pass", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=0, help="oracle sample: layers (0 = auto)")
@@ -120,12 +121,110 @@ def cpu_baseline(cfg, n_layers: int, min_seconds: float = 10.0):
             "seconds_per_token": t_tok, "host_cpus": os.cpu_count()}
 
 
+def bench_attention(args):
+    """Attention-only workload: batch 32, 32 heads x 128, lengths uniform in
+    [1024, 4096], bf16 K/V, two queries per head. Times K calls of
+    df_attention_dual (partial pass + combine) after W warm-up calls; the
+    value is the achieved HBM bandwidth of the whole call over the algorithmic
+    bytes (every K/V byte of the attended positions once, queries, outputs)."""
+    import numpy as np
+    import torch
+
+    from dual_flow_transformer_amd import _abi
+    from synth import device as synth_dev
+    from synth import stream_id
+    from synth.workloads import C2_ATTN, AttnInputs
+
+    c = C2_ATTN
+    src = AttnInputs(c)
+    lens = src.lengths()
+    log(f"[bench] attention workload {c.name}: lengths {lens.min()}..{lens.max()}")
+    K_ = torch.empty((c.B, c.H, c.S_max, c.Dh), dtype=torch.int16, device="cuda")
+    V_ = torch.empty_like(K_)
+    for which, t in (("k", K_), ("v", V_)):
+        st = [stream_id("attn_" + which, b, h) for b in range(c.B) for h in range(c.H)]
+        synth_dev.normal_streams(t, st, c.S_max * c.Dh, c.S_max * c.Dh, c.seed, 1.0, True)
+    q1, q2, a = src.queries()
+    dq = torch.from_numpy(np.stack([q1, q2], axis=1)).cuda()
+    da = torch.from_numpy(a).cuda()
+    dl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    o = torch.empty((c.B, 2, c.H, c.Dh), device="cuda")
+    lse = torch.empty((c.B, 2, c.H), device="cuda")
+    wsb = _abi.df_attention_workspace_bytes(c.B, c.H, c.S_max, c.Dh)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        _abi.check(_abi.df_attention_dual(_abi.DF_BF16, K_.data_ptr(), V_.data_ptr(), c.B, c.H, c.S_max, c.Dh,
+                                          dl.data_ptr(), dq.data_ptr(), da.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                          ws.data_ptr(), wsb, stream.cuda_stream), "df_attention_dual")
+
+    W, K = args.warmup, args.steps
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+    _abi.check(_abi.df_timing_enable(0), "df_timing_enable")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rc, part_ms, part_n = _abi.df_timing_read()
+    _abi.check(rc, "df_timing_read")
+    ms = e0.elapsed_time(e1) / K
+    kv_bytes = int(lens.astype(np.int64).sum()) * c.H * c.Dh * 2 * 2
+    io_bytes = c.B * c.H * c.Dh * 4 * 2 * 2 + c.H * c.Dh * 4 + c.B * 2 * c.H * 4
+    gbs = (kv_bytes + io_bytes) / (ms / 1e3) / 1e9
+    part_avg = part_ms / max(part_n, 1)
+    part_gbs = kv_bytes / (part_avg / 1e3) / 1e9
+    log(f"[bench] attention call {ms * 1e3:.1f} us ({gbs:.0f} GB/s); partial pass {part_avg * 1e3:.1f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import dualflow as odf
+        b = 0
+        Kb = odf.to_f64(src.kv_block("k", b, int(lens[b])))
+        Vb = odf.to_f64(src.kv_block("v", b, int(lens[b])))
+        t, reps = 0.0, 0
+        while t < 10.0:
+            t0 = time.perf_counter()
+            for h in range(c.H):
+                qq2 = q2[b, h] + a.reshape(c.H, c.Dh)[h] * q1[b, h]
+                for qq in (q1[b, h], qq2):
+                    odf.attention_one(qq.astype(np.float64), Kb[h], Vb[h])
+            t += time.perf_counter() - t0
+            reps += 1
+        per_seq = t / reps
+        seq_bytes = int(lens[b]) * c.H * c.Dh * 2 * 2
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        cpu = {"value": seq_bytes / per_seq / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"sequence 0 ({int(lens[b])} positions, all {c.H} heads, both queries), {reps} repetitions "
+                         f"({t:.1f} s)", "seconds_per_call_scaled": per_seq * float(lens.sum()) / float(lens[b])}
+    out = {
+        "metric": "shared-K/V dual-query attention: achieved HBM GB/s vs peak", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded K/V and queries)",
+        "config": {"workload": c.name, "batch": c.B, "heads": c.H, "head_dim": c.Dh,
+                   "lengths": [int(lens.min()), int(lens.max())], "mean_length": float(lens.mean())},
+        "roofline": {"kernel": "attn_partial (split-K pass)", "bound": "hbm", "achieved": part_gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": part_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "avg_launch_ms": part_avg, "launches": part_n, "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
               "this build. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "c2":
+        bench_attention(args)
+        return
     import numpy as np
     import torch
 
