@@ -3,19 +3,20 @@
 // coupled to Q1 through a_l, attends the primary K1/V1, so both flows are
 // served by one read of each K/V region).
 //
-// Split-K flash decode. The keys of every (sequence, head) pair are cut into
-// chunks of about equal length over the whole batch (C_b chunks for each head
-// of sequence b, C_b ~ n_b * items / total keys), so variable context lengths
-// still give equal work items. Pass 1 (attn_partial) runs one resident set of
-// wavefronts, each taking a fixed stride of items (one per wave: fewer, longer
-// items cost less setup and fewer partial results than several short ones),
-// so all finish together. Each 16-byte load of a key
-// row is shared by both queries; LPP lanes hold one key row (Dh/LPP elements
-// each), so a wave-wide load covers PPW consecutive positions. Every lane
-// group keeps its own online-softmax state (running max m, sum l, output o)
-// in the log2 domain; groups merge once at the end of the chunk. Pass 2
-// (attn_combine) merges the chunks of a pair in a fixed order: deterministic
-// (the item a wave happens to take does not change any result).
+// Split-K flash decode with an even split of all keys over the resident
+// waves. The keys of the (sequence, head) pairs are laid end to end (pair
+// p = b*H + h holds n_b keys); wave w of G takes the key range
+// [w*KT, (w+1)*KT), KT = ceil(total / G), which covers one segment of each
+// pair it overlaps, so every wave streams the same number of bytes whatever
+// the mix of context lengths. The partial result of (wave w, pair p) goes to
+// slot w + p (unique: the overlaps form a staircase in (w, p)), and the
+// slots of a pair are consecutive. Each 16-byte load of a key row is shared
+// by both queries; LPP lanes hold one key row (Dh/LPP elements each), so a
+// wave-wide load covers PPW consecutive positions. Every lane group keeps
+// its own online-softmax state (running max m, sum l, output o) in the log2
+// domain; groups merge at the end of a segment. The combine pass merges
+// the segments of a pair in a fixed order: deterministic (no result depends
+// on timing).
 #include <algorithm>
 
 #include "df_device.h"
@@ -33,10 +34,10 @@ struct PartParams {
     const int32_t* nkeys;
     float* part_o;     // [slots][2][Dh]
     float* part_ml;    // [slots][4]
-    int32_t* chunk_tab; // [B][2]: first item and chunk count of sequence b
+    long long* seq_tab; // [B + 1]: key offset of sequence b's first pair; [B]: keys per wave
     size_t seq_stride; // elements between sequences in the cache
     int B, H, S_max, nkeys_add, nflows;
-    int target;        // wanted number of items over the batch
+    int waves;         // G: waves of the launch
     float scale_log2;  // log2(e) / sqrt(Dh)
 };
 
@@ -57,21 +58,6 @@ __device__ __forceinline__ void unpack(const u32x4& r, float (&x)[EPL]) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-constexpr int kMinChunk = 64;   // keys per chunk at least
-
-// Chunking (pure integer function of the lengths). n: keys of sequence b;
-// total: sum over sequences of H*n. Returns C_b = floor(n * target / total),
-// at least 1, so the items of a launch never exceed `target` (one per
-// resident wave) unless a sequence is too short to go below one chunk.
-__device__ __forceinline__ int chunks_of(int n, long long total, int target) {
-    if (n <= 0) return 0;
-    long long c = ((long long)n * target) / (total > 0 ? total : 1);
-    const long long cmax = (n + kMinChunk - 1) / kMinChunk;
-    if (c < 1) c = 1;
-    if (c > cmax) c = cmax;
-    return (int)c;
-}
-
 __device__ __forceinline__ int keys_of(const int32_t* nkeys, int b, int add, int S_max) {
     int n = nkeys[b] + add;
     return n < 0 ? 0 : (n > S_max ? S_max : n);
@@ -86,35 +72,39 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     const int g = lane / LPP, sub = lane - (lane / LPP) * LPP;
     const bool dual = p.nflows == 2;
 
-    // Per-sequence chunk counts and item offsets (lane b holds sequence b).
+    // Key offsets of the sequences (lane b holds sequence b): pair (b, h)
+    // starts at key off_b + h * n_b of the flattened range.
     const int my_n = lane < p.B ? keys_of(p.nkeys, lane, p.nkeys_add, p.S_max) : 0;
-    long long total = (long long)p.H * my_n;
-    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o, 64);
-    const int my_c = chunks_of(my_n, total, p.target);
-    int incl = p.H * my_c;                       // inclusive prefix over lanes
+    long long incl = (long long)p.H * my_n;      // inclusive prefix over lanes
     for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
+        const long long t = __shfl_up(incl, o, 64);
         if (lane >= o) incl += t;
     }
-    const int my_base = incl - p.H * my_c;
-    const int n_items = __shfl(incl, 63, 64);
-    if (blockIdx.x == 0 && threadIdx.x < p.B) {   // the chunking, for the combine pass
-        p.chunk_tab[2 * threadIdx.x] = my_base;
-        p.chunk_tab[2 * threadIdx.x + 1] = my_c;
+    const long long my_off = incl - (long long)p.H * my_n;
+    const long long total = __shfl(incl, 63, 64);
+    const int G = p.waves;
+    const long long KT = total > G ? (total + G - 1) / G : 1;   // keys per wave
+    if (blockIdx.x == 0 && threadIdx.x < 64) {   // for the combine pass
+        if (lane < p.B) p.seq_tab[lane] = my_off;
+        if (lane == 0) p.seq_tab[p.B] = KT;
     }
 
-    // Items are of about equal length; wave w takes items w, w + G, w + 2G, ...
-    const int G = gridDim.x * 4;
-    for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < n_items; item += G) {
-        // sequence of this item: the last b whose base <= item
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long k_end = min(total, (long long)(w + 1) * KT);
+    long long key = (long long)w * KT;
+    while (key < k_end) {
+        // sequence of this key: the last b whose offset <= key
         int b = 0;
         for (int bb = 1; bb < p.B; ++bb)
-            if (__shfl(my_base, bb, 64) <= item) b = bb;
-        const int n = __shfl(my_n, b, 64), C = __shfl(my_c, b, 64), base = __shfl(my_base, b, 64);
-        const int rel = item - base;
-        const int h = rel / C, c = rel - h * C;
-        const int start = (int)(((long long)c * n) / C), end = (int)(((long long)(c + 1) * n) / C);
-
+            if (__shfl(my_off, bb, 64) <= key) b = bb;
+        const int n = __shfl(my_n, b, 64);
+        const long long off_b = __shfl(my_off, b, 64);
+        const int h = (int)((key - off_b) / n);
+        const long long pair_lo = off_b + (long long)h * n;
+        const int start = (int)(key - pair_lo);
+        const int end = (int)(min(k_end, pair_lo + n) - pair_lo);
+        const int slot = w + b * p.H + h;
+        key = pair_lo + end;
         float q1[EPL], q2[EPL];
         {
             const float* qp = p.q + ((size_t)(b * 2) * p.H + h) * DH + sub * EPL;
@@ -213,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
             m1 = mn1; m2 = mn2;
         }
         if (g == 0) {
-            float* po = p.part_o + (size_t)item * 2 * DH + sub * EPL;
+            float* po = p.part_o + (size_t)slot * 2 * DH + sub * EPL;
             #pragma unroll
             for (int e = 0; e < EPL; ++e) po[e] = o1[e];
             if (dual) {
@@ -222,7 +212,7 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
             }
         }
         if (lane == 0) {
-            float* pm = p.part_ml + (size_t)item * 4;
+            float* pm = p.part_ml + (size_t)slot * 4;
             pm[0] = m1; pm[1] = l1; pm[2] = m2; pm[3] = l2;
         }
     }
@@ -231,11 +221,12 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
 struct CombParams {
     const float* part_o;
     const float* part_ml;
-    const int32_t* chunk_tab;
+    const long long* seq_tab;
+    const int32_t* nkeys;
     float* o_f32;
     float* lse;
     float* o_rows;
-    int H, nflows;
+    int B, H, nflows, S_max, nkeys_add;
 };
 
 // One workgroup per (sequence, head): thread (cg, f, d4) merges chunks
@@ -251,8 +242,13 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
     const int cg = threadIdx.x / PER, r = threadIdx.x - cg * PER;
     const int f = r / D4, d4 = r - f * D4;
-    const int base = p.chunk_tab[2 * b], C = p.chunk_tab[2 * b + 1];
-    const size_t first = (size_t)base + (size_t)h * C;
+    // the waves that covered this pair, and so its consecutive slots
+    const long long KT = p.seq_tab[p.B];
+    const int n = keys_of(p.nkeys, b, p.nkeys_add, p.S_max);
+    const long long lo = p.seq_tab[b] + (long long)h * n;
+    const int w0 = (int)(lo / KT), w1 = (int)((lo + n - 1) / KT);
+    const size_t first = (size_t)w0 + (size_t)b * p.H + h;
+    const int C = w1 - w0 + 1;
     float m = -1e30f, l = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     if (f < p.nflows) {
@@ -304,8 +300,8 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     if (p.lse && d4 == 0) p.lse[(size_t)(2 * b + f) * p.H + h] = (m + __log2f(l)) * df::kLn2;
 }
 
-constexpr int kMaxTarget = 16384;   // items per launch at most (workspace bound)
-constexpr int kTabFloats = 256;     // chunk table [64][2] ints, padded
+constexpr int kMaxSlots = 16384;    // partial results per launch at most (workspace bound)
+constexpr int kTabFloats = 256;     // sequence table [65] 64-bit, padded
 
 // Resident waves of attn_partial on the current device (cached).
 template <typename T, int DH, int U>
@@ -330,15 +326,15 @@ template <typename T, int DH>
 hipError_t launch(const AttnArgs& a, hipStream_t s) {
     constexpr int U = 8;
     const int waves = resident_waves<T, DH, U>();
-    const int target = std::min(waves, kMaxTarget - a.B * a.H);
+    if (waves + a.B * a.H > kMaxSlots) return hipErrorInvalidValue;
     PartParams p;
     p.k = a.k; p.v = a.v; p.q = a.q; p.a = a.a; p.nkeys = a.nkeys;
-    p.chunk_tab = reinterpret_cast<int32_t*>(a.part);
+    p.seq_tab = reinterpret_cast<long long*>(a.part);
     p.part_ml = a.part + kTabFloats;
-    p.part_o = p.part_ml + (size_t)kMaxTarget * 4;
+    p.part_o = p.part_ml + (size_t)kMaxSlots * 4;
     p.seq_stride = (size_t)a.H * a.S_max * DH;
     p.B = a.B; p.H = a.H; p.S_max = a.S_max; p.nkeys_add = a.nkeys_add; p.nflows = a.nflows;
-    p.target = target;
+    p.waves = waves;
     p.scale_log2 = df::kLog2e / sqrtf((float)DH);
     (void)hipGetLastError();
     if (a.ev_start) (void)hipEventRecord(a.ev_start, s);
@@ -347,8 +343,9 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     CombParams c;
-    c.part_o = p.part_o; c.part_ml = p.part_ml; c.chunk_tab = p.chunk_tab; c.o_f32 = a.o_f32; c.lse = a.lse;
-    c.o_rows = a.o_rows; c.H = a.H; c.nflows = a.nflows;
+    c.part_o = p.part_o; c.part_ml = p.part_ml; c.seq_tab = p.seq_tab; c.nkeys = a.nkeys; c.o_f32 = a.o_f32;
+    c.lse = a.lse; c.o_rows = a.o_rows; c.B = a.B; c.H = a.H; c.nflows = a.nflows; c.S_max = a.S_max;
+    c.nkeys_add = a.nkeys_add;
     hipLaunchKernelGGL((attn_combine<DH>), dim3(a.B * a.H), dim3(256), 0, s, c);
     return hipGetLastError();
 }
@@ -357,9 +354,9 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
 
 size_t attention_part_floats(int B, int H, int S_max, int Dh) {
     (void)S_max;
-    // chunk table, then ml [kMaxTarget][4], then o [kMaxTarget][2][Dh]
+    // sequence table, then ml [kMaxSlots][4], then o [kMaxSlots][2][Dh]
     (void)B; (void)H;
-    return kTabFloats + (size_t)kMaxTarget * (4 + 2 * Dh);
+    return kTabFloats + (size_t)kMaxSlots * (4 + 2 * Dh);
 }
 
 hipError_t attention(const AttnArgs& a, hipStream_t s) {
