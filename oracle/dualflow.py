@@ -27,7 +27,14 @@ MLP output, one way only; the output is p_mix = alpha_t p_primary +
 primary distribution and kept at 0.5 or more; in MoE models the aux flow
 reuses the primary's chosen experts with its own gate weights ([ES] Mecanismos
 Clave). Prefill is unchanged and decode reads each weight and K/V region once
-for both flows ([ES] Costes de Inferencia vs. Entrenamiento).
+for both flows ([ES] Costes de Inferencia vs. Entrenamiento). The ablations
+name a minimal Dual construction without coupling and without the
+probability mixture ([ES] Resultados), and MoE models may set the expert
+fan-outs of the two flows independently ([ES] Contribuciones Clave 3,
+Significado y Reivindicaciones): the model variant switches of
+``synth.workloads`` (couplings off; output p_aux; alpha = (1 + CP) / 2) and
+``top_k_aux`` (the aux flow's experts: the first top_k_aux of the primary's
+ranking) select them.
 
 Readings taken where the pages are silent (each stated where it is used):
 pre-norm GPT block, LayerNorm with gain only (eps 1e-5, shared by both
@@ -154,13 +161,20 @@ def attention_dual(K: np.ndarray, V: np.ndarray, q1: np.ndarray, q2raw: np.ndarr
     return o, lse
 
 
-def mix_head(l1: np.ndarray, l2: Optional[np.ndarray]):
+MIX_COLLISION, MIX_AUX, MIX_HALF = "collision", "aux", "half"
+
+
+def mix_head(l1: np.ndarray, l2: Optional[np.ndarray], mode: str = MIX_COLLISION):
     """Mixture output ([ES] Mecanismos Clave, mixture objective):
     p_mix = alpha p1 + (1 - alpha) p2 with p_f = softmax(l_f) over the whole
     vocabulary (temperature 1). alpha is read as the collision probability
     sum_v p1(v)^2, floored at 0.5 (the primary keeps at least half the
     weight) and capped at 1 against rounding. With no aux logits (aux flow
     off) the step is primary-only: alpha = 1 and p_mix = p1.
+    Ablations ([ES] Resultados, ablations: the minimal Dual construction has
+    no probability mixture): mode "aux" outputs the aux distribution alone
+    (alpha = 0); mode "half" takes the other reading of the floor,
+    alpha = (1 + CP) / 2, also in [0.5, 1].
     next token: argmax of p_mix, ties to the lowest index (greedy reading)."""
     p1 = softmax(np.asarray(l1, dtype=np.float64))
     if l2 is None:
@@ -169,9 +183,23 @@ def mix_head(l1: np.ndarray, l2: Optional[np.ndarray]):
     else:
         p2 = softmax(np.asarray(l2, dtype=np.float64))
         cp = float(np.sum(p1 * p1))
-        alpha = min(1.0, max(0.5, cp))
+        if mode == MIX_AUX:
+            alpha = 0.0
+        elif mode == MIX_HALF:
+            alpha = min(1.0, 0.5 * (1.0 + cp))
+        elif mode == MIX_COLLISION:
+            alpha = min(1.0, max(0.5, cp))
+        else:
+            raise ValueError(mode)
         p = alpha * p1 + (1.0 - alpha) * p2
     return p, alpha, int(np.argmax(p))
+
+
+def mix_mode(variant: int) -> str:
+    """Mixture mode of a model variant (bit flags of synth.workloads)."""
+    if variant & 2 and variant & 4:
+        raise ValueError("aux output and alpha = (1 + CP) / 2 exclude each other")
+    return MIX_AUX if variant & 2 else (MIX_HALF if variant & 4 else MIX_COLLISION)
 
 
 def topk_ids(r: np.ndarray, k: int) -> np.ndarray:
@@ -352,17 +380,18 @@ def couple_out(y2: np.ndarray, c: np.ndarray, y1: np.ndarray) -> np.ndarray:
     return y2 + c * y1
 
 
-def qkv_rows(p: dict, u: list, cfg):
+def qkv_rows(p: dict, u: list, cfg, couple: bool = True):
     """Shared Q/K/V projection of the stacked rows. The primary row yields Q1
     and the K1/V1 to append (rounded to the storage dtype); the aux row goes
     through the same matrix but keeps only its query, coupled to Q1 (the aux
-    flow never writes the persistent cache, [ES] Arquitectura Central)."""
+    flow never writes the persistent cache, [ES] Arquitectura Central;
+    couple=False: the uncoupled ablation, [ES] Resultados)."""
     d = cfg.d
     qkv1 = _matvec(p["w_qkv"], u[0])
     q = [qkv1[:d]]
     if len(u) == 2:
         q2raw = _matvec(p["w_qkv"], u[1])[:d]
-        q.append(couple_query(q2raw, p["a"], q[0]))
+        q.append(couple_query(q2raw, p["a"], q[0]) if couple else q2raw)
     k_new = round_to(qkv1[d:2 * d], cfg.dtype).reshape(cfg.H, cfg.Dh)
     v_new = round_to(qkv1[2 * d:], cfg.dtype).reshape(cfg.H, cfg.Dh)
     return q, k_new, v_new
@@ -375,16 +404,17 @@ def attend(q: np.ndarray, K_bh: np.ndarray, V_bh: np.ndarray, pos: int) -> np.nd
     return o
 
 
-def _mlp_dense(p: dict, v: np.ndarray, flows: int, dtype: str, tr: Optional[dict] = None):
+def _mlp_dense(p: dict, v: np.ndarray, flows: int, dtype: str, tr: Optional[dict] = None, couple: bool = True):
     """Dense MLP of both flows with the two MLP couplings ([ES] Mecanismos Clave,
     light coupling): g2 = GELU(z2) + b * GELU(z1) (b_l on the post-activation
     intermediate), then y2 = g2 W2^T + c * y1 (c_l on the MLP output, before
-    the residual add). Primary rows never read aux values."""
+    the residual add). Primary rows never read aux values. couple=False: the
+    uncoupled ablation ([ES] Resultados)."""
     g = [gelu(_matvec(p["w_up"], v[f])) for f in range(flows)]
-    if flows == 2:
+    if flows == 2 and couple:
         g[1] = couple_mid(g[1], p["b"], g[0])
     y = [_matvec(p["w_down"], g[f]) for f in range(flows)]
-    if flows == 2:
+    if flows == 2 and couple:
         y[1] = couple_out(y[1], p["c"], y[0])
     if tr is not None:
         tr["mlp_g"] = np.stack(g)
@@ -393,31 +423,50 @@ def _mlp_dense(p: dict, v: np.ndarray, flows: int, dtype: str, tr: Optional[dict
 
 
 def _mlp_moe(p: dict, v: np.ndarray, flows: int, dtype: str, k: int,
-             r1_given: Optional[np.ndarray], tr: Optional[dict] = None):
+             r1_given: Optional[np.ndarray], tr: Optional[dict] = None, k_aux: int = 0,
+             couple: bool = True):
     """MoE MLP with router replay ([ES] Mecanismos Clave, router replay): the
     primary router picks the top-k experts; the aux flow reuses exactly those
     experts with its own gates. Gates of each flow are the softmax over that
-    flow's router logits at the k chosen ids. Each chosen expert is a GELU
+    flow's router logits at the chosen ids. Each chosen expert is a GELU
     MLP with the b_l coupling on its intermediate; the gate-weighted sum over
-    the k experts (in rank order) forms y, then c_l couples the outputs."""
+    the experts (in rank order) forms y, then c_l couples the outputs.
+
+    Independent fan-outs ([ES] Contribuciones Clave 3 and Significado y
+    Reivindicaciones: primary and aux expert fan-outs set separately): with
+    k_aux > 0 the aux flow takes the first k_aux experts of the primary's
+    ranking (k_aux = k is plain replay). The b_l coupling applies where the
+    primary has that expert's intermediate (ranks below k); an aux-only
+    expert has none to couple to."""
+    ka = k if k_aux <= 0 else k_aux
     r = [_matvec(p["w_router"], v[f]) for f in range(flows)]
     r1 = r[0] if r1_given is None else np.asarray(r1_given, dtype=np.float64)
-    ids = topk_ids(r1, k)
+    ranking = topk_ids(r1, max(k, ka))      # reported whatever the flows
+    ids = ranking[:k]
     gates = [softmax(r1[ids])]
     if flows == 2:
-        gates.append(softmax(r[1][ids]))
+        gates.append(softmax(r[1][ranking[:ka]]))
     y = [np.zeros(v.shape[-1]) for _ in range(flows)]
-    for j, e in enumerate(ids):
+    for j, e in enumerate(ranking):
+        if j >= k and (flows == 1 or j >= ka):
+            continue
         g = [gelu(_matvec(p["w_eup"][e], v[f])) for f in range(flows)]
-        if flows == 2:
+        if flows == 2 and couple and j < k:
             g[1] = couple_mid(g[1], p["b"], g[0])
-        for f in range(flows):
-            y[f] = y[f] + gates[f][j] * _matvec(p["w_edown"][e], g[f])
-    if flows == 2:
+        if j < k:
+            y[0] = y[0] + gates[0][j] * _matvec(p["w_edown"][e], g[0])
+        if flows == 2 and j < ka:
+            y[1] = y[1] + gates[1][j] * _matvec(p["w_edown"][e], g[1])
+    if flows == 2 and couple:
         y[1] = couple_out(y[1], p["c"], y[0])
     if tr is not None:
         tr["router"] = np.stack(r)
-    return y, ids, np.stack(gates)
+        tr["ranking"] = ranking
+    g_out = np.zeros((flows, max(k, ka)))   # gates by rank, zero beyond a flow's fan-out
+    g_out[0, :k] = gates[0]
+    if flows == 2:
+        g_out[1, :ka] = gates[1]
+    return y, ranking, g_out
 
 
 def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
@@ -439,6 +488,9 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
     c = model.cfg
     dt = c.dtype
     flows = 2 if aux_on else 1
+    couple = not (c.variant & 1)
+    mode = mix_mode(c.variant)
+    kr = max(c.top_k, c.top_k_aux, 1)
     nb = len(cache.seqs)
     pos = cache.lens.copy()
     if np.any(pos >= c.S_max):
@@ -448,8 +500,8 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
     h = np.zeros((nb, flows, c.d))
     for f in range(flows):
         h[:, f] = model.emb(f, tokens) + P
-    ids_all = np.zeros((c.L, nb, max(c.top_k, 1)), dtype=np.int32)
-    gates_all = np.zeros((c.L, nb, 2, max(c.top_k, 1)))
+    ids_all = np.zeros((c.L, nb, kr), dtype=np.int32)
+    gates_all = np.zeros((c.L, nb, 2, kr))
     tr: Dict[str, list] = {}
     g_prev = None
     for l in range(c.L):
@@ -459,7 +511,7 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
         for i in range(nb):
             lt = {} if trace else None
             u = [layer_norm(h[i, f], g_in, c.eps) for f in range(flows)]
-            q, k_new, v_new = qkv_rows(p, u, c)
+            q, k_new, v_new = qkv_rows(p, u, c, couple)
             cache.write(l, i, int(pos[i]), k_new, v_new)
             o = np.zeros((flows, c.d))
             for hh in range(c.H):
@@ -473,11 +525,11 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
             v = np.stack([layer_norm(h[i, f], p["ln2"], c.eps) for f in range(flows)])
             if c.moe:
                 r1 = None if router_logits is None else router_logits[l][i]
-                y, ids, gates = _mlp_moe(p, v, flows, dt, c.top_k, r1, lt)
+                y, ids, gates = _mlp_moe(p, v, flows, dt, c.top_k, r1, lt, c.top_k_aux, couple)
                 ids_all[l, i] = ids
                 gates_all[l, i, :flows] = gates
             else:
-                y = _mlp_dense(p, v, flows, dt, lt)
+                y = _mlp_dense(p, v, flows, dt, lt, couple)
             for f in range(flows):
                 h[i, f] = h[i, f] + y[f]
             if trace:
@@ -496,7 +548,7 @@ def decode_step(model: Model, cache: Cache, tokens, aux_on: bool = True,
     for i in range(nb):
         for f in range(flows):
             logits[i, f] = _matvec(W_out, layer_norm(h[i, f], model.lnf(), c.eps))
-        p_mix[i], alpha[i], nxt[i] = mix_head(logits[i, 0], logits[i, 1] if flows == 2 else None)
+        p_mix[i], alpha[i], nxt[i] = mix_head(logits[i, 0], logits[i, 1] if flows == 2 else None, mode)
     cache.lens = cache.lens + 1
     res = StepResult(logits, p_mix, alpha, nxt,
                      ids_all if c.moe else None, gates_all if c.moe else None)

@@ -54,6 +54,8 @@ class Config:
     zero_cpl: bool = False    # a = b = c = 0
     prompt_len: int = 0       # tiny config: prompt length (prefill prompt_len-1)
     n_steps: int = 0          # tiny config: dual decode steps after prefill
+    variant: int = 0          # ablation switches (VARIANT_* below)
+    top_k_aux: int = 0        # MoE: experts of the aux flow from the primary ranking (0: same as top_k)
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -75,6 +77,12 @@ class AttnConfig:
     S_max: int = 4096
     dtype: str = "bf16"
     seed: int = 1
+
+
+# Ablation switches of a model variant (bit flags).
+VARIANT_NO_COUPLING = 1   # a, b, c couplings off
+VARIANT_AUX_OUTPUT = 2    # no mixture: the step outputs the aux distribution
+VARIANT_ALPHA_HALF = 4    # alpha = (1 + collision probability) / 2
 
 
 # The five graded workloads.

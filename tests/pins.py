@@ -453,8 +453,158 @@ def pin_moe_replay():
             assert abs(r.gates[l, i, 0].sum() - 1) < 1e-12 and abs(r.gates[l, i, 1].sum() - 1) < 1e-12
 
 
+# ----------------------------------------------------------------------------
+# Ablation switches and independent aux expert fan-out
+# ----------------------------------------------------------------------------
+
+def pin_mix_aux_mode():
+    """No mixture ([ES] Resultados, minimal Dual): p_mix is the aux
+    distribution itself: alpha = 0, ratios p[i] / p[j] = exp(l2[i] - l2[j])
+    (brute force on small vocabularies), a distribution, argmax of l2."""
+    r = _rng(21)
+    for _ in range(20):
+        V = int(r.integers(2, 40))
+        l1, l2 = r.standard_normal(V) * 3, r.standard_normal(V) * 3
+        p, alpha, nt = odf.mix_head(l1, l2, odf.MIX_AUX)
+        assert alpha == 0.0 and abs(p.sum() - 1.0) < 1e-12
+        for i in range(V):
+            for j in range(V):
+                assert abs(p[i] / p[j] - math.exp(l2[i] - l2[j])) < 1e-9 * math.exp(abs(l2[i] - l2[j]))
+        assert nt == int(np.argmax(l2))
+
+
+def pin_mix_half_mode():
+    """The other reading of the floor, alpha = (1 + CP) / 2: in [0.5, 1];
+    uniform primary gives (1 + 1/V) / 2 exactly; one-hot primary gives 1; a
+    two-token primary p1 = (0.9, 0.1) (logits ln 9, 0) gives CP = 0.82,
+    alpha = 0.91, and p_mix = 0.91 p1 + 0.09 p2 by hand."""
+    r = _rng(22)
+    for _ in range(20):
+        V = int(r.integers(2, 3000))
+        p, alpha, _ = odf.mix_head(r.standard_normal(V) * 5, r.standard_normal(V), odf.MIX_HALF)
+        assert 0.5 <= alpha <= 1.0 and abs(p.sum() - 1.0) < 1e-12
+    p, alpha, _ = odf.mix_head(np.zeros(40), r.standard_normal(40), odf.MIX_HALF)
+    assert abs(alpha - 0.5 * (1 + 1 / 40)) < 1e-15
+    l1 = np.zeros(30)
+    l1[3] = 1000.0
+    assert odf.mix_head(l1, np.zeros(30), odf.MIX_HALF)[1] == 1.0
+    p, alpha, nt = odf.mix_head(np.array([math.log(9.0), 0.0]), np.array([0.0, 0.0]), odf.MIX_HALF)
+    assert abs(alpha - 0.91) < 1e-12
+    assert np.max(np.abs(p - np.array([0.91 * 0.9 + 0.09 * 0.5, 0.91 * 0.1 + 0.09 * 0.5]))) < 1e-12 and nt == 0
+
+
+def pin_no_coupling_tied(cfg):
+    """Couplings off ([ES] Resultados, minimal Dual): with the aux embedding
+    tied to the primary one the aux flow repeats the primary exactly, however
+    large a, b, c are (sigma 0.5 here), bitwise; and the switch equals zero
+    coupling vectors, bitwise, with untied embeddings."""
+    c1 = cfg.replace(tie_emb=True, variant=1, sigma_cpl=0.5)
+    _, outs = _two_steps(c1, True, override=False)
+    for r in outs:
+        assert np.array_equal(r.logits[:, 0], r.logits[:, 1])
+    _, oa = _two_steps(cfg.replace(variant=1), True)
+    _, ob = _two_steps(cfg.replace(zero_cpl=True), True)
+    for x, y in zip(oa, ob):
+        assert np.array_equal(x.logits, y.logits) and np.array_equal(x.p_mix, y.p_mix)
+
+
+def pin_variant_mix_in_step(cfg):
+    """The mixture switches act on the step's output only: with variant "aux
+    output" p_mix = softmax(aux logits) and alpha = 0; with "alpha half"
+    alpha = (1 + CP) / 2 from the step's primary logits; logits are the same
+    as the default variant's, bitwise."""
+    _, base = _two_steps(cfg, True)
+    _, aux = _two_steps(cfg.replace(variant=2), True)
+    _, half = _two_steps(cfg.replace(variant=4), True)
+    for r0, ra, rh in zip(base, aux, half):
+        assert np.array_equal(r0.logits, ra.logits) and np.array_equal(r0.logits, rh.logits)
+        for i in range(cfg.B):
+            assert ra.alpha[i] == 0.0
+            assert np.max(np.abs(ra.p_mix[i] - odf.softmax(ra.logits[i, 1]))) < 1e-15
+            p1 = odf.softmax(rh.logits[i, 0])
+            assert abs(rh.alpha[i] - 0.5 * (1 + np.sum(p1 * p1))) < 1e-15
+
+
+def pin_fanout_replay_and_primary():
+    """Independent fan-outs ([ES] Contribuciones Clave 3): k_aux = k is plain
+    replay (bitwise); any k_aux leaves the primary logits, the cache and the
+    primary ids unchanged (bitwise), and the reported ids are the primary's
+    ranking (top-max(k, k_aux) of its logits, ties to the lower id)."""
+    cfg = TINY_MOE
+    _, o0 = _two_steps(cfg, True)
+    _, ok = _two_steps(cfg.replace(top_k_aux=cfg.top_k), True)
+    for x, y in zip(o0, ok):
+        assert np.array_equal(x.logits, y.logits) and np.array_equal(x.ids, y.ids)
+    for ka in (1, 3, cfg.E):
+        c2 = cfg.replace(top_k_aux=ka)
+        ca, oa = _two_steps(c2, True)
+        cb, ob = _two_steps(cfg, True)
+        for s, (x, y) in enumerate(zip(oa, ob)):
+            assert np.array_equal(x.logits[:, 0], y.logits[:, 0])
+            assert np.array_equal(x.ids[:, :, :cfg.top_k], y.ids)
+            rl = _router(cfg, s)
+            for l in range(cfg.L):
+                for i in range(cfg.B):
+                    assert list(x.ids[l, i]) == list(odf.topk_ids(rl[l, i], max(cfg.top_k, ka)))
+        for l in range(cfg.L):
+            assert all(np.array_equal(a, b) for a, b in zip(ca.layer(l), cb.layer(l)))
+
+
+def pin_fanout_closed_forms():
+    """k_aux = E with b = c = 0: the aux MoE output is the full softmax mixture
+    of the aux router over all experts; k_aux = 1: the aux uses the primary's
+    top expert alone (gate 1) with the b coupling (that expert is the
+    primary's too); the primary output is the top-k mixture either way.
+    Brute force per expert."""
+    cfg = TINY_MOE.replace(zero_cpl=True)
+    m = odf.Model(Inputs(cfg))
+    p = m.layer(1)
+    r = _rng(23)
+    v = odf.round_to(r.standard_normal((2, cfg.d)), "bf16")
+    expert = lambda e, x: p["w_edown"][e] @ odf.gelu(p["w_eup"][e] @ x)
+    y, ranking, gates = odf._mlp_moe(p, v, 2, "bf16", cfg.top_k, None, k_aux=cfg.E)
+    l2 = p["w_router"] @ v[1]
+    w = np.exp(l2 - l2.max())
+    w /= w.sum()
+    assert np.max(np.abs(y[1] - sum(w[e] * expert(e, v[1]) for e in range(cfg.E)))) < 1e-12
+    l1 = p["w_router"] @ v[0]
+    top = odf.topk_ids(l1, cfg.top_k)
+    w1 = np.exp(l1[top] - l1[top].max())
+    w1 /= w1.sum()
+    assert np.max(np.abs(y[0] - sum(w1[j] * expert(e, v[0]) for j, e in enumerate(top)))) < 1e-12
+    cb = TINY_MOE
+    mb = odf.Model(Inputs(cb))
+    pb = mb.layer(0)
+    y, ranking, gates = odf._mlp_moe(pb, v, 2, "bf16", cb.top_k, None, k_aux=1)
+    e = int(ranking[0])
+    g1 = odf.gelu(pb["w_eup"][e] @ v[0])
+    g2 = odf.gelu(pb["w_eup"][e] @ v[1]) + pb["b"] * g1
+    l1 = pb["w_router"] @ v[0]
+    top = odf.topk_ids(l1, cb.top_k)
+    w1 = np.exp(l1[top] - l1[top].max())
+    w1 /= w1.sum()
+    y1 = sum(w1[j] * (pb["w_edown"][ee] @ odf.gelu(pb["w_eup"][ee] @ v[0])) for j, ee in enumerate(top))
+    assert np.max(np.abs(y[1] - (pb["w_edown"][e] @ g2 + pb["c"] * y1))) < 1e-12
+    assert gates[1, 0] == 1.0 and np.all(gates[1, 1:] == 0.0)
+    # k_aux = E with b, c != 0: b couples only the ranks the primary also ran
+    y, ranking, gates = odf._mlp_moe(pb, v, 2, "bf16", cb.top_k, None, k_aux=cb.E)
+    l2 = pb["w_router"] @ v[1]
+    w2 = np.exp(l2[ranking] - l2[ranking].max())
+    w2 /= w2.sum()
+    want = pb["c"] * y1
+    for j, ee in enumerate(ranking):
+        g2 = odf.gelu(pb["w_eup"][ee] @ v[1])
+        if j < cb.top_k:
+            g2 = g2 + pb["b"] * odf.gelu(pb["w_eup"][ee] @ v[0])
+        want = want + w2[j] * (pb["w_edown"][ee] @ g2)
+    assert np.max(np.abs(y[1] - want)) < 1e-12
+
+
 ALL_BASIC = [pin_round_bf16, pin_layer_norm, pin_gelu, pin_attention_sdpa, pin_attention_closed_forms,
-             pin_attention_dual, pin_mix_properties, pin_mix_golden, pin_topk]
+             pin_attention_dual, pin_mix_properties, pin_mix_golden, pin_topk, pin_mix_aux_mode,
+             pin_mix_half_mode]
 MODEL_PINS = [pin_aux_onoff, pin_tied_zero_coupling, pin_kv_sentinel, pin_prefill_equals_decode,
               pin_causality, pin_query_coupling, pin_mid_coupling, pin_out_coupling, pin_step_outputs]
-MOE_PINS = [pin_moe_single_expert_is_dense, pin_moe_all_experts_is_full_mixture, pin_moe_replay]
+MOE_PINS = [pin_moe_single_expert_is_dense, pin_moe_all_experts_is_full_mixture, pin_moe_replay,
+            pin_fanout_replay_and_primary, pin_fanout_closed_forms]
+VARIANT_PINS = [pin_no_coupling_tied, pin_variant_mix_in_step]

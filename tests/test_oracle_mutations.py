@@ -86,8 +86,8 @@ def _round_truncate(x, dtype):
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def _qkv_aux_writes(p, u, cfg):
-    q, k, v = _orig_qkv(p, u, cfg)
+def _qkv_aux_writes(p, u, cfg, couple=True):
+    q, k, v = _orig_qkv(p, u, cfg, couple)
     if len(u) == 2:
         qkv2 = odf._matvec(p["w_qkv"], u[1])
         k = odf.round_to(qkv2[cfg.d:2 * cfg.d], cfg.dtype).reshape(cfg.H, cfg.Dh)
@@ -95,7 +95,7 @@ def _qkv_aux_writes(p, u, cfg):
     return q, k, v
 
 
-def _qkv_no_round(p, u, cfg):
+def _qkv_no_round(p, u, cfg, couple=True):
     d = cfg.d
     qkv1 = odf._matvec(p["w_qkv"], u[0])
     q = [qkv1[:d]]
@@ -105,6 +105,43 @@ def _qkv_no_round(p, u, cfg):
 
 
 _orig_qkv = odf.qkv_rows
+
+
+def _qkv_ignores_switch(p, u, cfg, couple=True):
+    return _orig_qkv(p, u, cfg, True)
+
+
+_orig_mix = odf.mix_head
+
+
+def _mix_half_keeps_floor(l1, l2, mode=odf.MIX_COLLISION):
+    if mode == odf.MIX_HALF:
+        mode = odf.MIX_COLLISION
+    return _orig_mix(l1, l2, mode)
+
+
+def _mix_aux_mode_primary(l1, l2, mode=odf.MIX_COLLISION):
+    if mode == odf.MIX_AUX and l2 is not None:
+        p1 = odf.softmax(np.asarray(l1, float))
+        return p1, 0.0, int(np.argmax(p1))
+    return _orig_mix(l1, l2, mode)
+
+
+_orig_moe = odf._mlp_moe
+
+
+def _moe_couples_aux_only_experts(p, v, flows, dtype, k, r1_given, tr=None, k_aux=0, couple=True):
+    """b coupling also on aux-only experts (ranks k..k_aux-1), reading the
+    primary's intermediate there although the primary never ran them."""
+    ka = k if k_aux <= 0 else k_aux
+    if flows == 1 or ka <= k:
+        return _orig_moe(p, v, flows, dtype, k, r1_given, tr, k_aux, couple)
+    y, ranking, gates = _orig_moe(p, v, flows, dtype, k, r1_given, tr, k_aux, couple)
+    y = [y[0], y[1].copy()]
+    for j in range(k, ka):
+        e = ranking[j]
+        y[1] = y[1] + gates[1][j] * (p["w_edown"][e] @ (p["b"] * odf.gelu(p["w_eup"][e] @ v[0])))
+    return y, ranking, gates
 
 
 def _attend_excl_new(q, K, V, pos):
@@ -139,6 +176,11 @@ MUTATIONS = [
     ("aux_writes_kv", "qkv_rows", _qkv_aux_writes, [lambda: pins.pin_aux_onoff(pins.TINY_BF16)]),
     ("kv_not_rounded", "qkv_rows", _qkv_no_round, [lambda: pins.pin_prefill_equals_decode(pins.TINY_BF16),
                                                     lambda: pins.pin_query_coupling(pins.TINY_BF16)]),
+    ("no_coupling_switch_ignored", "qkv_rows", _qkv_ignores_switch,
+     [lambda: pins.pin_no_coupling_tied(pins.TINY_BF16)]),
+    ("alpha_half_keeps_floor", "mix_head", _mix_half_keeps_floor, [pins.pin_mix_half_mode]),
+    ("aux_output_mode_gives_primary", "mix_head", _mix_aux_mode_primary, [pins.pin_mix_aux_mode]),
+    ("aux_only_experts_coupled", "_mlp_moe", _moe_couples_aux_only_experts, [pins.pin_fanout_closed_forms]),
     ("attend_excludes_new_entry", "attend", _attend_excl_new,
      [lambda: pins.pin_prefill_equals_decode(pins.TINY_F32), lambda: pins.pin_query_coupling(pins.TINY_F32)]),
 ]
@@ -160,7 +202,7 @@ def test_mutation_is_caught(monkeypatch, name, attr, fn, checks):
 def test_moe_aux_gates_from_primary_is_caught(monkeypatch):
     orig = odf._mlp_moe
 
-    def wrong(p, v, flows, dtype, k, r1_given, tr=None):
+    def wrong(p, v, flows, dtype, k, r1_given, tr=None, k_aux=0, couple=True):
         y, ids, gates = orig(p, v, 1, dtype, k, r1_given, tr)
         if flows == 1:
             return y, ids, gates
