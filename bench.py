@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"],
                     help="c5 (default) / c3 / c4: full decode step; c2: the shared-K/V attention kernel alone")
+    ap.add_argument("--variant", type=int, default=0,
+                    help="model variant switches: 1 couplings off, 2 aux output (no mixture), 4 alpha=(1+CP)/2")
+    ap.add_argument("--top-k-aux", type=int, default=0,
+                    help="MoE: aux expert fan-out from the primary ranking (0 = replay of top_k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-primary-pass", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=0, help="oracle sample: layers (0 = auto)")
@@ -235,7 +239,7 @@ def main():
     cfg = PRESETS[args.workload]
     W, K = args.warmup, args.steps
     S = cfg.ctx + W + K + 8
-    cfg = cfg.replace(S_max=S)
+    cfg = cfg.replace(S_max=S, variant=args.variant, top_k_aux=args.top_k_aux if cfg.moe else 0)
     log(f"[bench] workload {cfg.name}: filling device inputs (S_max={S})")
     t0 = time.time()
     gm = DecodeModel(cfg, fill="device")
@@ -325,7 +329,7 @@ def main():
         log(f"[bench] oracle: {cpu['value']:.4f} tok/s ({cpu['seconds_per_token']:.2f} s/token)")
 
     att_sha, lib_sha = source_hashes()
-    same_work = cfg.name == COUNTERS["workload"]
+    same_work = cfg.name == COUNTERS["workload"] and cfg.variant == 0 and not cfg.top_k_aux
     traffic = COUNTERS["attention_traffic_bytes_per_launch"] if (
         same_work and att_sha == COUNTERS["attention_source_sha256"]) else None
     counter_ratio = None
@@ -340,7 +344,8 @@ def main():
         "config": {"workload": cfg.name, "layers": cfg.L, "d_model": cfg.d, "heads": cfg.H, "head_dim": cfg.Dh,
                    "ffn": cfg.F if not cfg.moe else None, "experts": cfg.E if cfg.moe else None,
                    "top_k": cfg.top_k if cfg.moe else None, "expert_ffn": cfg.Fe if cfg.moe else None,
-                   "vocab": cfg.V, "global_batch": cfg.B, "context": cfg.ctx, "parallelism": "none (1 GPU)"},
+                   "vocab": cfg.V, "global_batch": cfg.B, "context": cfg.ctx, "parallelism": "none (1 GPU)",
+                   "variant": cfg.variant, "top_k_aux": cfg.top_k_aux if cfg.moe else None},
         "roofline": {"kernel": "attn_partial (shared-K/V dual-query attention, split-K pass)", "bound": "hbm",
                      "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": attn_gbs / PEAK_HBM_GBS,
                      "traffic": traffic, "avg_launch_ms": attn_avg_ms, "launches": attn_n,

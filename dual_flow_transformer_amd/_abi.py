@@ -24,6 +24,10 @@ DF_ERR_HIP = -7
 DF_ERR_ARG = -8
 DF_F32 = 0
 DF_BF16 = 1
+DF_VARIANT_NO_COUPLING = 1
+DF_VARIANT_AUX_OUTPUT = 2
+DF_VARIANT_ALPHA_HALF = 4
+DF_MIX_PRIMARY, DF_MIX_COLLISION, DF_MIX_AUX, DF_MIX_HALF = 0, 1, 2, 3
 
 EXPORTS = ["df_workspace_bytes", "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
            "df_attention_dual", "df_attention_workspace_bytes", "df_device_status", "df_status_str",
@@ -36,7 +40,7 @@ class df_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float)]
+                ("ln_eps", ctypes.c_float), ("variant", ctypes.c_int32), ("top_k_aux", ctypes.c_int32)]
 
 
 class df_weights(ctypes.Structure):
@@ -130,8 +134,8 @@ def df_kv_append(cfg, kv, layer, d_pos, d_k, d_v, d_status=None, stream=0) -> in
     return lib().df_kv_append(ctypes.byref(cfg), ctypes.byref(kv), int(layer), d_pos, d_k, d_v, d_status, stream)
 
 
-def df_mix_head(d_logits, batch, vocab, aux_on, d_p_mix, d_alpha, d_next_tok=None, stream=0) -> int:
-    return lib().df_mix_head(d_logits, int(batch), int(vocab), int(aux_on), d_p_mix, d_alpha, d_next_tok, stream)
+def df_mix_head(d_logits, batch, vocab, mode, d_p_mix, d_alpha, d_next_tok=None, stream=0) -> int:
+    return lib().df_mix_head(d_logits, int(batch), int(vocab), int(mode), d_p_mix, d_alpha, d_next_tok, stream)
 
 
 def df_attention_dual(dtype, d_k, d_v, batch, n_heads, max_seq, head_dim, d_len, d_q, d_a, d_o, d_lse, d_ws,

@@ -2,6 +2,7 @@
 // carving and the per-layer kernel sequence on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -45,7 +46,7 @@ WsLayout layout(const df_config& c) {
     const size_t es = elem_size(c.dtype);
     const size_t M = 2 * (size_t)c.batch;
     const bool moe = c.n_experts > 0;
-    const size_t P = (size_t)c.batch * (moe ? c.top_k : 0);
+    const size_t P = (size_t)c.batch * (moe ? std::max(c.top_k, c.top_k_aux) : 0);
     WsLayout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
@@ -86,7 +87,13 @@ int check_config(const df_config* c) {
     if (c->d_model != c->n_heads * c->head_dim || c->d_model > 4096) return DF_ERR_SHAPE;
     if (c->batch > 64) return DF_ERR_SHAPE;
     if (!(c->ln_eps > 0.f)) return DF_ERR_ARG;
+    if ((c->variant & ~(DF_VARIANT_NO_COUPLING | DF_VARIANT_AUX_OUTPUT | DF_VARIANT_ALPHA_HALF)) != 0 ||
+        ((c->variant & DF_VARIANT_AUX_OUTPUT) && (c->variant & DF_VARIANT_ALPHA_HALF)))
+        return DF_ERR_ARG;
     const bool moe = c->n_experts > 0;
+    if (c->top_k_aux < 0 || c->top_k_aux > 16 || (!moe && c->top_k_aux != 0) ||
+        (moe && c->top_k_aux > c->n_experts))
+        return DF_ERR_SHAPE;
     if (moe) {
         if (c->dtype != DF_BF16) return DF_ERR_DTYPE;
         if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts || c->n_experts > 1024) return DF_ERR_SHAPE;
@@ -192,6 +199,8 @@ struct Step {
         // with bf16 storage the next projection normalises h on the fly from
         // them, otherwise ln_apply writes the normalised rows to xd first.
         const bool fused = c.dtype == DF_BF16;
+        const bool couple = (c.variant & DF_VARIANT_NO_COUPLING) == 0;   // a, b, c applied
+        const int kr = std::max(c.top_k, c.top_k_aux);                   // MoE ranking length
         float* stats = at<float>(L.stats);
         bool pending = false;   // h has fresh statistics whose norm has not been applied
         auto set_x = [&](dfk::GemvArgs& g, const float* gain) {
@@ -215,7 +224,7 @@ struct Step {
             // Q/K/V projection of LN1(h): Q coupling and primary K/V append fused
             set_x(g, g_ln1);
             g.w = reinterpret_cast<const char*>(w.w_qkv) + (size_t)l * 3 * d * d * es;
-            g.N = 3 * d; g.K = d; g.epi = dfk::EPI_QKV; g.cpl = w.cpl_a + (size_t)l * d; g.q_out = q;
+            g.N = 3 * d; g.K = d; g.epi = dfk::EPI_QKV; g.cpl = couple ? w.cpl_a + (size_t)l * d : nullptr; g.q_out = q;
             g.kc = kc; g.vc = vc; g.len = kv.len; g.status = status;
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             // shared-K/V attention of both queries over positions 0..len[b]
@@ -231,8 +240,8 @@ struct Step {
             g.N = d; g.K = d; g.epi = dfk::EPI_RESID; g.cpl = nullptr; g.h = h; g.stats_out = stats;
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             pending = true;
-            const float* cb = w.cpl_b + (size_t)l * ffn;
-            const float* cc = w.cpl_c + (size_t)l * d;
+            const float* cb = couple ? w.cpl_b + (size_t)l * ffn : nullptr;
+            const float* cc = couple ? w.cpl_c + (size_t)l * d : nullptr;
             if (!moe) {
                 if (!apply_norm(g_ln2)) return DF_ERR_HIP;
                 set_x(g, g_ln2);
@@ -262,8 +271,9 @@ struct Step {
                 m.w_up = reinterpret_cast<const char*>(w.w_exp_up) + (size_t)l * E * ffn * d * es;
                 m.w_down = reinterpret_cast<const char*>(w.w_exp_down) + (size_t)l * E * d * ffn * es;
                 m.cpl_b = cb; m.cpl_c = cc; m.B = B; m.d = d; m.E = E; m.k = c.top_k; m.Fe = (int)ffn;
+                m.ka = c.top_k_aux > 0 ? c.top_k_aux : c.top_k;
                 m.nflows = nflows; m.h = h;
-                m.ids_out = expert_ids ? expert_ids + (size_t)l * B * c.top_k : nullptr;
+                m.ids_out = expert_ids ? expert_ids + (size_t)l * B * kr : nullptr;
                 m.ids = at<int32_t>(L.ids); m.gates = at<float>(L.gates); m.offsets = at<int32_t>(L.offsets);
                 m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = at<float>(L.grows);
                 m.y_rows = at<float>(L.yrows);
@@ -280,7 +290,10 @@ struct Step {
             g.part = at<float>(L.gpart);
             set_x(g, w.lnf);   // final norm
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
-            if (dfk::mix_head(lg, B, c.vocab, nflows == 2, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
+            const int mode = nflows == 1 ? DF_MIX_PRIMARY
+                             : (c.variant & DF_VARIANT_AUX_OUTPUT) ? DF_MIX_AUX
+                             : (c.variant & DF_VARIANT_ALPHA_HALF) ? DF_MIX_HALF : DF_MIX_COLLISION;
+            if (dfk::mix_head(lg, B, c.vocab, mode, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
         }
         if (dfk::len_add(kv.len, B, 1, s) != hipSuccess) return DF_ERR_HIP;
         return DF_OK;
@@ -346,12 +359,12 @@ int df_kv_append(const df_config* cfg, const df_kv* kv, int32_t layer, const int
     return e == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
-int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t aux_on, float* d_p_mix,
+int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t mode, float* d_p_mix,
                 float* d_alpha, int32_t* d_next_tok, void* stream) {
     if (!d_logits || !d_p_mix || !d_alpha) return DF_ERR_NULL;
     if (batch < 1 || vocab < 1) return DF_ERR_SHAPE;
-    if (aux_on != 0 && aux_on != 1) return DF_ERR_ARG;
-    hipError_t e = dfk::mix_head(d_logits, batch, vocab, aux_on, d_p_mix, d_alpha, d_next_tok,
+    if (mode < DF_MIX_PRIMARY || mode > DF_MIX_HALF) return DF_ERR_ARG;
+    hipError_t e = dfk::mix_head(d_logits, batch, vocab, mode, d_p_mix, d_alpha, d_next_tok,
                                  reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? DF_OK : DF_ERR_HIP;
 }

@@ -34,8 +34,8 @@ hipError_t attention(const AttnArgs& a, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Row operations
 // ---------------------------------------------------------------------------
-// Mixture head over logits [B][2][V].
-hipError_t mix_head(const float* logits, int B, int V, int aux_on, float* p_mix, float* alpha,
+// Mixture head over logits [B][2][V]; mode: DF_MIX_*.
+hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
                     int32_t* next_tok, hipStream_t s);
 
 // K/V write at explicit positions (values fp32 [B][H][Dh]).
@@ -127,19 +127,20 @@ struct MoeArgs {
     const float* cpl_b;     // [Fe]
     const float* cpl_c;     // [d]
     int B, d, E, k, Fe, nflows;
+    int ka;                 // aux fan-out: first ka experts of the primary ranking
     float eps;
     const float* g_next;    // gain of the next norm
     float* h;               // [2B][d] residual (updated)
     float* x_next;          // [2B][d] LN(h; g_next)
-    int32_t* ids_out;       // [B][k] or nullptr
-    // workspace
-    int32_t* ids;           // [B][k]
-    float* gates;           // [B][2][k]
+    int32_t* ids_out;       // [B][max(k, ka)] or nullptr
+    // workspace (kr = max(k, ka) ranks per sequence)
+    int32_t* ids;           // [B][kr]
+    float* gates;           // [B][2][kr], zero beyond a flow's fan-out
     int32_t* offsets;       // [E+1]
-    int32_t* perm;          // [B*k]: sorted slot -> b*k + j
-    int32_t* inv;           // [B*k]: b*k + j -> sorted slot
-    float* g_rows;          // [B*k][2][Fe] fp32
-    float* y_rows;          // [B*k][2][d]
+    int32_t* perm;          // [B*kr]: sorted slot -> b*kk + j (kk ranks in use)
+    int32_t* inv;           // [B*kr]: b*kk + j -> sorted slot
+    float* g_rows;          // [B*kr][2][Fe] fp32
+    float* y_rows;          // [B*kr][2][d]
 };
 hipError_t moe(const MoeArgs& a, hipStream_t s);
 

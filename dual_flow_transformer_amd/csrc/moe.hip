@@ -3,16 +3,19 @@
 // aux flow reuses the set of experts the primary router picked, applying
 // them with its own mixture weights).
 //
-// 1. moe_route (one workgroup): primary top-k per sequence (descending
-//    logit, ties to the lower expert id), softmax gates of both flows over
-//    the chosen ids, then a stable counting sort of the (sequence, rank)
+// 1. moe_route (one workgroup): the primary ranking per sequence
+//    (descending logit, ties to the lower expert id), softmax gates of each
+//    flow over its fan-out (k primary ranks; the aux flow may take more or
+//    fewer of the primary's ranks: independent fan-outs, "Contribuciones
+//    Clave" item 3), then a stable counting sort of the (sequence, rank)
 //    pairs by expert: offsets[E+1], perm (sorted slot -> pair), inv.
-// 2. moe_up: one workgroup per (expert, 32 rows of the expert FFN); the
-//    expert's stacked rows are the primary and aux rows of its pairs, so each
-//    touched expert's weights are read once for both flows; untouched experts
-//    exit without reading. Epilogue: GELU, then b coupling on the aux row.
-// 3. moe_down: same grouping over the expert's down projection.
-// 4. moe_combine: gate-weighted sum over the k ranks in rank order, c
+// 2. moe_expert (up): one workgroup per (expert, 32 rows of the expert FFN);
+//    the expert's stacked rows are the primary and aux rows of its pairs, so
+//    each touched expert's weights are read once for both flows; untouched
+//    experts exit without reading. Epilogue: GELU, then the b coupling on the
+//    aux row where the primary also ran that expert.
+// 3. moe_expert (down): same grouping over the expert's down projection.
+// 4. moe_combine: gate-weighted sum over each flow's ranks in rank order, c
 //    coupling on the aux output, residual add. Integer work (ids, offsets,
 //    perm) is exact; no atomics.
 #include <algorithm>
@@ -31,52 +34,78 @@ using tile::ROWS;
 
 constexpr int kMaxK = 16;
 
-__global__ __launch_bounds__(256) void moe_route(const float* r, const float* r1_given, int B, int E, int k,
-                                                 int nflows, int32_t* ids, float* gates, int32_t* ids_out,
-                                                 int32_t* offsets, int32_t* perm, int32_t* inv) {
+// Routing: the primary ranking (top-kr of the primary router logits by
+// descending value, ties to the lower id), gates of each flow over its
+// fan-out (primary: the first k ranks, aux: the first ka), then a stable
+// counting sort of the (sequence, rank) pairs in use by expert. kk ranks per
+// sequence are in use: kr with both flows, k for the primary alone.
+// One workgroup of 1024 threads: wave w ranks sequences w, w + 16, ... by kr
+// rounds of a wave-wide argmax over the logits held in registers (E <= 1024,
+// 16 per lane); then thread e counts expert e's pairs, thread t places pair t.
+constexpr int kRouteThreads = 1024;
+constexpr int kPerLane = 16;   // E <= 64 * kPerLane
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route(const float* r, const float* r1_given, int B, int E,
+                                                           int k, int ka, int nflows, int32_t* ids, float* gates,
+                                                           int32_t* ids_out, int32_t* offsets, int32_t* perm,
+                                                           int32_t* inv) {
     __shared__ int32_t s_ids[64 * kMaxK];
     __shared__ int32_t s_cnt[1025];
-    const int tid = threadIdx.x;
-    if (tid < B) {
-        const int b = tid;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int kr = max(k, ka), kk = nflows == 2 ? kr : k;
+    for (int b = wv; b < B; b += kRouteThreads / 64) {
         const float* r1 = r1_given ? r1_given + (size_t)b * E : r + (size_t)(2 * b) * E;
+        float v[kPerLane];
+        #pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = lane + 64 * i;
+            v[i] = e < E ? r1[e] : -INFINITY;
+        }
+        unsigned taken = 0;   // bit i: entry lane + 64 i already ranked
         int sel[kMaxK];
-        float v1[kMaxK];
-        for (int j = 0; j < k; ++j) {
-            int best = -1;
+        float val[kMaxK];
+        for (int j = 0; j < kr; ++j) {
+            // lane-local best (largest value, then lowest id), then the wave's
             float bv = -INFINITY;
-            for (int e = 0; e < E; ++e) {
-                bool taken = false;
-                for (int q = 0; q < j; ++q) taken |= (sel[q] == e);
-                if (taken) continue;
-                const float v = r1[e];
-                if (best < 0 || v > bv) { best = e; bv = v; }
+            int bi = 0x7fffffff;
+            #pragma unroll
+            for (int i = 0; i < kPerLane; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) { bv = v[i]; bi = e; }
             }
-            sel[j] = best;
-            v1[j] = bv;
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            }
+            sel[j] = bi;
+            val[j] = bv;
+            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
         }
-        // gates: softmax over the chosen ids, per flow
-        float mx = v1[0], s = 0.f;
-        for (int j = 1; j < k; ++j) mx = fmaxf(mx, v1[j]);
-        float e1[kMaxK];
-        for (int j = 0; j < k; ++j) { e1[j] = expf(v1[j] - mx); s += e1[j]; }
-        for (int j = 0; j < k; ++j) {
-            gates[((size_t)b * 2) * k + j] = e1[j] / s;
-            ids[(size_t)b * k + j] = sel[j];
-            s_ids[b * k + j] = sel[j];
-            if (ids_out) ids_out[(size_t)b * k + j] = sel[j];
-        }
-        if (nflows == 2) {
-            const float* r2 = r + (size_t)(2 * b + 1) * E;
-            float mx2 = r2[sel[0]], s2 = 0.f;
-            for (int j = 1; j < k; ++j) mx2 = fmaxf(mx2, r2[sel[j]]);
-            float e2[kMaxK];
-            for (int j = 0; j < k; ++j) { e2[j] = expf(r2[sel[j]] - mx2); s2 += e2[j]; }
-            for (int j = 0; j < k; ++j) gates[((size_t)b * 2 + 1) * k + j] = e2[j] / s2;
+        if (lane == 0) {
+            // gates: softmax over each flow's ranks, zero beyond its fan-out
+            float mx = val[0], s = 0.f;
+            for (int j = 1; j < k; ++j) mx = fmaxf(mx, val[j]);
+            float e1[kMaxK];
+            for (int j = 0; j < k; ++j) { e1[j] = expf(val[j] - mx); s += e1[j]; }
+            for (int j = 0; j < kr; ++j) {
+                gates[((size_t)b * 2) * kr + j] = j < k ? e1[j] / s : 0.f;
+                ids[(size_t)b * kr + j] = sel[j];
+                if (ids_out) ids_out[(size_t)b * kr + j] = sel[j];
+            }
+            for (int j = 0; j < kk; ++j) s_ids[b * kk + j] = sel[j];
+            if (nflows == 2) {
+                const float* r2 = r + (size_t)(2 * b + 1) * E;
+                float mx2 = r2[sel[0]], s2 = 0.f;
+                for (int j = 1; j < ka; ++j) mx2 = fmaxf(mx2, r2[sel[j]]);
+                float e2[kMaxK];
+                for (int j = 0; j < ka; ++j) { e2[j] = expf(r2[sel[j]] - mx2); s2 += e2[j]; }
+                for (int j = 0; j < kr; ++j) gates[((size_t)b * 2 + 1) * kr + j] = j < ka ? e2[j] / s2 : 0.f;
+            }
         }
     }
     __syncthreads();
-    const int P = B * k;
+    const int P = B * kk;
     for (int e = tid; e < E; e += blockDim.x) {
         int c = 0;
         for (int t = 0; t < P; ++t) c += (s_ids[t] == e);
@@ -102,7 +131,7 @@ __global__ __launch_bounds__(256) void moe_route(const float* r, const float* r1
 struct ExpParams {
     const float* x;        // up: [2B][d] rows; down: g_rows [P][2][Fe] (fp32)
     const bf16_t* w;       // [E][N][K], each expert matrix in the fragment layout
-    int N, K, k, nflows, kw;
+    int N, K, kk, kp, nflows, kw;   // kk: ranks in use per sequence; kp: primary fan-out
     const int32_t* offsets;
     const int32_t* perm;
     const float* cpl_b;
@@ -136,7 +165,7 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
             const int m = min(mbase + mt * 16 + li, M - 1);
             const int s = off + m / p.nflows, f = m - (m / p.nflows) * p.nflows;
             size_t row;
-            if (p.up) row = (size_t)(2 * (p.perm[s] / p.k) + f);    // sequence b = pair / k
+            if (p.up) row = (size_t)(2 * (p.perm[s] / p.kk) + f);   // sequence b = pair / kk
             else row = (size_t)s * 2 + f;                         // g_rows[slot][flow]
             xrow[mt] = p.x + row * p.K + lg * 8;
         }
@@ -160,7 +189,8 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
                 p.g_out[((size_t)s * 2) * p.N + n] = g1;
                 if (p.nflows == 2) {
                     float g2 = 0.5f * y2 * (1.0f + erff(y2 * 0.70710678118654752f));
-                    g2 = fmaf(p.cpl_b[n], g1, g2);      // intermediate coupling b_l, per expert
+                    // intermediate coupling b_l, per expert the primary also ran (rank < kp)
+                    if (p.cpl_b && p.perm[s] % p.kk < p.kp) g2 = fmaf(p.cpl_b[n], g1, g2);
                     p.g_out[((size_t)s * 2 + 1) * p.N + n] = g2;
                 }
             } else {
@@ -171,17 +201,23 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
     }
 }
 
-// y_f[b] = sum_j gate_f[b][j] * y(slot of (b, j))_f; y2 += c * y1; h += y.
+// y_1[b] = sum_{j < k} gate_1[b][j] * y(slot of (b, j))_1, y_2 likewise over
+// j < ka; y2 += c * y1; h += y.
 __global__ __launch_bounds__(256) void moe_combine(const float* y_rows, const float* gates, const int32_t* inv,
-                                                   const float* cpl_c, int d, int k, int nflows, float* h) {
+                                                   const float* cpl_c, int d, int k, int ka, int kr, int kk,
+                                                   int nflows, float* h) {
     const int b = blockIdx.x;
     for (int n = threadIdx.x; n < d; n += blockDim.x) {
         float y1 = 0.f, y2 = 0.f;
         for (int j = 0; j < k; ++j) {
-            const size_t s = inv[(size_t)b * k + j];
-            y1 = fmaf(gates[((size_t)b * 2) * k + j], y_rows[(s * 2) * d + n], y1);
-            if (nflows == 2) y2 = fmaf(gates[((size_t)b * 2 + 1) * k + j], y_rows[(s * 2 + 1) * d + n], y2);
+            const size_t s = inv[(size_t)b * kk + j];
+            y1 = fmaf(gates[((size_t)b * 2) * kr + j], y_rows[(s * 2) * d + n], y1);
         }
+        if (nflows == 2)
+            for (int j = 0; j < ka; ++j) {
+                const size_t s = inv[(size_t)b * kk + j];
+                y2 = fmaf(gates[((size_t)b * 2 + 1) * kr + j], y_rows[(s * 2 + 1) * d + n], y2);
+            }
         h[(size_t)(2 * b) * d + n] += y1;
         if (nflows == 2) {
             if (cpl_c) y2 = fmaf(cpl_c[n], y1, y2);   // output coupling c_l
@@ -206,16 +242,18 @@ hipError_t launch_expert(ExpParams& p, int E, hipStream_t s) {
 }  // namespace
 
 hipError_t moe(const MoeArgs& a, hipStream_t s) {
-    if (a.k > kMaxK || a.B > 64 || a.E > 1024 || a.dtype != DF_BF16) return hipErrorInvalidValue;
+    const int ka = a.ka > 0 ? a.ka : a.k;
+    const int kr = std::max(a.k, ka), kk = a.nflows == 2 ? kr : a.k;
+    if (kr > kMaxK || a.B > 64 || a.E > 64 * kPerLane || a.dtype != DF_BF16) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(moe_route, dim3(1), dim3(256), 0, s, a.r, a.r1_given, a.B, a.E, a.k, a.nflows, a.ids,
-                       a.gates, a.ids_out, a.offsets, a.perm, a.inv);
+    hipLaunchKernelGGL(moe_route, dim3(1), dim3(kRouteThreads), 0, s, a.r, a.r1_given, a.B, a.E, a.k, ka, a.nflows,
+                       a.ids, a.gates, a.ids_out, a.offsets, a.perm, a.inv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ExpParams up;
     up.x = a.x;
     up.w = reinterpret_cast<const bf16_t*>(a.w_up);
-    up.N = a.Fe; up.K = a.d; up.k = a.k; up.nflows = a.nflows; up.offsets = a.offsets; up.perm = a.perm;
+    up.N = a.Fe; up.K = a.d; up.kk = kk; up.kp = a.k; up.nflows = a.nflows; up.offsets = a.offsets; up.perm = a.perm;
     up.cpl_b = a.cpl_b; up.g_out = a.g_rows; up.y_out = nullptr; up.up = true;
     e = launch_expert<2>(up, a.E, s);
     if (e != hipSuccess) return e;
@@ -225,8 +263,8 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     dn.N = a.d; dn.K = a.Fe; dn.g_out = nullptr; dn.y_out = a.y_rows; dn.up = false;
     e = launch_expert<2>(dn, a.E, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(256), 0, s, a.y_rows, a.gates, a.inv, a.cpl_c, a.d, a.k,
-                       a.nflows, a.h);
+    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(256), 0, s, a.y_rows, a.gates, a.inv, a.cpl_c, a.d, a.k, ka,
+                       kr, kk, a.nflows, a.h);
     return hipGetLastError();
 }
 

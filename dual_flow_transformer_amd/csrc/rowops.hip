@@ -128,9 +128,10 @@ __global__ void len_add_kernel(int32_t* len, int B, int inc) {
     if (b < B) len[b] += inc;
 }
 
-// Mixture head: one block of 1024 threads per sequence.
-__global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int V, int aux_on,
+// Mixture head: one block of 1024 threads per sequence. mode: DF_MIX_*.
+__global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int V, int mode,
                                                         float* p_mix, float* alpha, int32_t* next_tok) {
+    const int aux_on = mode != DF_MIX_PRIMARY;
     __shared__ float red[16];
     __shared__ float bv[16];
     __shared__ int bi[16];
@@ -155,7 +156,9 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int
     c1 = df::block_sum(c1, red);
     if (aux_on) s2 = df::block_sum(s2, red);
     float a = 1.f;
-    if (aux_on) a = fminf(1.f, fmaxf(0.5f, c1 / (s1 * s1)));
+    if (mode == DF_MIX_COLLISION) a = fminf(1.f, fmaxf(0.5f, c1 / (s1 * s1)));
+    else if (mode == DF_MIX_HALF) a = fminf(1.f, 0.5f * (1.f + c1 / (s1 * s1)));
+    else if (mode == DF_MIX_AUX) a = 0.f;
     const float w1 = a / s1;
     const float w2 = aux_on ? (1.f - a) / s2 : 0.f;
     float best = -1.f;
@@ -188,10 +191,10 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int
 
 }  // namespace
 
-hipError_t mix_head(const float* logits, int B, int V, int aux_on, float* p_mix, float* alpha,
+hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
                     int32_t* next_tok, hipStream_t s) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, logits, V, aux_on, p_mix, alpha, next_tok);
+    hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, logits, V, mode, p_mix, alpha, next_tok);
     return hipGetLastError();
 }
 

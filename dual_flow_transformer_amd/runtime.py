@@ -72,7 +72,8 @@ class DecodeModel:
 
         self.config = _abi.df_config(c.L, c.d, c.H, c.Dh, 0 if moe else c.F, c.V, c.E if moe else 0,
                                      c.top_k if moe else 0, c.Fe if moe else 0, c.B, self.S,
-                                     _abi.DF_BF16 if self.bf16 else _abi.DF_F32, c.eps)
+                                     _abi.DF_BF16 if self.bf16 else _abi.DF_F32, c.eps, c.variant,
+                                     c.top_k_aux if moe else 0)
         w = _abi.df_weights()
         w.tok_emb[0] = self.tok_emb[0].data_ptr()
         w.tok_emb[1] = self.tok_emb[1].data_ptr()
@@ -93,7 +94,7 @@ class DecodeModel:
         self.p_mix = torch.zeros(c.B, c.V, dtype=torch.float32, device=self.dev)
         self.alpha = torch.zeros(c.B, dtype=torch.float32, device=self.dev)
         self.next_tok = torch.zeros(c.B, dtype=torch.int32, device=self.dev)
-        self.expert_ids = torch.zeros(c.L, c.B, max(c.top_k, 1), dtype=torch.int32, device=self.dev)
+        self.expert_ids = torch.zeros(c.L, c.B, max(c.top_k, c.top_k_aux, 1), dtype=torch.int32, device=self.dev)
 
     # -- inputs -----------------------------------------------------------------
     def _up(self, dst: torch.Tensor, arr: np.ndarray):

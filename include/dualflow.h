@@ -64,8 +64,27 @@ enum {
 
 enum { DF_F32 = 0, DF_BF16 = 1 };
 
+/* Model variant switches (df_config.variant, bit flags): the ablations of
+ * gist.science/es/paper/2608.12385, section "Resultados" (a minimal Dual
+ * construction without the cross-flow coupling and without the probability
+ * mixture), and the other reading of the alpha floor. */
+enum {
+    DF_VARIANT_NO_COUPLING = 1,  /* a_l, b_l, c_l not applied (their vectors are not read) */
+    DF_VARIANT_AUX_OUTPUT = 2,   /* no mixture: p_mix = p_aux, alpha = 0 */
+    DF_VARIANT_ALPHA_HALF = 4    /* alpha = (1 + sum_v p_primary(v)^2) / 2; excludes AUX_OUTPUT */
+};
+
+/* Mixture modes of df_mix_head. */
+enum { DF_MIX_PRIMARY = 0, DF_MIX_COLLISION = 1, DF_MIX_AUX = 2, DF_MIX_HALF = 3 };
+
 /* Model and batch sizes. n_experts == 0 selects the dense MLP (width ffn);
  * n_experts > 0 selects the MoE MLP (top_k experts of width expert_ffn).
+ * top_k_aux (MoE): 0 = the aux flow replays the primary's top_k experts;
+ * 1..16 = the aux flow takes the first top_k_aux experts of the primary's
+ * ranking, with its own gates (independent expert fan-outs, section
+ * "Contribuciones Clave" item 3); the b_l coupling then applies on the
+ * experts the primary also ran (ranks below top_k). Must be 0 for dense
+ * models.
  * Supported: head_dim in {32, 64, 128}; d_model == n_heads * head_dim;
  * with DF_BF16, d_model, ffn and expert_ffn multiples of 256 and vocab and
  * n_experts multiples of 16; batch <= 64 (stacked rows 2*batch <= 128). */
@@ -83,6 +102,8 @@ typedef struct df_config {
     int32_t max_seq;     /* cache capacity (positions) = rows of pos_emb */
     int32_t dtype;       /* DF_F32 or DF_BF16 */
     float ln_eps;        /* LayerNorm epsilon */
+    int32_t variant;     /* DF_VARIANT_* flags, 0 = the full method */
+    int32_t top_k_aux;   /* MoE aux expert fan-out, 0 = replay of top_k */
 } df_config;
 
 /* Parameters, all device pointers, layer-major stacks. Embeddings and
@@ -133,8 +154,10 @@ size_t df_workspace_bytes(const df_config* cfg);
  *  d_logits [batch][2][vocab] or NULL: raw logits of both flows (fp32).
  *  d_p_mix [batch][vocab], d_alpha [batch]: the mixture output.
  *  d_next_tok [batch] or NULL: argmax of p_mix, ties to the lowest id.
- *  d_expert_ids [L][batch][top_k] or NULL: MoE expert ids of the primary
- *    (replayed by the aux flow), by descending logit, ties to the lower id.
+ *  d_expert_ids [L][batch][max(top_k, top_k_aux)] or NULL: MoE, the
+ *    primary's expert ranking by descending logit, ties to the lower id (the
+ *    first top_k are the primary's experts; the aux flow uses the first
+ *    top_k_aux, or the first top_k when top_k_aux = 0).
  * Appends the primary K/V at len[b] in every layer, then len[b] += 1 (on
  * the device). A sequence whose len[b] >= max_seq is not written and is
  * flagged in the device status (df_device_status). */
@@ -162,10 +185,13 @@ int df_kv_append(const df_config* cfg, const df_kv* kv, int32_t layer, const int
 
 /* The mixture head alone (section "Mecanismos Clave", mixture objective):
  * d_logits [batch][2][vocab] fp32. p_f = softmax(logits_f) over the whole
- * vocabulary; alpha = min(1, max(0.5, sum_v p_primary(v)^2));
- * p_mix = alpha p_primary + (1 - alpha) p_aux. aux_on = 0: alpha = 1 and
- * p_mix = p_primary (aux logits not read). d_next_tok may be NULL. */
-int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t aux_on,
+ * vocabulary; p_mix = alpha p_primary + (1 - alpha) p_aux with, by mode:
+ * DF_MIX_COLLISION: alpha = min(1, max(0.5, sum_v p_primary(v)^2));
+ * DF_MIX_HALF: alpha = (1 + sum_v p_primary(v)^2) / 2;
+ * DF_MIX_AUX: alpha = 0 (p_mix = p_aux);
+ * DF_MIX_PRIMARY: alpha = 1 (p_mix = p_primary, aux logits not read).
+ * d_next_tok (argmax of p_mix, ties to the lowest id) may be NULL. */
+int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t mode,
                 float* d_p_mix, float* d_alpha, int32_t* d_next_tok, void* stream);
 
 /* Asymmetric shared-K/V attention alone (section "Mecanismos Clave"): for

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 def good_config(**kw):
     base = dict(n_layers=2, d_model=256, n_heads=2, head_dim=128, ffn=1024, vocab=512, n_experts=0, top_k=0,
-                expert_ffn=0, batch=3, max_seq=64, dtype=_abi.DF_BF16, ln_eps=1e-5)
+                expert_ffn=0, batch=3, max_seq=64, dtype=_abi.DF_BF16, ln_eps=1e-5, variant=0, top_k_aux=0)
     base.update(kw)
     return _abi.df_config(*[base[f] for f, _ in _abi.df_config._fields_])
 
@@ -60,6 +60,10 @@ def test_workspace_query():
     (dict(ln_eps=0.0), _abi.DF_ERR_ARG),
     (dict(n_experts=16, top_k=17, expert_ffn=256), _abi.DF_ERR_SHAPE),
     (dict(n_experts=16, top_k=4, expert_ffn=256, dtype=_abi.DF_F32, d_model=256), _abi.DF_ERR_DTYPE),
+    (dict(variant=8), _abi.DF_ERR_ARG),                                        # unknown switch
+    (dict(variant=_abi.DF_VARIANT_AUX_OUTPUT | _abi.DF_VARIANT_ALPHA_HALF), _abi.DF_ERR_ARG),
+    (dict(top_k_aux=2), _abi.DF_ERR_SHAPE),                                    # dense model
+    (dict(n_experts=16, top_k=4, expert_ffn=256, top_k_aux=17), _abi.DF_ERR_SHAPE),
 ])
 def test_decode_rejects_bad_config(kw, code):
     cfg = good_config(**kw)
@@ -107,7 +111,8 @@ def test_other_entry_points_reject_bad_arguments():
     assert _abi.df_kv_append(cfg, kv, 0, None, 0x2000, 0x3000) == _abi.DF_ERR_NULL
     assert _abi.df_mix_head(None, 1, 10, 1, 0x1000, 0x2000) == _abi.DF_ERR_NULL
     assert _abi.df_mix_head(0x1000, 0, 10, 1, 0x1000, 0x2000) == _abi.DF_ERR_SHAPE
-    assert _abi.df_mix_head(0x1000, 1, 10, 3, 0x1000, 0x2000) == _abi.DF_ERR_ARG
+    assert _abi.df_mix_head(0x1000, 1, 10, 4, 0x1000, 0x2000) == _abi.DF_ERR_ARG
+    assert _abi.df_mix_head(0x1000, 1, 10, -1, 0x1000, 0x2000) == _abi.DF_ERR_ARG
     a = lambda **kw: _abi.df_attention_dual(kw.get("dt", 1), 0x10000, 0x20000, 2, 2, 64, kw.get("dh", 128),
                                             0x30000, 0x40000, None, 0x50000, 0x60000, kw.get("ws", 0x70000),
                                             kw.get("wsb", 1 << 30))

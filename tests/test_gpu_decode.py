@@ -191,3 +191,71 @@ def test_small_moe_router_replay():
         r = odf.decode_step(m, cache, tok, aux_on=True, router_logits=rl.cpu().numpy())
         assert np.array_equal(gm.expert_ids.cpu().numpy(), r.ids), "expert ids differ"
         _compare_step(cfg, gm, r)
+
+
+# Ablation switches and independent aux expert fan-out ([ES] Resultados;
+# Contribuciones Clave 3): GPU against the oracle, two steps each.
+@pytest.mark.parametrize("variant", [1, 2, 4, 3], ids=["no_coupling", "aux_output", "alpha_half", "minimal_dual"])
+def test_variants_dense(variant):
+    cfg = SMALL_BF16.replace(variant=variant)
+    say(f"variant {variant} dense")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    for step in range(2):
+        tok = src.step_tokens(step)
+        gm.decode_step(gm.tokens(tok))
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True)
+        _compare_step(cfg, gm, r)
+        if variant & 2:
+            assert torch.equal(gm.alpha, torch.zeros_like(gm.alpha))
+
+
+def test_no_coupling_tied_aux_equals_primary():
+    """Couplings off with tied embeddings: aux = primary bitwise on the GPU too,
+    with nonzero coupling vectors present."""
+    cfg = SMALL_BF16.replace(variant=1, tie_emb=True, sigma_cpl=0.5)
+    gm = DecodeModel(cfg, fill="device")
+    gm.decode_step(gm.tokens(Inputs(cfg).step_tokens(0)))
+    torch.cuda.synchronize()
+    assert torch.equal(gm.logits[:, 0], gm.logits[:, 1])
+
+
+@pytest.mark.parametrize("ka,variant", [(8, 0), (1, 0), (16, 0), (8, 1)], ids=["ka8", "ka1", "ka16", "ka8_nocpl"])
+def test_moe_aux_fanout(ka, variant):
+    """The aux flow takes the first ka experts of the primary ranking: logits,
+    p_mix and the reported ranking against the oracle (ranking bit-exact)."""
+    cfg = SMALL_MOE.replace(top_k_aux=ka, variant=variant)
+    say(f"moe aux fan-out ka={ka} variant={variant}")
+    gm = DecodeModel(cfg, fill="host")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    for step in range(2):
+        tok = src.step_tokens(step)
+        rl = gm.router_logits(step)
+        gm.decode_step(gm.tokens(tok), router_logits=rl)
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True, router_logits=rl.cpu().numpy())
+        assert np.array_equal(gm.expert_ids.cpu().numpy(), r.ids), "expert ranking differs"
+        _compare_step(cfg, gm, r)
+
+
+def test_moe_aux_fanout_leaves_primary_bitwise():
+    """Whatever the aux fan-out, the primary logits and the cache are bitwise
+    those of a primary-only step."""
+    cfg = SMALL_MOE.replace(top_k_aux=12)
+    src = Inputs(cfg)
+    a = DecodeModel(cfg, fill="device")
+    b = DecodeModel(cfg, fill="device")
+    for step in range(2):
+        tok = src.step_tokens(step)
+        rl = a.router_logits(step)
+        a.decode_step(a.tokens(tok), aux_on=True, router_logits=rl)
+        b.decode_step(b.tokens(tok), aux_on=False, router_logits=rl)
+        torch.cuda.synchronize()
+        assert torch.equal(a.logits[:, 0], b.logits[:, 0])
+        assert torch.equal(a.expert_ids, b.expert_ids)
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)

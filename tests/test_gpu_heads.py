@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
+MODES = {_abi.DF_MIX_PRIMARY: None, _abi.DF_MIX_COLLISION: odf.MIX_COLLISION, _abi.DF_MIX_AUX: odf.MIX_AUX,
+         _abi.DF_MIX_HALF: odf.MIX_HALF}
+
+
 def _mix(l, aux_on):
     B, _, V = l.shape
     dl = torch.from_numpy(np.ascontiguousarray(l, dtype=np.float32)).cuda()
@@ -29,14 +33,16 @@ def _mix(l, aux_on):
     return p.cpu().numpy(), a.cpu().numpy(), t.cpu().numpy()
 
 
-@pytest.mark.parametrize("V,scale,aux_on", [(32000, 1.0, 1), (517, 3.0, 1), (1000, 12.0, 1), (32000, 1.0, 0)])
+@pytest.mark.parametrize("V,scale,aux_on", [(32000, 1.0, 1), (517, 3.0, 1), (1000, 12.0, 1), (32000, 1.0, 0),
+                                            (32000, 1.0, 2), (1000, 12.0, 2), (32000, 1.0, 3), (1000, 12.0, 3)])
 def test_mix_head_random(V, scale, aux_on):
-    say(f"mix head V={V} scale={scale} aux_on={aux_on}")
+    say(f"mix head V={V} scale={scale} mode={aux_on}")
     B = 4
     l = synth.normal((B, 2, V), 5, synth.stream_id("mixl", V), scale, "f32")
     p, a, t = _mix(l, aux_on)
     for b in range(B):
-        rp, ra, _ = odf.mix_head(l[b, 0], l[b, 1] if aux_on else None)
+        mode = MODES[aux_on]
+        rp, ra, _ = odf.mix_head(l[b, 0], l[b, 1] if mode else None, mode or odf.MIX_COLLISION)
         assert max_abs(p[b], rp) < 1e-6 + 1e-4 * rp.max()
         assert abs(a[b] - ra) < 1e-5
         assert argmax_agrees(p[b], rp, t[b])
