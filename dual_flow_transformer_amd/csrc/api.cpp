@@ -12,6 +12,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kStackedRows = 128;   // df_stacked_gemv: above this, the tiled GEMM
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -394,8 +395,13 @@ int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t b
 }
 
 size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K) {
-    if ((dtype != DF_F32 && dtype != DF_BF16) || rows < 2 || (rows & 1) || N < 1 || K < 1) return 0;
-    if (dtype == DF_BF16 && (rows > 128 || K % 256 || N % 16)) return 0;
+    if ((dtype != DF_F32 && dtype != DF_BF16) || rows < 1 || N < 1 || K < 1) return 0;
+    if (dtype == DF_BF16 && rows > kStackedRows) {   // tiled GEMM: no scratch
+        if (N % 16 || K % 64) return 0;
+        return kAlign;
+    }
+    if (rows < 2 || (rows & 1)) return 0;
+    if (dtype == DF_BF16 && (K % 256 || N % 16)) return 0;
     if (dtype == DF_F32 && (rows > 16 || K % 4)) return 0;
     const dfk::GemvPlan pl = dfk::plan_gemv(dtype, N, K, rows);
     if (dtype == DF_BF16 && pl.MT == 0) return 0;
@@ -410,10 +416,13 @@ int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t ro
     if (need == 0) return DF_ERR_SHAPE;
     if (!aligned16(d_x) || !aligned16(d_w) || !aligned16(d_y) || (uintptr_t)d_ws % kAlign) return DF_ERR_ALIGN;
     if (ws_bytes < need) return DF_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (dtype == DF_BF16 && rows > kStackedRows)
+        return dfk::gemm(d_x, d_w, rows, N, K, dfk::GEMM_STORE, d_y, s) == hipSuccess ? DF_OK : DF_ERR_HIP;
     dfk::GemvArgs g{};
     g.dtype = dtype; g.x = d_x; g.w = d_w; g.N = N; g.K = K; g.B = rows / 2; g.nflows = 2;
     g.epi = dfk::EPI_STORE; g.out_f32 = d_y; g.part = reinterpret_cast<float*>(d_ws);
-    return dfk::gemv(g, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
+    return dfk::gemv(g, s) == hipSuccess ? DF_OK : DF_ERR_HIP;
 }
 
 int df_pack_weights(int32_t dtype, const void* d_src, void* d_dst, int64_t n_mats, int32_t rows, int32_t cols,

@@ -115,6 +115,17 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M);
 hipError_t gemv(const GemvArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Tiled GEMM for prefill: y[r][n] = sum_k x[r][k] w[n][k] (w bf16, fragment
+// layout; x fp32), N % 16 == 0, K % 64 == 0.
+// ---------------------------------------------------------------------------
+enum GemmEpi {
+    GEMM_STORE = 0,   // y = x w^T
+    GEMM_GELU = 1,    // y = GELU(x w^T)
+    GEMM_RESID = 2,   // y += x w^T (y: residual rows)
+};
+hipError_t gemm(const float* x, const void* w, int R, int N, int K, int epi, float* y, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // MoE with router replay
 // ---------------------------------------------------------------------------
 struct MoeArgs {

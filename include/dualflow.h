@@ -219,10 +219,12 @@ size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_
  * y[m][n] = sum_k x[m][k] w[n][k] for m < rows.
  *  d_x: fp32 [rows][K]; d_w: [N][K] in `dtype` (DF_F32 row-major, DF_BF16
  *  in the fragment layout of df_pack_weights); d_y: fp32 [rows][N].
- *  rows even (primary/aux row pairs), rows <= 128 (DF_F32: rows <= 16);
- *  DF_BF16: K a multiple of 256, N a multiple of 16. With DF_BF16 each x
- *  element enters the bf16 matrix cores as two bf16 parts whose sum is
- *  within 2^-17 of it.
+ *  rows <= 128: the decode projection (rows even: primary/aux row pairs;
+ *  DF_F32: rows <= 16; DF_BF16: K a multiple of 256, N of 16).
+ *  DF_BF16 and rows > 128: the tiled matrix-core GEMM of the prefill (any
+ *  row count; K a multiple of 64, N of 16).
+ *  With DF_BF16 each x element enters the bf16 matrix cores as two bf16
+ *  parts whose sum is within 2^-17 of it.
  *  d_ws: df_stacked_gemv_workspace_bytes bytes (split-K partial sums). */
 int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t rows, int32_t N, int32_t K,
                     float* d_y, void* d_ws, size_t ws_bytes, void* stream);

@@ -143,4 +143,6 @@ def test_pack_and_gemv_reject_bad_arguments():
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 24, 4096) == 0   # N % 16
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 4096, 4000) == 0  # K % 256
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 3, 4096, 4096) == 0   # odd rows
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 333, 4096, 2048) > 0  # tiled GEMM
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 333, 4096, 2000) == 0  # K % 64
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 4096, 4096) > 0
