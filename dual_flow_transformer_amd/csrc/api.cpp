@@ -76,6 +76,27 @@ WsLayout layout(const df_config& c) {
     return L;
 }
 
+// Compute-bound prefill (dense bf16, head_dim 128): chunk of Tc positions
+// per sequence, rows r = b * Tc + t.
+bool fast_prefill(const df_config& c) { return c.dtype == DF_BF16 && c.n_experts == 0 && c.head_dim == 128; }
+int prefill_chunk(const df_config& c) { return std::max(1, std::min(c.max_seq, DF_PREFILL_ROWS / c.batch)); }
+
+struct PrefillLayout {
+    size_t h, x, qkv, f, total;   // byte offsets from the workspace base
+};
+PrefillLayout prefill_layout(const df_config& c) {
+    PrefillLayout P{};
+    size_t o = layout(c).total;
+    const size_t R = (size_t)c.batch * prefill_chunk(c);
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    P.h = take(R * c.d_model * 4);
+    P.x = take(R * c.d_model * 4);
+    P.qkv = take(R * 3 * c.d_model * 4);
+    P.f = take(R * (size_t)c.ffn * 4);
+    P.total = o;
+    return P;
+}
+
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
 
 int check_config(const df_config* c) {
@@ -327,6 +348,11 @@ int df_decode_step(const df_config* cfg, const df_weights* w, const df_kv* kv, c
                   d_expert_ids, true);
 }
 
+size_t df_prefill_workspace_bytes(const df_config* cfg) {
+    if (check_config(cfg) != DF_OK) return 0;
+    return fast_prefill(*cfg) ? prefill_layout(*cfg).total : layout(*cfg).total;
+}
+
 int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* kv, const int32_t* d_tokens,
                        int32_t T, void* d_ws, size_t ws_bytes, void* stream) {
     int rc = check_config(cfg);
@@ -336,12 +362,55 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
     if (!d_tokens) return DF_ERR_NULL;
     if (T < 0 || T > cfg->max_seq) return DF_ERR_SHAPE;
     if ((rc = check_ws(*cfg, d_ws, ws_bytes))) return rc;
-    Step st{*cfg, *w, *kv, reinterpret_cast<char*>(d_ws), layout(*cfg), reinterpret_cast<hipStream_t>(stream)};
-    for (int t = 0; t < T; ++t) {
-        rc = st.run(d_tokens + t, T, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false);
-        if (rc) return rc;
+    if (ws_bytes < df_prefill_workspace_bytes(cfg)) return DF_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const df_config& c = *cfg;
+    if (!fast_prefill(c)) {
+        Step st{c, *w, *kv, reinterpret_cast<char*>(d_ws), layout(c), s};
+        for (int t = 0; t < T; ++t) {
+            rc = st.run(d_tokens + t, T, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false);
+            if (rc) return rc;
+        }
+        return DF_OK;
     }
-    return DF_OK;
+    // Standard causal Transformer over the prompt, chunk by chunk; every
+    // layer of a chunk sees the K/V its earlier chunks left in the cache.
+    char* ws = reinterpret_cast<char*>(d_ws);
+    const PrefillLayout P = prefill_layout(c);
+    int32_t* status = reinterpret_cast<int32_t*>(ws + layout(c).status);
+    float* h = reinterpret_cast<float*>(ws + P.h);
+    float* x = reinterpret_cast<float*>(ws + P.x);
+    float* qkv = reinterpret_cast<float*>(ws + P.qkv);
+    float* f = reinterpret_cast<float*>(ws + P.f);
+    const int B = c.batch, d = c.d_model, H = c.n_heads, Dh = c.head_dim, F = c.ffn;
+    const size_t es = 2;
+    const size_t kv_layer = (size_t)B * H * c.max_seq * Dh * es;
+    const int Tmax = prefill_chunk(c);
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    for (int t0 = 0; t0 < T; t0 += Tmax) {
+        const int Tc = std::min(Tmax, T - t0), R = B * Tc;
+        if (!ok(dfk::prefill_embed_rows(w->tok_emb[0], w->pos_emb, d_tokens, T, t0, Tc, kv->len, B, d, c.max_seq,
+                                        c.vocab, h, status, s)))
+            return DF_ERR_HIP;
+        for (int l = 0; l < c.n_layers; ++l) {
+            char* kc = reinterpret_cast<char*>(kv->k) + l * kv_layer;
+            char* vc = reinterpret_cast<char*>(kv->v) + l * kv_layer;
+            const char* wqkv = reinterpret_cast<const char*>(w->w_qkv) + (size_t)l * 3 * d * d * es;
+            const char* wo = reinterpret_cast<const char*>(w->w_o) + (size_t)l * d * d * es;
+            const char* wup = reinterpret_cast<const char*>(w->w_up) + (size_t)l * F * d * es;
+            const char* wdn = reinterpret_cast<const char*>(w->w_down) + (size_t)l * d * F * es;
+            if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R, d, x, s)) ||
+                !ok(dfk::gemm(x, wqkv, R, 3 * d, d, dfk::GEMM_STORE, qkv, s)) ||
+                !ok(dfk::prefill_kv(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, status, s)) ||
+                !ok(dfk::prefill_attention(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, x, s)) ||
+                !ok(dfk::gemm(x, wo, R, d, d, dfk::GEMM_RESID, h, s)) ||
+                !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R, d, x, s)) ||
+                !ok(dfk::gemm(x, wup, R, F, d, dfk::GEMM_GELU, f, s)) ||
+                !ok(dfk::gemm(f, wdn, R, d, F, dfk::GEMM_RESID, h, s)))
+                return DF_ERR_HIP;
+        }
+    }
+    return ok(dfk::len_add(kv->len, B, T, s)) ? DF_OK : DF_ERR_HIP;
 }
 
 int df_kv_append(const df_config* cfg, const df_kv* kv, int32_t layer, const int32_t* d_pos, const float* d_k,

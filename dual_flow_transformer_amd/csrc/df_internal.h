@@ -126,6 +126,24 @@ enum GemmEpi {
 hipError_t gemm(const float* x, const void* w, int R, int N, int K, int epi, float* y, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Prefill row kernels (rows r = b * Tc + t of one chunk of Tc positions
+// t0 .. t0 + Tc - 1 per sequence, sequence b at position len[b] + t0 + t).
+// ---------------------------------------------------------------------------
+// h[r] = primary token embedding + position row (fp32).
+hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_t* tok, int T, int t0, int Tc,
+                              const int32_t* len, int B, int d, int S_max, int V, float* h, int32_t* status,
+                              hipStream_t s);
+// x[r] = LayerNorm(h[r]) * g, d <= 4096.
+hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, float* x, hipStream_t s);
+// K/V columns of qkv rows [R][3 d] to the bf16 cache.
+hipError_t prefill_kv(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
+                      void* kc, void* vc, int32_t* status, hipStream_t s);
+// Causal attention of the chunk queries (Q columns of qkv) over the bf16
+// cache: o[r] for head h = softmax over keys 0 .. len[b] + t0 + t. Dh == 128.
+hipError_t prefill_attention(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
+                             const void* kc, const void* vc, float* o, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // MoE with router replay
 // ---------------------------------------------------------------------------
 struct MoeArgs {

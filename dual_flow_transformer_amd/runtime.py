@@ -86,8 +86,9 @@ class DecodeModel:
         w.w_out = self.w_out.data_ptr()
         self.weights = w
         self.kv = _abi.df_kv(self.k.data_ptr(), self.v.data_ptr(), self.len.data_ptr())
-        self.ws_bytes = _abi.df_workspace_bytes(self.config)
-        if self.ws_bytes == 0:
+        # one workspace for both calls (the prefill one is the larger)
+        self.ws_bytes = _abi.df_prefill_workspace_bytes(self.config)
+        if self.ws_bytes == 0 or _abi.df_workspace_bytes(self.config) == 0:
             raise ValueError(f"unsupported config {c}")
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.dev)
         self.logits = torch.zeros(c.B, 2, c.V, dtype=torch.float32, device=self.dev)

@@ -166,10 +166,31 @@ int df_decode_step(const df_config* cfg, const df_weights* w, const df_kv* kv,
                    float* d_logits, float* d_p_mix, float* d_alpha, int32_t* d_next_tok,
                    int32_t* d_expert_ids, void* d_ws, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace df_prefill_primary needs (>= df_workspace_bytes):
+ * dense bf16 models with head_dim 128 add room for one chunk of prompt rows
+ * (fp32 residual, normed rows, Q/K/V rows and FFN hidden rows). 0 when the
+ * config is invalid. */
+size_t df_prefill_workspace_bytes(const df_config* cfg);
+
+/* Rows (batch x positions) per chunk of the compute-bound prefill. */
+#define DF_PREFILL_ROWS 2048
+
 /* Primary-only prefill of T tokens per sequence (d_tokens [batch][T]) at
- * positions len[b] .. len[b]+T-1; the aux flow is skipped in prefill
- * (section "Arquitectura Central"). Advances len[b] by T. Runs the same
- * kernels as a primary-only decode step, one position at a time. */
+ * positions len[b] .. len[b]+T-1: the aux flow is skipped in prefill and
+ * the primary flow is a standard causal Transformer over the prompt
+ * (sections "Arquitectura Central" and "Costes de Inferencia vs.
+ * Entrenamiento"). Writes the K/V of every prompt position (rounded to the
+ * storage dtype) and advances len[b] by T; no logits are produced.
+ *  Dense bf16 models with head_dim 128: the prompt goes through in chunks
+ *    of Tc = max(1, min(max_seq, DF_PREFILL_ROWS / batch)) positions per
+ *    sequence; per chunk and layer the projections are tiled matrix-core
+ *    GEMMs over the batch * Tc rows, and a causal attention pass takes each
+ *    chunk query over the cached keys 0 .. its own position.
+ *  Other models: the kernels of a primary-only decode step, one position at
+ *    a time.
+ * ws_bytes must be at least df_prefill_workspace_bytes(cfg). Positions at or
+ * past max_seq are not written and are flagged in the device status; token
+ * ids outside [0, vocab) are clamped and flagged. */
 int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* kv,
                        const int32_t* d_tokens, int32_t T, void* d_ws, size_t ws_bytes,
                        void* stream);
