@@ -54,8 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"],
-                    help="c5 (default) / c3 / c4: full decode step; c2: the shared-K/V attention kernel alone")
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "prefill"],
+                    help="c5 (default) / c3 / c4: full decode step; c2: the shared-K/V attention kernel alone; "
+                         "prefill: primary prefill of 16 x 2048 tokens through the 1.3B dense model")
     ap.add_argument("--variant", type=int, default=0,
                     help="model variant switches: 1 couplings off, 2 aux output (no mixture), 4 alpha=(1+CP)/2")
     ap.add_argument("--top-k-aux", type=int, default=0,
@@ -220,6 +221,134 @@ def bench_attention(args):
     print(json.dumps(out), flush=True)
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def prefill_flops(cfg, T: int) -> dict:
+    """Algorithmic flops of a primary prefill of T positions per sequence from
+    an empty cache: 2 flops per multiply-add of every projection row (QKV, O,
+    up, down) and of the causal attention (scores and weighted values over
+    keys 0..t for position t)."""
+    proj = 2 * cfg.B * T * (4 * cfg.d * cfg.d + 2 * cfg.d * cfg.F) * cfg.L
+    attn = 2 * 2 * cfg.B * cfg.d * (T * (T + 1) // 2) * cfg.L
+    return {"projections": proj, "attention": attn, "total": proj + attn}
+
+
+def prefill_cpu_baseline(cfg, T: int, n_layers: int = 1, min_seconds: float = 10.0):
+    """The oracle's prefill as it stands on a bounded sample: sequence 0's
+    prompt through the first n_layers layers (inputs drawn before timing),
+    repeated until min_seconds; tokens/s scaled to the full depth."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dualflow as odf
+    from synth.workloads import Inputs
+
+    sub = cfg.replace(L=n_layers, B=1)
+    src = Inputs(sub)
+    model = odf.Model(src, keep_layers=True)
+    for l in range(n_layers):
+        model.layer(l)
+    model.w_out()
+    model.lnf()
+    prompt = Inputs(cfg).prompt()[:1, :T]
+    t, reps = 0.0, 0
+    while t < min_seconds or reps < 1:
+        cache = odf.Cache(sub, [0], src)
+        cache.lens[:] = 0
+        t0 = time.perf_counter()
+        odf.prefill_primary(model, cache, prompt)
+        t += time.perf_counter() - t0
+        reps += 1
+    # the oracle also forms the logits of every prompt position; the GPU
+    # prefill does not, so that part is timed alone and taken out
+    h = np.zeros((T, cfg.d))
+    t0 = time.perf_counter()
+    odf.layer_norm(h, model.lnf(), cfg.eps) @ model.w_out().T
+    t_head = time.perf_counter() - t0
+    per_layer = max(t / reps - t_head, 1e-9) / n_layers
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": T / (per_layer * cfg.L), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"sequence 0 of {cfg.B}: its {T}-token prompt through the first {n_layers} of {cfg.L} "
+                       f"layers, {reps} repetitions ({t:.1f} s, less {t_head:.1f} s per repetition for the "
+                       f"logits of every position); time scaled to {cfg.L} layers"), "host_cpus": os.cpu_count()}
+
+
+def bench_prefill(args):
+    """Primary prefill workload: 16 prompts of 2048 tokens through the 24-layer
+    d 2048 dense model (bf16 weights), empty cache. A step is one
+    df_prefill_primary call over all prompts (len reset to 0 before it). The
+    value is prompt tokens/s; the roofline is that of the tiled GEMM (the
+    projections), timed with HIP events on its stream, against the dense
+    bf16 matrix-core peak."""
+    import torch
+
+    from dual_flow_transformer_amd import _abi
+    from dual_flow_transformer_amd.runtime import DecodeModel
+    from synth.workloads import PREFILL_DENSE, Inputs
+
+    cfg = PREFILL_DENSE
+    T = cfg.prompt_len
+    log(f"[bench] prefill workload {cfg.name}: filling device inputs")
+    gm = DecodeModel(cfg, fill="device")
+    tok = gm.tokens(Inputs(cfg).prompt()).contiguous()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gm.len.zero_()
+        gm.prefill(tok)
+
+    W, K = args.warmup, args.steps
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    res = {}
+    for kclass in (1, 2):              # GEMM launches, then attention launches, each over the K steps
+        _abi.check(_abi.df_timing_enable(kclass), "df_timing_enable")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rc, kms, kn = _abi.df_timing_read()
+        _abi.check(rc, "df_timing_read")
+        res[kclass] = (e0.elapsed_time(e1) / K, kms, kn)
+    ms = min(res[1][0], res[2][0])
+    status = gm.status()
+    fl = prefill_flops(cfg, T)
+    tok_s = cfg.B * T / (ms / 1e3)
+    gemm_ms, gemm_n = res[1][1], res[1][2]
+    attn_ms, attn_n = res[2][1], res[2][2]
+    gemm_tf = fl["projections"] / (gemm_ms / K / 1e3) / 1e12
+    attn_tf = fl["attention"] / (attn_ms / K / 1e3) / 1e12
+    log(f"[bench] prefill {ms:.2f} ms/step, {tok_s:.0f} tok/s; GEMM {gemm_ms / K:.2f} ms/step ({gemm_tf:.0f} TF/s), "
+        f"attention {attn_ms / K:.2f} ms/step ({attn_tf:.0f} TF/s); status {status}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        del gm
+        torch.cuda.empty_cache()
+        cpu = prefill_cpu_baseline(cfg, T)
+        log(f"[bench] oracle prefill: {cpu['value']:.2f} tok/s")
+    out = {
+        "metric": "primary prefill tokens/s at 1 GPU; GEMM TFLOP/s vs dense bf16 matrix-core peak",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded random-init weights, uniform random prompt tokens)",
+        "config": {"workload": cfg.name, "layers": cfg.L, "d_model": cfg.d, "heads": cfg.H, "head_dim": cfg.Dh,
+                   "ffn": cfg.F, "global_batch": cfg.B, "prompt_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "gemm_bf16 (prefill projections)", "bound": "mfma", "achieved": gemm_tf,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tf / PEAK_BF16_TFLOPS,
+                     "traffic": None, "avg_launch_ms": gemm_ms / max(gemm_n, 1), "launches": gemm_n,
+                     "algorithmic_flops_per_launch": fl["projections"] * K / max(gemm_n, 1)},
+        "attention": {"kernel": "attn_prefill", "achieved_TFLOPs": attn_tf, "avg_launch_ms": attn_ms / max(attn_n, 1),
+                      "launches": attn_n, "algorithmic_flops_per_step": fl["attention"]},
+        "flops_per_step": fl, "device_status": status, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -228,6 +357,9 @@ def main():
         sys.exit(2)
     if args.workload == "c2":
         bench_attention(args)
+        return
+    if args.workload == "prefill":
+        bench_prefill(args)
         return
     import numpy as np
     import torch

@@ -387,6 +387,17 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
     const size_t kv_layer = (size_t)B * H * c.max_seq * Dh * es;
     const int Tmax = prefill_chunk(c);
     auto ok = [](hipError_t e) { return e == hipSuccess; };
+    auto timed = [&](int kclass, auto&& launch) -> hipError_t {   // HIP events around one launch
+        hipEvent_t e0, e1;
+        timing_events(kclass, &e0, &e1);
+        if (e0 && hipEventRecord(e0, s) != hipSuccess) return hipErrorUnknown;
+        const hipError_t e = launch();
+        if (e == hipSuccess && e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorUnknown;
+        return e;
+    };
+    auto gemm = [&](const float* xin, const char* wt, int R, int N, int K, int epi, float* y) {
+        return timed(1, [&] { return dfk::gemm(xin, wt, R, N, K, epi, y, s); });
+    };
     for (int t0 = 0; t0 < T; t0 += Tmax) {
         const int Tc = std::min(Tmax, T - t0), R = B * Tc;
         if (!ok(dfk::prefill_embed_rows(w->tok_emb[0], w->pos_emb, d_tokens, T, t0, Tc, kv->len, B, d, c.max_seq,
@@ -400,13 +411,15 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
             const char* wup = reinterpret_cast<const char*>(w->w_up) + (size_t)l * F * d * es;
             const char* wdn = reinterpret_cast<const char*>(w->w_down) + (size_t)l * d * F * es;
             if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R, d, x, s)) ||
-                !ok(dfk::gemm(x, wqkv, R, 3 * d, d, dfk::GEMM_STORE, qkv, s)) ||
+                !ok(gemm(x, wqkv, R, 3 * d, d, dfk::GEMM_STORE, qkv)) ||
                 !ok(dfk::prefill_kv(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, status, s)) ||
-                !ok(dfk::prefill_attention(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, x, s)) ||
-                !ok(dfk::gemm(x, wo, R, d, d, dfk::GEMM_RESID, h, s)) ||
+                !ok(timed(2, [&] {
+                    return dfk::prefill_attention(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, x, s);
+                })) ||
+                !ok(gemm(x, wo, R, d, d, dfk::GEMM_RESID, h)) ||
                 !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R, d, x, s)) ||
-                !ok(dfk::gemm(x, wup, R, F, d, dfk::GEMM_GELU, f, s)) ||
-                !ok(dfk::gemm(f, wdn, R, d, F, dfk::GEMM_RESID, h, s)))
+                !ok(gemm(x, wup, R, F, d, dfk::GEMM_GELU, f)) ||
+                !ok(gemm(f, wdn, R, d, F, dfk::GEMM_RESID, h)))
                 return DF_ERR_HIP;
         }
     }
@@ -539,7 +552,7 @@ const char* df_status_str(int code) {
 }
 
 int df_timing_enable(int32_t kclass) {
-    if (kclass != 0) return DF_ERR_ARG;
+    if (kclass < 0 || kclass > 2) return DF_ERR_ARG;
     std::lock_guard<std::mutex> lk(g_timing.mu);
     g_timing.kclass = kclass;
     g_timing.used = 0;

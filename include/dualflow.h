@@ -274,8 +274,9 @@ int df_device_status(void* d_ws, void* stream, int32_t* status_out);
 const char* df_status_str(int code);
 
 /* Kernel timing with HIP events on the launching stream. While enabled,
- * every launch of the kernels of class `kclass` (0 = attention partial
- * pass) is bracketed by a pair of events. df_timing_read synchronises
+ * every launch of the kernels of class `kclass` is bracketed by a pair of
+ * events: 0 = attention partial pass (decode), 1 = tiled GEMM (prefill
+ * projections), 2 = causal prefill attention. df_timing_read synchronises
  * them and returns the summed duration (ms) and the launch count, then
  * disables timing. At most 65536 launches are recorded. */
 int df_timing_enable(int32_t kclass);

@@ -99,6 +99,10 @@ C5_LARGE = Config("dense_32l_d4096_b16_ctx8192", L=32, d=4096, H=32, Dh=128, F=1
 
 PRESETS = {"c1": C1_TINY, "c2": C2_ATTN, "c3": C3_DENSE, "c4": C4_MOE, "c5": C5_LARGE}
 
+# Primary prefill of the 1.3B dense model: the 2048-position prompts whose
+# cache the dense decode workload starts from (16 sequences, empty cache).
+PREFILL_DENSE = C3_DENSE.replace(name="prefill_dense_1p3b_b16_t2048", ctx=0, S_max=2048, prompt_len=2048)
+
 
 def normal_quantiles(n: int) -> np.ndarray:
     """Phi^-1((i + 1/2) / n), i = 0..n-1, as float32."""
