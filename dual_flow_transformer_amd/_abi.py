@@ -40,7 +40,8 @@ class df_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float), ("variant", ctypes.c_int32), ("top_k_aux", ctypes.c_int32)]
+                ("ln_eps", ctypes.c_float), ("variant", ctypes.c_int32), ("top_k_aux", ctypes.c_int32),
+                ("prefill_rows", ctypes.c_int32)]
 
 
 class df_weights(ctypes.Structure):

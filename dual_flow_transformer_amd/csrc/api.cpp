@@ -79,20 +79,28 @@ WsLayout layout(const df_config& c) {
 // Compute-bound prefill (dense bf16, head_dim 128): chunk of Tc positions
 // per sequence, rows r = b * Tc + t.
 bool fast_prefill(const df_config& c) { return c.dtype == DF_BF16 && c.n_experts == 0 && c.head_dim == 128; }
-int prefill_chunk(const df_config& c) { return std::max(1, std::min(c.max_seq, DF_PREFILL_ROWS / c.batch)); }
+int prefill_chunk(const df_config& c) {
+    const int rows = c.prefill_rows > 0 ? c.prefill_rows : DF_PREFILL_ROWS;
+    return std::max(1, std::min(c.max_seq, rows / c.batch));
+}
 
+// Chunk buffers: fp32 residual rows h and Q/K/V rows; the GEMM operands
+// (normed rows / attention output, FFN hidden rows) as bf16 hi and lo planes
+// in the fragment layout, rows padded to a multiple of 16.
 struct PrefillLayout {
-    size_t h, x, qkv, f, total;   // byte offsets from the workspace base
+    size_t h, xh, xl, qkv, fh, fl, total;   // byte offsets from the workspace base
 };
 PrefillLayout prefill_layout(const df_config& c) {
     PrefillLayout P{};
     size_t o = layout(c).total;
-    const size_t R = (size_t)c.batch * prefill_chunk(c);
+    const size_t R = (size_t)c.batch * prefill_chunk(c), R16 = (R + 15) / 16 * 16;
     auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
     P.h = take(R * c.d_model * 4);
-    P.x = take(R * c.d_model * 4);
+    P.xh = take(R16 * c.d_model * 2);
+    P.xl = take(R16 * c.d_model * 2);
     P.qkv = take(R * 3 * c.d_model * 4);
-    P.f = take(R * (size_t)c.ffn * 4);
+    P.fh = take(R16 * (size_t)c.ffn * 2);
+    P.fl = take(R16 * (size_t)c.ffn * 2);
     P.total = o;
     return P;
 }
@@ -108,7 +116,7 @@ int check_config(const df_config* c) {
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return DF_ERR_SHAPE;
     if (c->d_model != c->n_heads * c->head_dim || c->d_model > 4096) return DF_ERR_SHAPE;
     if (c->batch > 64) return DF_ERR_SHAPE;
-    if (!(c->ln_eps > 0.f)) return DF_ERR_ARG;
+    if (!(c->ln_eps > 0.f) || c->prefill_rows < 0) return DF_ERR_ARG;
     if ((c->variant & ~(DF_VARIANT_NO_COUPLING | DF_VARIANT_AUX_OUTPUT | DF_VARIANT_ALPHA_HALF)) != 0 ||
         ((c->variant & DF_VARIANT_AUX_OUTPUT) && (c->variant & DF_VARIANT_ALPHA_HALF)))
         return DF_ERR_ARG;
@@ -379,9 +387,11 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
     const PrefillLayout P = prefill_layout(c);
     int32_t* status = reinterpret_cast<int32_t*>(ws + layout(c).status);
     float* h = reinterpret_cast<float*>(ws + P.h);
-    float* x = reinterpret_cast<float*>(ws + P.x);
     float* qkv = reinterpret_cast<float*>(ws + P.qkv);
-    float* f = reinterpret_cast<float*>(ws + P.f);
+    void* xh = ws + P.xh;
+    void* xl = ws + P.xl;
+    void* fh = ws + P.fh;
+    void* fl = ws + P.fl;
     const int B = c.batch, d = c.d_model, H = c.n_heads, Dh = c.head_dim, F = c.ffn;
     const size_t es = 2;
     const size_t kv_layer = (size_t)B * H * c.max_seq * Dh * es;
@@ -395,8 +405,8 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
         if (e == hipSuccess && e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorUnknown;
         return e;
     };
-    auto gemm = [&](const float* xin, const char* wt, int R, int N, int K, int epi, float* y) {
-        return timed(1, [&] { return dfk::gemm(xin, wt, R, N, K, epi, y, s); });
+    auto gemm = [&](const void* ah, const void* al, const char* wt, int R, int N, int K, int epi, float* y) {
+        return timed(1, [&] { return dfk::gemm(ah, al, wt, R, N, K, epi, y, fh, fl, s); });
     };
     for (int t0 = 0; t0 < T; t0 += Tmax) {
         const int Tc = std::min(Tmax, T - t0), R = B * Tc;
@@ -410,16 +420,16 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
             const char* wo = reinterpret_cast<const char*>(w->w_o) + (size_t)l * d * d * es;
             const char* wup = reinterpret_cast<const char*>(w->w_up) + (size_t)l * F * d * es;
             const char* wdn = reinterpret_cast<const char*>(w->w_down) + (size_t)l * d * F * es;
-            if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R, d, x, s)) ||
-                !ok(gemm(x, wqkv, R, 3 * d, d, dfk::GEMM_STORE, qkv)) ||
+            if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R, d, xh, xl, s)) ||
+                !ok(gemm(xh, xl, wqkv, R, 3 * d, d, dfk::GEMM_STORE, qkv)) ||
                 !ok(dfk::prefill_kv(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, status, s)) ||
                 !ok(timed(2, [&] {
-                    return dfk::prefill_attention(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, x, s);
+                    return dfk::prefill_attention(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s);
                 })) ||
-                !ok(gemm(x, wo, R, d, d, dfk::GEMM_RESID, h)) ||
-                !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R, d, x, s)) ||
-                !ok(gemm(x, wup, R, F, d, dfk::GEMM_GELU, f)) ||
-                !ok(gemm(f, wdn, R, d, F, dfk::GEMM_RESID, h)))
+                !ok(gemm(xh, xl, wo, R, d, d, dfk::GEMM_RESID, h)) ||
+                !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R, d, xh, xl, s)) ||
+                !ok(gemm(xh, xl, wup, R, F, d, dfk::GEMM_GELU_SPLIT, nullptr)) ||
+                !ok(gemm(fh, fl, wdn, R, d, F, dfk::GEMM_RESID, h)))
                 return DF_ERR_HIP;
         }
     }
@@ -478,9 +488,9 @@ int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t b
 
 size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K) {
     if ((dtype != DF_F32 && dtype != DF_BF16) || rows < 1 || N < 1 || K < 1) return 0;
-    if (dtype == DF_BF16 && rows > kStackedRows) {   // tiled GEMM: no scratch
-        if (N % 16 || K % 64) return 0;
-        return kAlign;
+    if (dtype == DF_BF16 && rows > kStackedRows) {   // tiled GEMM: the rows as hi / lo fragment planes
+        if (N % 16 || K % 32) return 0;
+        return 2 * align_up((size_t)(rows + 15) / 16 * 16 * K * 2);
     }
     if (rows < 2 || (rows & 1)) return 0;
     if (dtype == DF_BF16 && (K % 256 || N % 16)) return 0;
@@ -499,8 +509,14 @@ int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t ro
     if (!aligned16(d_x) || !aligned16(d_w) || !aligned16(d_y) || (uintptr_t)d_ws % kAlign) return DF_ERR_ALIGN;
     if (ws_bytes < need) return DF_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (dtype == DF_BF16 && rows > kStackedRows)
-        return dfk::gemm(d_x, d_w, rows, N, K, dfk::GEMM_STORE, d_y, s) == hipSuccess ? DF_OK : DF_ERR_HIP;
+    if (dtype == DF_BF16 && rows > kStackedRows) {
+        char* xh = reinterpret_cast<char*>(d_ws);
+        char* xl = xh + need / 2;
+        if (dfk::split_rows(d_x, rows, K, xh, xl, s) != hipSuccess) return DF_ERR_HIP;
+        return dfk::gemm(xh, xl, d_w, rows, N, K, dfk::GEMM_STORE, d_y, nullptr, nullptr, s) == hipSuccess
+                   ? DF_OK
+                   : DF_ERR_HIP;
+    }
     dfk::GemvArgs g{};
     g.dtype = dtype; g.x = d_x; g.w = d_w; g.N = N; g.K = K; g.B = rows / 2; g.nflows = 2;
     g.epi = dfk::EPI_STORE; g.out_f32 = d_y; g.part = reinterpret_cast<float*>(d_ws);

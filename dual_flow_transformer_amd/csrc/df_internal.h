@@ -115,15 +115,19 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M);
 hipError_t gemv(const GemvArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Tiled GEMM for prefill: y[r][n] = sum_k x[r][k] w[n][k] (w bf16, fragment
-// layout; x fp32), N % 16 == 0, K % 64 == 0.
+// Tiled GEMM for prefill: y[r][n] = sum_k x[r][k] w[n][k]; w bf16 [N][K] and
+// x as bf16 hi / lo planes [ceil(R/16)*16][K], all in the fragment layout
+// (mfma_tile.h). N % 16 == 0, K % 32 == 0.
 // ---------------------------------------------------------------------------
 enum GemmEpi {
-    GEMM_STORE = 0,   // y = x w^T
-    GEMM_GELU = 1,    // y = GELU(x w^T)
-    GEMM_RESID = 2,   // y += x w^T (y: residual rows)
+    GEMM_STORE = 0,        // y = x w^T (fp32 [R][N])
+    GEMM_GELU_SPLIT = 1,   // GELU(x w^T) as hi / lo fragment planes yh, yl [R16][N] (N % 32 == 0)
+    GEMM_RESID = 2,        // y += x w^T (y: fp32 residual rows [R][N])
 };
-hipError_t gemm(const float* x, const void* w, int R, int N, int K, int epi, float* y, hipStream_t s);
+hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
+                void* yl, hipStream_t s);
+// fp32 rows [R][K] -> hi / lo fragment planes (K % 32 == 0).
+hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Prefill row kernels (rows r = b * Tc + t of one chunk of Tc positions
@@ -133,15 +137,17 @@ hipError_t gemm(const float* x, const void* w, int R, int N, int K, int epi, flo
 hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_t* tok, int T, int t0, int Tc,
                               const int32_t* len, int B, int d, int S_max, int V, float* h, int32_t* status,
                               hipStream_t s);
-// x[r] = LayerNorm(h[r]) * g, d <= 4096.
-hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, float* x, hipStream_t s);
+// LayerNorm(h[r]) * g as hi / lo fragment planes xh, xl [R16][d]; d <= 4096, d % 32 == 0.
+hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, void* xh, void* xl,
+                              hipStream_t s);
 // K/V columns of qkv rows [R][3 d] to the bf16 cache.
 hipError_t prefill_kv(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
                       void* kc, void* vc, int32_t* status, hipStream_t s);
 // Causal attention of the chunk queries (Q columns of qkv) over the bf16
-// cache: o[r] for head h = softmax over keys 0 .. len[b] + t0 + t. Dh == 128.
+// cache: row r, head h = softmax over keys 0 .. len[b] + t0 + t, written as
+// hi / lo fragment planes oh, ol [R16][H * Dh]. Dh == 128.
 hipError_t prefill_attention(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
-                             const void* kc, const void* vc, float* o, hipStream_t s);
+                             const void* kc, const void* vc, void* oh, void* ol, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // MoE with router replay

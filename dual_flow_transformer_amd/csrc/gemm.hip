@@ -1,17 +1,22 @@
 // Tiled bf16 matrix-core GEMM for the primary prefill (many rows at once):
-// Y[r][n] = sum_k X[r][k] W[n][k], X fp32 rows, W bf16 in the 16x32 fragment
-// layout (mfma_tile.h). Prefill costs exactly a standard Transformer over the
-// prompt (gist.science/es/paper/2608.12385, "Costes de Inferencia vs.
-// Entrenamiento"), so this path is bound by the matrix cores, not by HBM.
+// Y[r][n] = sum_k X[r][k] W[n][k]. Prefill costs exactly a standard
+// Transformer over the prompt (gist.science/es/paper/2608.12385, "Costes de
+// Inferencia vs. Entrenamiento"), so this path is bound by the matrix cores,
+// not by HBM.
 //
-// Workgroup tile: 128 weight rows x 128 activation rows, 4 waves in a 2x2
-// grid of 64 x 64 each (4 x 4 v_mfma_f32_16x16x32_bf16 tiles). Per 64-wide
-// k step the activation tile is split into bf16 hi/lo parts into LDS
-// (double buffered, the next step's fp32 values already in registers) and
-// every wave takes its weight fragments straight from HBM/L2 (each
-// fragment is one contiguous 1 KiB piece), the next step's in flight. Both
-// activation parts go through the matrix cores into one fp32 accumulator,
-// as in the decode projections. Epilogues: store, GELU, residual add.
+// Both operands arrive in the 16 x 32 fragment layout (mfma_tile.h): W as
+// bf16 [N][K], X as two bf16 planes [R][K], hi = rne(x) and lo = rne(x - hi)
+// of the fp32 activation, written that way by the kernel that produces X
+// (LayerNorm, attention, the GELU epilogue, or split_rows below). Every
+// operand fetch, global or LDS, is then one contiguous 1 KiB piece per wave.
+//
+// Workgroup tile: 256 weight rows x 256 activation rows, 8 waves in a 2 x 4
+// grid of 128 x 64 each (8 x 4 v_mfma_f32_16x16x32_bf16 tiles, both
+// activation parts into one fp32 accumulator). Per 32-wide k block the
+// workgroup stages 48 fragments (16 of W, 16 + 16 of X) through LDS, double
+// buffered: the next block's fragments are in flight in registers while the
+// matrix cores work on the current one. Epilogues: fp32 store, residual add,
+// or GELU written back as hi/lo fragment planes for the next GEMM.
 #include "df_device.h"
 #include "df_internal.h"
 #include "mfma_tile.h"
@@ -24,143 +29,167 @@ using tile::bf16x8;
 using tile::f32x4;
 using tile::u32x4;
 
-constexpr int GT = 128;          // tile edge (weight rows and activation rows)
-constexpr int GK = 64;           // k per step
-constexpr int GXS = GK + 8;      // LDS row pitch (bf16 elements)
-constexpr int GTHREADS = 256;
-constexpr int XF4 = GT * GK / 4 / GTHREADS;   // fp32 float4 per thread per step (8)
+constexpr int TT = 256;                   // tile edge (weight rows and activation rows)
+constexpr int TT16 = TT / 16;             // 16-row fragments per tile edge
+constexpr int NWAVE = 8;
+constexpr int NTHREADS = 64 * NWAVE;
+constexpr int PIECES = 3 * TT16;          // fragments staged per k block (W, X hi, X lo)
+constexpr int PPW = PIECES / NWAVE;       // fragments per wave (6)
+constexpr int FRAG = 512;                 // bf16 elements per fragment (1 KiB)
+constexpr size_t kGemmLds = (size_t)2 * PIECES * FRAG * sizeof(bf16_t);   // 96 KiB
 
 struct GemmParams {
-    const float* x;     // [R][K]
+    const bf16_t* xh;   // [R16][K] fragment layout, R16 = ceil(R / 16) * 16
+    const bf16_t* xl;
     const bf16_t* w;    // [N][K] fragment layout
     int R, N, K;
-    int epi;            // GEMM_STORE / GEMM_GELU / GEMM_RESID
-    float* y;           // [R][N] (STORE, GELU) or the residual rows h (RESID)
+    int epi;            // GEMM_STORE / GEMM_RESID: y fp32 [R][N]; GEMM_GELU_SPLIT: yh / yl planes [R16][N]
+    float* y;
+    bf16_t* yh;
+    bf16_t* yl;
 };
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-constexpr size_t kGemmLds = (size_t)2 * 2 * GT * GXS * sizeof(bf16_t);
+// Offset of element (r, k) in the fragment layout of a [*][K] matrix.
+__device__ __forceinline__ size_t frag_off(int r, int k, int K) {
+    return ((size_t)((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
 
-__global__ __launch_bounds__(GTHREADS) void gemm_bf16(GemmParams p) {
-    extern __shared__ bf16_t lds[];   // [buffer][hi/lo][row][k]
-    auto xs = [&](int buf, int part) { return lds + (size_t)(buf * 2 + part) * GT * GXS; };
+__global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
+    extern __shared__ u32x4 lds[];   // [stage][piece][lane]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int li = lane & 15, lg = lane >> 4;
-    const int wn = wv & 1, wm = wv >> 1;
-    const int n0 = blockIdx.x * GT, r0 = blockIdx.y * GT;
-    const int KB = p.K / 32, NT16 = p.N / 16, nsteps = p.K / GK;
+    const int wn = wv & 1, wr = wv >> 1;           // 128 weight rows x 64 activation rows per wave
+    const int KB = p.K >> 5, NT16 = p.N >> 4, RT16 = (p.R + 15) >> 4;
+    // XCD-aware order: consecutive workgroups go to different XCDs, so give
+    // each XCD a contiguous band of tiles (shared activation rows in its L2).
+    const int gx = gridDim.x, total = gx * gridDim.y;
+    int id = blockIdx.x + gx * blockIdx.y;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+    const int n0 = (id % gx) * TT16, r0 = (id / gx) * TT16;   // first 16-row fragment of each edge
 
-    // activation tile loads: thread i covers rows (i / 16) + 16 j, columns 4 (i % 16)
-    auto load_x = [&](int step, float4 (&v)[XF4]) {
-        #pragma unroll
-        for (int j = 0; j < XF4; ++j) {
-            const int e = tid + j * GTHREADS;
-            const int row = e >> 4, c4 = e & 15;
-            const int r = min(r0 + row, p.R - 1);
-            v[j] = *reinterpret_cast<const float4*>(p.x + (size_t)r * p.K + step * GK + 4 * c4);
-        }
-    };
-    auto store_x = [&](int buf, const float4 (&v)[XF4]) {
-        #pragma unroll
-        for (int j = 0; j < XF4; ++j) {
-            const int e = tid + j * GTHREADS;
-            const int row = e >> 4, c4 = e & 15;
-            uint2 hv, lv;
-            df::split_hi_lo(v[j], hv, lv);
-            *reinterpret_cast<uint2*>(xs(buf, 0) + row * GXS + 4 * c4) = hv;
-            *reinterpret_cast<uint2*>(xs(buf, 1) + row * GXS + 4 * c4) = lv;
-        }
-    };
-    // weight fragments of this wave: 4 tiles of 16 rows x 2 k-blocks of 32
-    auto load_w = [&](int step, u32x4 (&a)[4][2]) {
-        #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int t16 = min((n0 + wn * 64 + nt * 16) / 16, NT16 - 1);
-            const bf16_t* q = p.w + (((size_t)t16 * KB + step * 2) * 64 + lane) * 8;
-            #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) a[nt][kb] = *reinterpret_cast<const u32x4*>(q + kb * 512);
-        }
-    };
-
-    f32x4 acc[4][4];
+    // this wave's share of the staged fragments: piece q = wv * PPW + j
+    const bf16_t* src[PPW];
     #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < PPW; ++j) {
+        const int q = wv * PPW + j;
+        const bf16_t* base;
+        int t16;
+        if (q < TT16) { base = p.w; t16 = min(n0 + q, NT16 - 1); }
+        else if (q < 2 * TT16) { base = p.xh; t16 = min(r0 + q - TT16, RT16 - 1); }
+        else { base = p.xl; t16 = min(r0 + q - 2 * TT16, RT16 - 1); }
+        src[j] = base + ((size_t)t16 * KB * 64 + lane) * 8;
+    }
+    auto fetch = [&](int kb, u32x4 (&v)[PPW]) {
+        #pragma unroll
+        for (int j = 0; j < PPW; ++j) v[j] = *reinterpret_cast<const u32x4*>(src[j] + (size_t)kb * FRAG);
+    };
+    auto stash = [&](int st, const u32x4 (&v)[PPW]) {
+        #pragma unroll
+        for (int j = 0; j < PPW; ++j) lds[((size_t)st * PIECES + wv * PPW + j) * 64 + lane] = v[j];
+    };
+
+    f32x4 acc[8][4];
+    #pragma unroll
+    for (int i = 0; i < 8; ++i)
         #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    float4 xv[XF4];
-    u32x4 wa[4][2], wb[4][2];
-    load_x(0, xv);
-    load_w(0, wa);
-    store_x(0, xv);
+    u32x4 pre[PPW];
+    fetch(0, pre);
+    stash(0, pre);
     __syncthreads();
-    for (int step = 0; step < nsteps; ++step) {
-        const int buf = step & 1;
-        const bool more = step + 1 < nsteps;
-        if (more) {
-            load_x(step + 1, xv);
-            load_w(step + 1, wb);
+    for (int kb = 0; kb < KB; ++kb) {
+        const int st = kb & 1;
+        fetch(min(kb + 1, KB - 1), pre);          // unconditional: keeps the waits exact
+        const u32x4* S = lds + (size_t)st * PIECES * 64;
+        bf16x8 bh[4], bl[4];
+        #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            bh[mt] = __builtin_bit_cast(bf16x8, S[(TT16 + wr * 4 + mt) * 64 + lane]);
+            bl[mt] = __builtin_bit_cast(bf16x8, S[(2 * TT16 + wr * 4 + mt) * 64 + lane]);
         }
         #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 bh[4], bl[4];
+        for (int nt = 0; nt < 8; ++nt) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, S[(wn * 8 + nt) * 64 + lane]);
             #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const int o = (wm * 64 + mt * 16 + li) * GXS + kb * 32 + lg * 8;
-                bh[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs(buf, 0) + o));
-                bl[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs(buf, 1) + o));
-            }
-            #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, wa[nt][kb]);
-                #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[mt], acc[nt][mt], 0, 0, 0);
-                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[mt], acc[nt][mt], 0, 0, 0);
-                }
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[mt], acc[nt][mt], 0, 0, 0);
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[mt], acc[nt][mt], 0, 0, 0);
             }
         }
-        if (more) {
-            store_x(buf ^ 1, xv);
-            #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) wa[nt][kb] = wb[nt][kb];
-        }
+        stash(st ^ 1, pre);    // the other stage: every wave left it at the last barrier
         __syncthreads();
     }
 
     // lane holds D[n = 4 lg + i][r = li] of each 16 x 16 tile
+    const int li = lane & 15, lg = lane >> 4;
     #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn * 64 + nt * 16 + 4 * lg;
+    for (int nt = 0; nt < 8; ++nt) {
+        const int n = (n0 + wn * 8 + nt) * 16 + 4 * lg;
         #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int r = r0 + wm * 64 + mt * 16 + li;
+            const int r = (r0 + wr * 4 + mt) * 16 + li;
             if (r >= p.R || n >= p.N) continue;
             float4 v = make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
-            float4* dst = reinterpret_cast<float4*>(p.y + (size_t)r * p.N + n);
-            if (p.epi == GEMM_GELU) {
+            if (p.epi == GEMM_GELU_SPLIT) {
                 v.x = gelu(v.x); v.y = gelu(v.y); v.z = gelu(v.z); v.w = gelu(v.w);
-            } else if (p.epi == GEMM_RESID) {
-                const float4 h = *dst;
-                v.x += h.x; v.y += h.y; v.z += h.z; v.w += h.w;
+                uint2 hv, lv;
+                df::split_hi_lo(v, hv, lv);
+                const size_t o = frag_off(r, n, p.N);
+                *reinterpret_cast<uint2*>(p.yh + o) = hv;
+                *reinterpret_cast<uint2*>(p.yl + o) = lv;
+            } else {
+                float4* dst = reinterpret_cast<float4*>(p.y + (size_t)r * p.N + n);
+                if (p.epi == GEMM_RESID) {
+                    const float4 h = *dst;
+                    v.x += h.x; v.y += h.y; v.z += h.z; v.w += h.w;
+                }
+                *dst = v;
             }
-            *dst = v;
         }
     }
 }
 
+// fp32 rows [R][K] (row-major) -> hi / lo fragment planes; one thread per
+// eight consecutive k of one row.
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* x, int R, int K, bf16_t* xh, bf16_t* xl) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per_row = K >> 3;
+    if (i >= (size_t)R * per_row) return;
+    const int r = (int)(i / per_row), k = (int)(i - (size_t)r * per_row) * 8;
+    const float4 a = *reinterpret_cast<const float4*>(x + (size_t)r * K + k);
+    const float4 b = *reinterpret_cast<const float4*>(x + (size_t)r * K + k + 4);
+    uint2 h0, l0, h1, l1;
+    df::split_hi_lo(a, h0, l0);
+    df::split_hi_lo(b, h1, l1);
+    const size_t o = frag_off(r, k, K);
+    *reinterpret_cast<u32x4*>(xh + o) = (u32x4){h0.x, h0.y, h1.x, h1.y};
+    *reinterpret_cast<u32x4*>(xl + o) = (u32x4){l0.x, l0.y, l1.x, l1.y};
+}
+
 }  // namespace
 
-hipError_t gemm(const float* x, const void* w, int R, int N, int K, int epi, float* y, hipStream_t s) {
-    if (R < 1 || N < 16 || N % 16 || K < GK || K % GK) return hipErrorInvalidValue;
-    GemmParams p{x, reinterpret_cast<const bf16_t*>(w), R, N, K, epi, y};
+hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
+                void* yl, hipStream_t s) {
+    if (R < 1 || N < 16 || N % 16 || K < 32 || K % 32) return hipErrorInvalidValue;
+    if (epi == GEMM_GELU_SPLIT ? (!yh || !yl || N % 32) : !y) return hipErrorInvalidValue;
+    GemmParams p{reinterpret_cast<const bf16_t*>(xh), reinterpret_cast<const bf16_t*>(xl),
+                 reinterpret_cast<const bf16_t*>(w), R, N, K, epi, y, reinterpret_cast<bf16_t*>(yh),
+                 reinterpret_cast<bf16_t*>(yl)};
     hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&gemm_bf16), kGemmLds);
     if (e != hipSuccess) return e;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(gemm_bf16, dim3((N + GT - 1) / GT, (R + GT - 1) / GT), dim3(GTHREADS), kGemmLds, s, p);
+    hipLaunchKernelGGL(gemm_bf16, dim3((N + TT - 1) / TT, (R + TT - 1) / TT), dim3(NTHREADS), kGemmLds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStream_t s) {
+    if (R < 1 || K < 32 || K % 32) return hipErrorInvalidValue;
+    const size_t n = (size_t)R * (K / 8);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, R, K,
+                       reinterpret_cast<bf16_t*>(xh), reinterpret_cast<bf16_t*>(xl));
     return hipGetLastError();
 }
 

@@ -34,32 +34,62 @@ __global__ __launch_bounds__(256) void prefill_embed(const bf16_t* emb, const bf
         h[(size_t)r * d + i] = df::bf16_to_f32(emb[(size_t)id * d + i]) + df::bf16_to_f32(pos_emb[(size_t)pos * d + i]);
 }
 
-// x[r] = LN(h[r]; g) for R rows of width d (one block per row, two passes
-// over the row held in registers).
-__global__ __launch_bounds__(256) void prefill_ln(const float* h, const float* g, float eps, int d, float* x) {
+// Offset of element (r, k) in the fragment layout of a [*][K] matrix.
+__device__ __forceinline__ size_t frag_off(int r, int k, int K) {
+    return ((size_t)((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
+// LN(h[r]; g) for R rows of width d as hi / lo fragment planes: one block
+// per row, each thread up to two runs of eight columns held in registers.
+__global__ __launch_bounds__(256) void prefill_ln(const float* h, const float* g, float eps, int d, bf16_t* xh,
+                                                  bf16_t* xl) {
     __shared__ float red[16];
     const int r = blockIdx.x;
     const float* hr = h + (size_t)r * d;
-    float v[16];
+    float4 v[2][2];
     float s = 0.f;
     #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int i = threadIdx.x + 256 * e;
-        v[e] = i < d ? hr[i] : 0.f;
-        s += v[e];
+    for (int e = 0; e < 2; ++e) {
+        const int k = 8 * (threadIdx.x + 256 * e);
+        if (k < d) {
+            v[e][0] = *reinterpret_cast<const float4*>(hr + k);
+            v[e][1] = *reinterpret_cast<const float4*>(hr + k + 4);
+        } else {
+            v[e][0] = v[e][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        s += (v[e][0].x + v[e][0].y + v[e][0].z + v[e][0].w) + (v[e][1].x + v[e][1].y + v[e][1].z + v[e][1].w);
     }
     const float mean = df::block_sum(s, red) / (float)d;
     float q = 0.f;
     #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int i = threadIdx.x + 256 * e;
-        if (i < d) { const float t = v[e] - mean; q = fmaf(t, t, q); }
+    for (int e = 0; e < 2; ++e) {
+        if (8 * (threadIdx.x + 256 * e) >= d) continue;
+        #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float4 t = v[e][u];
+            q = fmaf(t.x - mean, t.x - mean, q);
+            q = fmaf(t.y - mean, t.y - mean, q);
+            q = fmaf(t.z - mean, t.z - mean, q);
+            q = fmaf(t.w - mean, t.w - mean, q);
+        }
     }
     const float rstd = 1.0f / sqrtf(df::block_sum(q, red) / (float)d + eps);
     #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int i = threadIdx.x + 256 * e;
-        if (i < d) x[(size_t)r * d + i] = (v[e] - mean) * rstd * g[i];
+    for (int e = 0; e < 2; ++e) {
+        const int k = 8 * (threadIdx.x + 256 * e);
+        if (k >= d) continue;
+        const float4 g0 = *reinterpret_cast<const float4*>(g + k);
+        const float4 g1 = *reinterpret_cast<const float4*>(g + k + 4);
+        const float4 a = make_float4((v[e][0].x - mean) * rstd * g0.x, (v[e][0].y - mean) * rstd * g0.y,
+                                     (v[e][0].z - mean) * rstd * g0.z, (v[e][0].w - mean) * rstd * g0.w);
+        const float4 b = make_float4((v[e][1].x - mean) * rstd * g1.x, (v[e][1].y - mean) * rstd * g1.y,
+                                     (v[e][1].z - mean) * rstd * g1.z, (v[e][1].w - mean) * rstd * g1.w);
+        uint2 h0, l0, h1, l1;
+        df::split_hi_lo(a, h0, l0);
+        df::split_hi_lo(b, h1, l1);
+        const size_t o = frag_off(r, k, d);
+        *reinterpret_cast<u32x4*>(xh + o) = (u32x4){h0.x, h0.y, h1.x, h1.y};
+        *reinterpret_cast<u32x4*>(xl + o) = (u32x4){l0.x, l0.y, l1.x, l1.y};
     }
 }
 
@@ -88,7 +118,8 @@ __global__ __launch_bounds__(256) void prefill_kv_store(const float* qkv, int Tc
 // queries. Per block of 64 keys: S^T = K Q^T on the matrix cores (K from
 // LDS, Q as bf16 hi/lo parts in registers), online softmax per query in the
 // log2 domain, P (hi/lo parts through LDS) then O^T += V^T P^T with V
-// transposed into LDS. fp32 accumulation throughout.
+// transposed into LDS. fp32 accumulation throughout; the output rows leave
+// as hi / lo fragment planes, the operand form of the next GEMM.
 constexpr int ADH = 128;
 constexpr int AKB = 64;                 // keys per block
 constexpr int KSP = ADH + 8;            // K row pitch in LDS
@@ -97,7 +128,7 @@ constexpr int PSP = AKB + 8;            // P row pitch
 
 __global__ __launch_bounds__(256) void attn_prefill(const float* qkv, int Tc, int t0, const int32_t* len, int H,
                                                     int S_max, const bf16_t* kc, const bf16_t* vc, float scale_log2,
-                                                    float* o) {
+                                                    bf16_t* oh, bf16_t* ol) {
     __shared__ bf16_t Ks[AKB * KSP];
     __shared__ bf16_t Vt[ADH * VSP];
     __shared__ bf16_t Ps[4][2][16 * PSP];
@@ -214,11 +245,15 @@ __global__ __launch_bounds__(256) void attn_prefill(const float* qkv, int Tc, in
     l += __shfl_xor(l, 32, 64);
     if (!q_ok) return;
     const float inv = 1.0f / l;
-    float* orow = o + (size_t)(b * Tc + t_q) * d + h * ADH;
+    const int row = b * Tc + t_q;
     #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
         const float4 v = make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
-        *reinterpret_cast<float4*>(orow + dt * 16 + 4 * lg) = v;
+        uint2 hv, lv;
+        df::split_hi_lo(v, hv, lv);
+        const size_t o = frag_off(row, h * ADH + dt * 16 + 4 * lg, d);
+        *reinterpret_cast<uint2*>(oh + o) = hv;
+        *reinterpret_cast<uint2*>(ol + o) = lv;
     }
 }
 
@@ -233,10 +268,12 @@ hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_
     return hipGetLastError();
 }
 
-hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, float* x, hipStream_t s) {
-    if (d > 16 * 256) return hipErrorInvalidValue;
+hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, void* xh, void* xl,
+                              hipStream_t s) {
+    if (d > 16 * 256 || d % 32) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(prefill_ln, dim3(R), dim3(256), 0, s, h, g, eps, d, x);
+    hipLaunchKernelGGL(prefill_ln, dim3(R), dim3(256), 0, s, h, g, eps, d, reinterpret_cast<bf16_t*>(xh),
+                       reinterpret_cast<bf16_t*>(xl));
     return hipGetLastError();
 }
 
@@ -249,12 +286,12 @@ hipError_t prefill_kv(const float* qkv, int B, int Tc, int t0, const int32_t* le
 }
 
 hipError_t prefill_attention(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
-                             const void* kc, const void* vc, float* o, hipStream_t s) {
+                             const void* kc, const void* vc, void* oh, void* ol, hipStream_t s) {
     if (Dh != ADH) return hipErrorInvalidValue;
     (void)hipGetLastError();
     hipLaunchKernelGGL(attn_prefill, dim3((Tc + 63) / 64, H, B), dim3(256), 0, s, qkv, Tc, t0, len, H, S_max,
                        reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
-                       df::kLog2e / sqrtf((float)Dh), o);
+                       df::kLog2e / sqrtf((float)Dh), reinterpret_cast<bf16_t*>(oh), reinterpret_cast<bf16_t*>(ol));
     return hipGetLastError();
 }
 

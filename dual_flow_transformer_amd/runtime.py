@@ -34,7 +34,7 @@ class DecodeModel:
     device into the fragment layout the library reads (df_pack_weights)."""
 
     def __init__(self, cfg: Config, device: str = "cuda", fill: str = "device", src: Optional[Inputs] = None,
-                 max_seq: Optional[int] = None):
+                 max_seq: Optional[int] = None, prefill_rows: int = 0):
         self.cfg = cfg
         self.dev = torch.device(device)
         self.src = src or Inputs(cfg)
@@ -73,7 +73,7 @@ class DecodeModel:
         self.config = _abi.df_config(c.L, c.d, c.H, c.Dh, 0 if moe else c.F, c.V, c.E if moe else 0,
                                      c.top_k if moe else 0, c.Fe if moe else 0, c.B, self.S,
                                      _abi.DF_BF16 if self.bf16 else _abi.DF_F32, c.eps, c.variant,
-                                     c.top_k_aux if moe else 0)
+                                     c.top_k_aux if moe else 0, prefill_rows)
         w = _abi.df_weights()
         w.tok_emb[0] = self.tok_emb[0].data_ptr()
         w.tok_emb[1] = self.tok_emb[1].data_ptr()

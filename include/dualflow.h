@@ -104,6 +104,7 @@ typedef struct df_config {
     float ln_eps;        /* LayerNorm epsilon */
     int32_t variant;     /* DF_VARIANT_* flags, 0 = the full method */
     int32_t top_k_aux;   /* MoE aux expert fan-out, 0 = replay of top_k */
+    int32_t prefill_rows; /* rows (batch x positions) per prefill chunk, 0 = DF_PREFILL_ROWS */
 } df_config;
 
 /* Parameters, all device pointers, layer-major stacks. Embeddings and
@@ -167,13 +168,13 @@ int df_decode_step(const df_config* cfg, const df_weights* w, const df_kv* kv,
                    int32_t* d_expert_ids, void* d_ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace df_prefill_primary needs (>= df_workspace_bytes):
- * dense bf16 models with head_dim 128 add room for one chunk of prompt rows
- * (fp32 residual, normed rows, Q/K/V rows and FFN hidden rows). 0 when the
- * config is invalid. */
+ * dense bf16 models with head_dim 128 add room for one chunk of R prompt
+ * rows, about R * (5 d + ffn) * 4 bytes (fp32 residual and Q/K/V rows, the
+ * GEMM operands as bf16 hi/lo planes). 0 when the config is invalid. */
 size_t df_prefill_workspace_bytes(const df_config* cfg);
 
-/* Rows (batch x positions) per chunk of the compute-bound prefill. */
-#define DF_PREFILL_ROWS 2048
+/* Default rows (batch x positions) per chunk of the compute-bound prefill. */
+#define DF_PREFILL_ROWS 16384
 
 /* Primary-only prefill of T tokens per sequence (d_tokens [batch][T]) at
  * positions len[b] .. len[b]+T-1: the aux flow is skipped in prefill and
@@ -182,8 +183,8 @@ size_t df_prefill_workspace_bytes(const df_config* cfg);
  * Entrenamiento"). Writes the K/V of every prompt position (rounded to the
  * storage dtype) and advances len[b] by T; no logits are produced.
  *  Dense bf16 models with head_dim 128: the prompt goes through in chunks
- *    of Tc = max(1, min(max_seq, DF_PREFILL_ROWS / batch)) positions per
- *    sequence; per chunk and layer the projections are tiled matrix-core
+ *    of Tc = max(1, min(max_seq, rows / batch)) positions per sequence, rows
+ *    = cfg->prefill_rows or DF_PREFILL_ROWS; per chunk and layer the projections are tiled matrix-core
  *    GEMMs over the batch * Tc rows, and a causal attention pass takes each
  *    chunk query over the cached keys 0 .. its own position.
  *  Other models: the kernels of a primary-only decode step, one position at
@@ -243,10 +244,11 @@ size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_
  *  rows <= 128: the decode projection (rows even: primary/aux row pairs;
  *  DF_F32: rows <= 16; DF_BF16: K a multiple of 256, N of 16).
  *  DF_BF16 and rows > 128: the tiled matrix-core GEMM of the prefill (any
- *  row count; K a multiple of 64, N of 16).
+ *  row count; K a multiple of 32, N of 16).
  *  With DF_BF16 each x element enters the bf16 matrix cores as two bf16
  *  parts whose sum is within 2^-17 of it.
- *  d_ws: df_stacked_gemv_workspace_bytes bytes (split-K partial sums). */
+ *  d_ws: df_stacked_gemv_workspace_bytes bytes (split-K partial sums, or for
+ *  the tiled GEMM the rows as bf16 hi / lo planes). */
 int df_stacked_gemv(int32_t dtype, const float* d_x, const void* d_w, int32_t rows, int32_t N, int32_t K,
                     float* d_y, void* d_ws, size_t ws_bytes, void* stream);
 

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
 
 def good_config(**kw):
     base = dict(n_layers=2, d_model=256, n_heads=2, head_dim=128, ffn=1024, vocab=512, n_experts=0, top_k=0,
-                expert_ffn=0, batch=3, max_seq=64, dtype=_abi.DF_BF16, ln_eps=1e-5, variant=0, top_k_aux=0)
+                expert_ffn=0, batch=3, max_seq=64, dtype=_abi.DF_BF16, ln_eps=1e-5, variant=0, top_k_aux=0,
+                prefill_rows=0)
     base.update(kw)
     return _abi.df_config(*[base[f] for f, _ in _abi.df_config._fields_])
 
@@ -47,6 +48,13 @@ def fake_weights(p=0x10000, moe=False):
 def test_workspace_query():
     assert _abi.df_workspace_bytes(good_config()) > 0
     assert _abi.df_workspace_bytes(good_config(head_dim=48, d_model=96)) == 0
+    # prefill: one chunk of batch * min(max_seq, rows / batch) rows on top of the decode workspace
+    base = _abi.df_workspace_bytes(good_config())
+    for rows, tc in ((0, 64), (96, 32), (2, 1)):
+        extra = _abi.df_prefill_workspace_bytes(good_config(prefill_rows=rows)) - base
+        assert extra >= 3 * tc * (5 * 256 + 1024) * 4
+    assert _abi.df_prefill_workspace_bytes(good_config(dtype=_abi.DF_F32, batch=2)) == \
+        _abi.df_workspace_bytes(good_config(dtype=_abi.DF_F32, batch=2))            # one position at a time
     assert _abi.df_attention_workspace_bytes(32, 32, 4096, 128) > 0
     assert _abi.df_attention_workspace_bytes(32, 32, 4096, 100) == 0
 
@@ -61,6 +69,7 @@ def test_workspace_query():
     (dict(n_experts=16, top_k=17, expert_ffn=256), _abi.DF_ERR_SHAPE),
     (dict(n_experts=16, top_k=4, expert_ffn=256, dtype=_abi.DF_F32, d_model=256), _abi.DF_ERR_DTYPE),
     (dict(variant=8), _abi.DF_ERR_ARG),                                        # unknown switch
+    (dict(prefill_rows=-1), _abi.DF_ERR_ARG),
     (dict(variant=_abi.DF_VARIANT_AUX_OUTPUT | _abi.DF_VARIANT_ALPHA_HALF), _abi.DF_ERR_ARG),
     (dict(top_k_aux=2), _abi.DF_ERR_SHAPE),                                    # dense model
     (dict(n_experts=16, top_k=4, expert_ffn=256, top_k_aux=17), _abi.DF_ERR_SHAPE),
@@ -144,5 +153,5 @@ def test_pack_and_gemv_reject_bad_arguments():
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 4096, 4000) == 0  # K % 256
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 3, 4096, 4096) == 0   # odd rows
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 333, 4096, 2048) > 0  # tiled GEMM
-    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 333, 4096, 2000) == 0  # K % 64
+    assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 333, 4096, 2000) == 0  # K % 32
     assert _abi.df_stacked_gemv_workspace_bytes(_abi.DF_BF16, 32, 4096, 4096) > 0

@@ -63,7 +63,8 @@ CASES = [
     (2, 16, 256), (6, 48, 768), (16, 1024, 512), (32, 8192, 1024), (32, 4096, 4096), (32, 12288, 4096),
     (32, 4096, 16384), (32, 32000, 4096), (64, 2048, 1536), (128, 6144, 2048), (128, 64, 2048), (30, 1040, 2304),
     # tiled GEMM (prefill rows): ragged row and column tiles, one and many k steps
-    (129, 16, 64), (256, 256, 256), (1000, 1040, 512), (2048, 3072, 1024), (333, 4096, 2048),
+    (129, 16, 32), (256, 256, 256), (1000, 1040, 512), (2048, 3072, 1024), (333, 4096, 2048),
+    (4100, 2064, 2048),
 ]
 
 

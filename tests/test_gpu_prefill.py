@@ -30,9 +30,10 @@ pytestmark = pytest.mark.gpu
 # one chunk (Tc = max_seq): query blocks of 64 with a ragged tail
 ONE_CHUNK = Config("prefill_one_chunk", L=2, d=256, H=2, Dh=128, F=1024, V=512, B=3, ctx=70, S_max=400,
                    dtype="bf16", seed=31, sigma_w=0.05, sigma_ln=0.1, prompt_len=150)
-# 32 sequences: chunks of 2048 / 32 = 64 positions, the last one ragged
+# 32 sequences with 2048-row chunks: 64 positions per chunk, the last one ragged
 MULTI_CHUNK = Config("prefill_multi_chunk", L=2, d=256, H=2, Dh=128, F=512, V=256, B=32, ctx=40, S_max=256,
                      dtype="bf16", seed=32, sigma_w=0.05, sigma_ln=0.1, prompt_len=150)
+CHUNK_ROWS = {"prefill_multi_chunk": 2048}
 
 
 def _excess(got, want):
@@ -58,7 +59,7 @@ def _oracle_prefill(cfg, m, src, lens, prompt, perturb):
 def _run(cfg, lens, T):
     src = Inputs(cfg)
     prompt = src.prompt()[:, :T]
-    gm = DecodeModel(cfg, fill="host")
+    gm = DecodeModel(cfg, fill="host", prefill_rows=CHUNK_ROWS.get(cfg.name, 0))
     sentinel = 0x4242
     gm.k[:, :, :, cfg.ctx:] = sentinel
     gm.v[:, :, :, cfg.ctx:] = sentinel
@@ -142,7 +143,7 @@ def test_prefill_workspace_query():
     cfg = ONE_CHUNK
     gm = DecodeModel(cfg, fill="host")
     need = _abi.df_prefill_workspace_bytes(gm.config)
-    rows = cfg.B * min(cfg.S_max, 2048 // cfg.B)
+    rows = cfg.B * min(cfg.S_max, 16384 // cfg.B)
     assert need >= _abi.df_workspace_bytes(gm.config) + rows * (5 * cfg.d + cfg.F) * 4
     rc = _abi.df_prefill_primary(gm.config, gm.weights, gm.kv, gm.tokens(np.zeros((cfg.B, 2), np.int64)).data_ptr(),
                                  2, gm.ws.data_ptr(), need - 256, 0)
