@@ -114,146 +114,196 @@ __global__ __launch_bounds__(256) void prefill_kv_store(const float* qkv, int Tc
 }
 
 // Causal attention of a chunk's queries over the cache (positions 0 .. own
-// position): workgroup (64 queries, head h, sequence b), wave w takes 16
-// queries. Per block of 64 keys: S^T = K Q^T on the matrix cores (K from
-// LDS, Q as bf16 hi/lo parts in registers), online softmax per query in the
-// log2 domain, P (hi/lo parts through LDS) then O^T += V^T P^T with V
-// transposed into LDS. fp32 accumulation throughout; the output rows leave
-// as hi / lo fragment planes, the operand form of the next GEMM.
+// position): workgroup (128 queries, head h, sequence b), wave w takes 32
+// queries as two 16-query tiles. Per block of 64 keys, staged in LDS for
+// the four waves (the next block already in flight in registers):
+// S^T = K Q^T on the matrix cores (K rows from LDS, Q as bf16 hi/lo parts
+// in registers), online softmax per query in the log2 domain, then
+// O^T += V^T P^T. The order of the key reduction is free, so k-slot
+// 8 g + j of the product covers key 4 g + (j % 4) of the even (j < 4) or
+// odd (j >= 4) 16-key tile: the slots each lane holds after the score
+// product. P thus enters the matrix cores from registers (bf16 hi/lo
+// parts), and V^T is laid out in LDS in the same key order. Waves whose
+// queries all precede a key block skip it. fp32 accumulation; the output
+// rows leave as hi / lo fragment planes, the operand form of the next GEMM.
 constexpr int ADH = 128;
-constexpr int AKB = 64;                 // keys per block
-constexpr int KSP = ADH + 8;            // K row pitch in LDS
-constexpr int VSP = AKB + 8;            // V^T row pitch
-constexpr int PSP = AKB + 8;            // P row pitch
+constexpr int AKB = 64;          // keys per block
+constexpr int AQW = 32;          // queries per wave
+constexpr int AQG = 4 * AQW;     // queries per workgroup
+constexpr int KSP = ADH + 8;     // K row pitch in LDS (bf16)
+constexpr int VSP = AKB + 8;     // V^T row pitch
+
+// Column of key j (0..63 within a block) in the V^T rows: keys 4 g .. 4 g + 3
+// of 16-key tile 2 c + o sit at 32 c + 8 g + 4 o.
+__device__ __forceinline__ int vt_col(int j) {
+    const int c = j >> 5, o = (j >> 4) & 1, g = (j >> 2) & 3;
+    return c * 32 + g * 8 + o * 4 + (j & 3);
+}
 
 __global__ __launch_bounds__(256) void attn_prefill(const float* qkv, int Tc, int t0, const int32_t* len, int H,
                                                     int S_max, const bf16_t* kc, const bf16_t* vc, float scale_log2,
                                                     bf16_t* oh, bf16_t* ol) {
     __shared__ bf16_t Ks[AKB * KSP];
     __shared__ bf16_t Vt[ADH * VSP];
-    __shared__ bf16_t Ps[4][2][16 * PSP];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int d = H * ADH;
-    const int pos0 = len[b] + t0;                       // position of chunk row t = 0
-    const int t_q = qb * 64 + wv * 16 + li;             // this lane's query (column li)
-    const bool q_ok = t_q < Tc;
-    const int qpos = pos0 + min(t_q, Tc - 1);
-    const int last_key = min(pos0 + min(Tc, qb * 64 + 64) - 1, S_max - 1);
+    const int pos0 = len[b] + t0;                            // position of chunk row t = 0
+    const int tw0 = qb * AQG + wv * AQW;                     // first query (chunk row) of this wave
+    const int wave_last = tw0 < Tc ? pos0 + min(Tc - 1, tw0 + AQW - 1) : -1;
+    const int last_key = min(pos0 + min(Tc, qb * AQG + AQG) - 1, S_max - 1);
     const size_t head = ((size_t)b * H + h) * S_max * ADH;
 
     // the wave's queries as bf16 hi/lo B operands, scaled by log2(e)/sqrt(Dh)
-    bf16x8 qh[4], ql[4];
-    {
-        const float* qr = qkv + (size_t)(b * Tc + min(t_q, Tc - 1)) * 3 * d + h * ADH;
+    int t_q[2], qpos[2];
+    bf16x8 qh[2][4], ql[2][4];
+    #pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        t_q[qt] = tw0 + qt * 16 + li;
+        const int tq = min(t_q[qt], Tc - 1);
+        qpos[qt] = pos0 + tq;
+        const float* qr = qkv + (size_t)(b * Tc + tq) * 3 * d + h * ADH;
         #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const float4 a = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8);
             const float4 c = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8 + 4);
-            const float4 a2 = make_float4(a.x * scale_log2, a.y * scale_log2, a.z * scale_log2, a.w * scale_log2);
-            const float4 c2 = make_float4(c.x * scale_log2, c.y * scale_log2, c.z * scale_log2, c.w * scale_log2);
             uint2 h0, l0, h1, l1;
-            df::split_hi_lo(a2, h0, l0);
-            df::split_hi_lo(c2, h1, l1);
-            qh[ks] = __builtin_bit_cast(bf16x8, (u32x4){h0.x, h0.y, h1.x, h1.y});
-            ql[ks] = __builtin_bit_cast(bf16x8, (u32x4){l0.x, l0.y, l1.x, l1.y});
+            df::split_hi_lo(make_float4(a.x * scale_log2, a.y * scale_log2, a.z * scale_log2, a.w * scale_log2),
+                            h0, l0);
+            df::split_hi_lo(make_float4(c.x * scale_log2, c.y * scale_log2, c.z * scale_log2, c.w * scale_log2),
+                            h1, l1);
+            qh[qt][ks] = __builtin_bit_cast(bf16x8, (u32x4){h0.x, h0.y, h1.x, h1.y});
+            ql[qt][ks] = __builtin_bit_cast(bf16x8, (u32x4){l0.x, l0.y, l1.x, l1.y});
         }
     }
-    f32x4 oacc[8];
+    f32x4 oacc[2][8];
     #pragma unroll
-    for (int i = 0; i < 8; ++i) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float m = -1e30f, l = 0.f;
-    bf16_t* pw_h = Ps[wv][0];
-    bf16_t* pw_l = Ps[wv][1];
+    for (int qt = 0; qt < 2; ++qt)
+        #pragma unroll
+        for (int i = 0; i < 8; ++i) oacc[qt][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-1e30f, -1e30f}, l[2] = {0.f, 0.f};
 
-    for (int k0 = 0; k0 <= last_key; k0 += AKB) {
-        __syncthreads();
-        // K block [64][128] into LDS rows; V block transposed into [128][64]
+    // staging: K as 4 pieces of 8 dims per thread (rows of the block), V as
+    // 4 consecutive keys x 8 dims per thread (written transposed)
+    const int kc8 = tid & 15, kg = tid & 15, vc8 = tid >> 4;
+    u32x4 kr[4], vr[4];
+    auto fetch = [&](int k0) {
         #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int e = tid + j * 256;                // 1024 pieces of 8 elements
-            const int key = e >> 4, c8 = e & 15;
-            const int kk = min(k0 + key, last_key);
-            const u32x4 kv = *reinterpret_cast<const u32x4*>(kc + head + (size_t)kk * ADH + c8 * 8);
-            *reinterpret_cast<u32x4*>(&Ks[key * KSP + c8 * 8]) = kv;
-            const u32x4 vv = *reinterpret_cast<const u32x4*>(vc + head + (size_t)kk * ADH + c8 * 8);
-            #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                Vt[(c8 * 8 + 2 * q) * VSP + key] = (bf16_t)(vv[q] & 0xffffu);
-                Vt[(c8 * 8 + 2 * q + 1) * VSP + key] = (bf16_t)(vv[q] >> 16);
-            }
+            const int kk = min(k0 + ((tid + 256 * j) >> 4), last_key);
+            kr[j] = *reinterpret_cast<const u32x4*>(kc + head + (size_t)kk * ADH + kc8 * 8);
         }
-        __syncthreads();
-        // scores S^T[key][query] for 4 tiles of 16 keys
-        f32x4 s[4];
         #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            s[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+            const int kk = min(k0 + 4 * kg + i, last_key);
+            vr[i] = *reinterpret_cast<const u32x4*>(vc + head + (size_t)kk * ADH + vc8 * 8);
+        }
+    };
+    auto stash = [&]() {
+        #pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x4*>(&Ks[((tid + 256 * j) >> 4) * KSP + kc8 * 8]) = kr[j];
+        const int col = vt_col(4 * kg);
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1, sh = (e & 1) * 16;
+            const uint32_t x0 = (vr[0][w] >> sh) & 0xffffu, x1 = (vr[1][w] >> sh) & 0xffffu;
+            const uint32_t x2 = (vr[2][w] >> sh) & 0xffffu, x3 = (vr[3][w] >> sh) & 0xffffu;
+            *reinterpret_cast<uint2*>(&Vt[(vc8 * 8 + e) * VSP + col]) = make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
+        }
+    };
+
+    if (last_key >= 0) fetch(0);
+    for (int k0 = 0; k0 <= last_key; k0 += AKB) {
+        __syncthreads();                 // every wave is done with the previous block
+        stash();
+        __syncthreads();
+        fetch(min(k0 + AKB, last_key));  // next block (clamped: always a valid address)
+        if (k0 > wave_last) continue;    // all of this wave's queries precede the block
+        f32x4 s[2][4];
+        #pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
             #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int kt = 0; kt < 4; ++kt) s[qt][kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            #pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
                 const bf16x8 a = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(&Ks[(kt * 16 + li) * KSP + ks * 32 + lg * 8]));
-                s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], s[kt], 0, 0, 0);
-                s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], s[kt], 0, 0, 0);
+                #pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    s[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[qt][ks], s[qt][kt], 0, 0, 0);
+                    s[qt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[qt][ks], s[qt][kt], 0, 0, 0);
+                }
             }
-        }
-        // causal mask and the block maximum of this lane's query
-        float mb = -INFINITY;
+        const bool diag = k0 + AKB - 1 > pos0 + tw0;   // a key of the block may follow a query of the wave
+        bf16x8 ph[2][2], pl[2][2];
         #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int qt = 0; qt < 2; ++qt) {
+            float mb = -INFINITY;
             #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = k0 + kt * 16 + 4 * lg + rr;
-                if (key > qpos) s[kt][rr] = -INFINITY;
-                mb = fmaxf(mb, s[kt][rr]);
+            for (int kt = 0; kt < 4; ++kt)
+                #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (diag && k0 + kt * 16 + 4 * lg + r > qpos[qt]) s[qt][kt][r] = -INFINITY;
+                    mb = fmaxf(mb, s[qt][kt][r]);
+                }
+            mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+            mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+            const float mn = fmaxf(m[qt], mb);
+            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+            m[qt] = mn;
+            l[qt] *= alpha;
+            #pragma unroll
+            for (int i = 0; i < 8; ++i) oacc[qt][i] *= alpha;
+            #pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2) {
+                const f32x4 sa = s[qt][2 * g2], sb = s[qt][2 * g2 + 1];
+                const float4 pa = make_float4(__builtin_amdgcn_exp2f(sa[0] - mn), __builtin_amdgcn_exp2f(sa[1] - mn),
+                                              __builtin_amdgcn_exp2f(sa[2] - mn), __builtin_amdgcn_exp2f(sa[3] - mn));
+                const float4 pb = make_float4(__builtin_amdgcn_exp2f(sb[0] - mn), __builtin_amdgcn_exp2f(sb[1] - mn),
+                                              __builtin_amdgcn_exp2f(sb[2] - mn), __builtin_amdgcn_exp2f(sb[3] - mn));
+                l[qt] += (pa.x + pa.y + pa.z + pa.w) + (pb.x + pb.y + pb.z + pb.w);
+                uint2 ha, la, hb, lb;
+                df::split_hi_lo(pa, ha, la);
+                df::split_hi_lo(pb, hb, lb);
+                ph[qt][g2] = __builtin_bit_cast(bf16x8, (u32x4){ha.x, ha.y, hb.x, hb.y});
+                pl[qt][g2] = __builtin_bit_cast(bf16x8, (u32x4){la.x, la.y, lb.x, lb.y});
             }
-        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float mn = fmaxf(m, mb);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        l *= alpha;
-        #pragma unroll
-        for (int i = 0; i < 8; ++i) oacc[i] *= alpha;
-        // P = exp2(s - m) as bf16 hi/lo, row li (query), columns = keys
-        #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const float4 pv = make_float4(__builtin_amdgcn_exp2f(s[kt][0] - mn), __builtin_amdgcn_exp2f(s[kt][1] - mn),
-                                          __builtin_amdgcn_exp2f(s[kt][2] - mn), __builtin_amdgcn_exp2f(s[kt][3] - mn));
-            l += pv.x + pv.y + pv.z + pv.w;
-            uint2 ph, pl;
-            df::split_hi_lo(pv, ph, pl);
-            *reinterpret_cast<uint2*>(&pw_h[li * PSP + kt * 16 + 4 * lg]) = ph;
-            *reinterpret_cast<uint2*>(&pw_l[li * PSP + kt * 16 + 4 * lg]) = pl;
         }
-        // O^T[dim][query] += V^T[dim][key] P^T[key][query] over 2 groups of 32 keys
         #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) {
-            const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw_h[li * PSP + g2 * 32 + 8 * lg]));
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&pw_l[li * PSP + g2 * 32 + 8 * lg]));
+        for (int g2 = 0; g2 < 2; ++g2)
             #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const bf16x8 a = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(&Vt[(dt * 16 + li) * VSP + g2 * 32 + 8 * lg]));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[dt], 0, 0, 0);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[dt], 0, 0, 0);
+                #pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[qt][g2], oacc[qt][dt], 0, 0, 0);
+                    oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[qt][g2], oacc[qt][dt], 0, 0, 0);
+                }
             }
-        }
     }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (!q_ok) return;
-    const float inv = 1.0f / l;
-    const int row = b * Tc + t_q;
     #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const float4 v = make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
-        uint2 hv, lv;
-        df::split_hi_lo(v, hv, lv);
-        const size_t o = frag_off(row, h * ADH + dt * 16 + 4 * lg, d);
-        *reinterpret_cast<uint2*>(oh + o) = hv;
-        *reinterpret_cast<uint2*>(ol + o) = lv;
+    for (int qt = 0; qt < 2; ++qt) {
+        float lt = l[qt];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (t_q[qt] >= Tc) continue;
+        const float inv = 1.0f / lt;
+        const int row = b * Tc + t_q[qt];
+        #pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const float4 v = make_float4(oacc[qt][dt][0] * inv, oacc[qt][dt][1] * inv, oacc[qt][dt][2] * inv,
+                                         oacc[qt][dt][3] * inv);
+            uint2 hv, lv;
+            df::split_hi_lo(v, hv, lv);
+            const size_t o = frag_off(row, h * ADH + dt * 16 + 4 * lg, d);
+            *reinterpret_cast<uint2*>(oh + o) = hv;
+            *reinterpret_cast<uint2*>(ol + o) = lv;
+        }
     }
 }
 
@@ -289,7 +339,7 @@ hipError_t prefill_attention(const float* qkv, int B, int Tc, int t0, const int3
                              const void* kc, const void* vc, void* oh, void* ol, hipStream_t s) {
     if (Dh != ADH) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(attn_prefill, dim3((Tc + 63) / 64, H, B), dim3(256), 0, s, qkv, Tc, t0, len, H, S_max,
+    hipLaunchKernelGGL(attn_prefill, dim3((Tc + AQG - 1) / AQG, H, B), dim3(256), 0, s, qkv, Tc, t0, len, H, S_max,
                        reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
                        df::kLog2e / sqrtf((float)Dh), reinterpret_cast<bf16_t*>(oh), reinterpret_cast<bf16_t*>(ol));
     return hipGetLastError();
