@@ -13,10 +13,11 @@
 // Workgroup tile: 256 weight rows x 256 activation rows, 8 waves in a 2 x 4
 // grid of 128 x 64 each (8 x 4 v_mfma_f32_16x16x32_bf16 tiles, both
 // activation parts into one fp32 accumulator). Per 32-wide k block the
-// workgroup stages 48 fragments (16 of W, 16 + 16 of X) through LDS, double
-// buffered: the next block's fragments are in flight in registers while the
-// matrix cores work on the current one. Epilogues: fp32 store, residual add,
-// or GELU written back as hi/lo fragment planes for the next GEMM.
+// workgroup stages 48 fragments (16 of W, 16 + 16 of X) in LDS with
+// direct global-to-LDS loads (each wave-wide load lands as one 1 KiB piece),
+// three stages deep: blocks kb + 1 and kb + 2 are in flight while the matrix
+// cores work on block kb. Epilogues: fp32 store, residual add, or GELU
+// written back as hi/lo fragment planes for the next GEMM.
 #include "df_device.h"
 #include "df_internal.h"
 #include "mfma_tile.h"
@@ -36,7 +37,11 @@ constexpr int NTHREADS = 64 * NWAVE;
 constexpr int PIECES = 3 * TT16;          // fragments staged per k block (W, X hi, X lo)
 constexpr int PPW = PIECES / NWAVE;       // fragments per wave (6)
 constexpr int FRAG = 512;                 // bf16 elements per fragment (1 KiB)
-constexpr size_t kGemmLds = (size_t)2 * PIECES * FRAG * sizeof(bf16_t);   // 96 KiB
+constexpr int NSTAGE = 3;
+constexpr size_t kGemmLds = (size_t)NSTAGE * PIECES * FRAG * sizeof(bf16_t);   // 144 KiB
+
+// s_waitcnt with vmcnt <= n (n < 16), expcnt and lgkmcnt unconstrained.
+#define GEMM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
 struct GemmParams {
     const bf16_t* xh;   // [R16][K] fragment layout, R16 = ceil(R / 16) * 16
@@ -80,13 +85,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
         else { base = p.xl; t16 = min(r0 + q - 2 * TT16, RT16 - 1); }
         src[j] = base + ((size_t)t16 * KB * 64 + lane) * 8;
     }
-    auto fetch = [&](int kb, u32x4 (&v)[PPW]) {
+    // block kb of this wave's pieces -> stage st (global_load_lds: lane i of
+    // the wave lands at byte 16 i of the piece)
+    auto issue = [&](int kb, int st) {
         #pragma unroll
-        for (int j = 0; j < PPW; ++j) v[j] = *reinterpret_cast<const u32x4*>(src[j] + (size_t)kb * FRAG);
-    };
-    auto stash = [&](int st, const u32x4 (&v)[PPW]) {
-        #pragma unroll
-        for (int j = 0; j < PPW; ++j) lds[((size_t)st * PIECES + wv * PPW + j) * 64 + lane] = v[j];
+        for (int j = 0; j < PPW; ++j)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src[j] + (size_t)kb * FRAG),
+                (__attribute__((address_space(3))) void*)(lds + ((size_t)st * PIECES + wv * PPW + j) * 64), 16, 0,
+                0);
     };
 
     f32x4 acc[8][4];
@@ -95,13 +102,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
         #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    u32x4 pre[PPW];
-    fetch(0, pre);
-    stash(0, pre);
-    __syncthreads();
+    issue(0, 0);
+    issue(min(1, KB - 1), 1);
+    int st = 0;
     for (int kb = 0; kb < KB; ++kb) {
-        const int st = kb & 1;
-        fetch(min(kb + 1, KB - 1), pre);          // unconditional: keeps the waits exact
+        GEMM_WAIT_VM(PPW);       // this wave's pieces of block kb have landed (kb + 1 may be in flight)
+        // ... and every other wave's; all are done with block kb - 1. A bare
+        // barrier: the waits above are exact, where a fenced one would drain
+        // the loads still in flight for block kb + 1.
+        asm volatile("s_barrier" ::: "memory");
+        issue(min(kb + 2, KB - 1), st == 0 ? 2 : st - 1);   // stage of block kb - 1 (clamped: always PPW loads)
         const u32x4* S = lds + (size_t)st * PIECES * 64;
         bf16x8 bh[4], bl[4];
         #pragma unroll
@@ -118,9 +128,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
                 acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[mt], acc[nt][mt], 0, 0, 0);
             }
         }
-        stash(st ^ 1, pre);    // the other stage: every wave left it at the last barrier
-        __syncthreads();
+        st = st == 2 ? 0 : st + 1;
     }
+    GEMM_WAIT_VM(0);             // no load still landing when the wave leaves
 
     // lane holds D[n = 4 lg + i][r = li] of each 16 x 16 tile
     const int li = lane & 15, lg = lane >> 4;
