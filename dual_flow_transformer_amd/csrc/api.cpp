@@ -84,11 +84,12 @@ int prefill_chunk(const df_config& c) {
     return std::max(1, std::min(c.max_seq, rows / c.batch));
 }
 
-// Chunk buffers: fp32 residual rows h and Q/K/V rows; the GEMM operands
-// (normed rows / attention output, FFN hidden rows) as bf16 hi and lo planes
-// in the fragment layout, rows padded to a multiple of 16.
+// Chunk buffers: fp32 residual rows h and Q rows (K and V go straight to
+// the cache); the GEMM operands (normed rows / attention output, FFN hidden
+// rows) as bf16 hi and lo planes in the fragment layout, rows padded to a
+// multiple of 16.
 struct PrefillLayout {
-    size_t h, xh, xl, qkv, fh, fl, total;   // byte offsets from the workspace base
+    size_t h, xh, xl, q, fh, fl, total;   // byte offsets from the workspace base
 };
 PrefillLayout prefill_layout(const df_config& c) {
     PrefillLayout P{};
@@ -98,7 +99,7 @@ PrefillLayout prefill_layout(const df_config& c) {
     P.h = take(R * c.d_model * 4);
     P.xh = take(R16 * c.d_model * 2);
     P.xl = take(R16 * c.d_model * 2);
-    P.qkv = take(R * 3 * c.d_model * 4);
+    P.q = take(R * c.d_model * 4);
     P.fh = take(R16 * (size_t)c.ffn * 2);
     P.fl = take(R16 * (size_t)c.ffn * 2);
     P.total = o;
@@ -387,7 +388,7 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
     const PrefillLayout P = prefill_layout(c);
     int32_t* status = reinterpret_cast<int32_t*>(ws + layout(c).status);
     float* h = reinterpret_cast<float*>(ws + P.h);
-    float* qkv = reinterpret_cast<float*>(ws + P.qkv);
+    float* q = reinterpret_cast<float*>(ws + P.q);
     void* xh = ws + P.xh;
     void* xl = ws + P.xl;
     void* fh = ws + P.fh;
@@ -405,8 +406,9 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
         if (e == hipSuccess && e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorUnknown;
         return e;
     };
-    auto gemm = [&](const void* ah, const void* al, const char* wt, int R, int N, int K, int epi, float* y) {
-        return timed(1, [&] { return dfk::gemm(ah, al, wt, R, N, K, epi, y, fh, fl, s); });
+    auto gemm = [&](const void* ah, const void* al, const char* wt, int R, int N, int K, int epi, float* y,
+                    const dfk::QkvStore* st = nullptr) {
+        return timed(1, [&] { return dfk::gemm(ah, al, wt, R, N, K, epi, y, fh, fl, s, st); });
     };
     for (int t0 = 0; t0 < T; t0 += Tmax) {
         const int Tc = std::min(Tmax, T - t0), R = B * Tc;
@@ -420,11 +422,12 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
             const char* wo = reinterpret_cast<const char*>(w->w_o) + (size_t)l * d * d * es;
             const char* wup = reinterpret_cast<const char*>(w->w_up) + (size_t)l * F * d * es;
             const char* wdn = reinterpret_cast<const char*>(w->w_down) + (size_t)l * d * F * es;
+            const dfk::QkvStore st{reinterpret_cast<uint16_t*>(kc), reinterpret_cast<uint16_t*>(vc), kv->len, Tc,
+                                   t0, H, Dh, c.max_seq, status};
             if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R, d, xh, xl, s)) ||
-                !ok(gemm(xh, xl, wqkv, R, 3 * d, d, dfk::GEMM_STORE, qkv)) ||
-                !ok(dfk::prefill_kv(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, status, s)) ||
+                !ok(gemm(xh, xl, wqkv, R, 3 * d, d, dfk::GEMM_QKV, q, &st)) ||
                 !ok(timed(2, [&] {
-                    return dfk::prefill_attention(qkv, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s);
+                    return dfk::prefill_attention(q, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s);
                 })) ||
                 !ok(gemm(xh, xl, wo, R, d, d, dfk::GEMM_RESID, h)) ||
                 !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R, d, xh, xl, s)) ||

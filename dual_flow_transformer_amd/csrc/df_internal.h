@@ -123,9 +123,20 @@ enum GemmEpi {
     GEMM_STORE = 0,        // y = x w^T (fp32 [R][N])
     GEMM_GELU_SPLIT = 1,   // GELU(x w^T) as hi / lo fragment planes yh, yl [R16][N] (N % 32 == 0)
     GEMM_RESID = 2,        // y += x w^T (y: fp32 residual rows [R][N])
+    GEMM_QKV = 3,          // N = 3 d: Q columns to y [R][d] (fp32), K / V columns into the bf16 cache
+};
+// Where GEMM_QKV puts K and V: row r = b * Tc + t goes to position
+// len[b] + t0 + t of sequence b; positions outside [0, S_max) are skipped
+// and flagged (status bit 0).
+struct QkvStore {
+    uint16_t* kc;         // bf16 [B][H][S_max][Dh], one layer
+    uint16_t* vc;
+    const int32_t* len;
+    int Tc, t0, H, Dh, S_max;
+    int32_t* status;
 };
 hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
-                void* yl, hipStream_t s);
+                void* yl, hipStream_t s, const QkvStore* kv = nullptr);
 // fp32 rows [R][K] -> hi / lo fragment planes (K % 32 == 0).
 hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStream_t s);
 
@@ -140,13 +151,10 @@ hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_
 // LayerNorm(h[r]) * g as hi / lo fragment planes xh, xl [R16][d]; d <= 4096, d % 32 == 0.
 hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, void* xh, void* xl,
                               hipStream_t s);
-// K/V columns of qkv rows [R][3 d] to the bf16 cache.
-hipError_t prefill_kv(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
-                      void* kc, void* vc, int32_t* status, hipStream_t s);
-// Causal attention of the chunk queries (Q columns of qkv) over the bf16
+// Causal attention of the chunk queries q [R][H * Dh] (fp32) over the bf16
 // cache: row r, head h = softmax over keys 0 .. len[b] + t0 + t, written as
 // hi / lo fragment planes oh, ol [R16][H * Dh]. Dh == 128.
-hipError_t prefill_attention(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
+hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
                              const void* kc, const void* vc, void* oh, void* ol, hipStream_t s);
 
 // ---------------------------------------------------------------------------

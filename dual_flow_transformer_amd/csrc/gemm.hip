@@ -16,8 +16,9 @@
 // workgroup stages 48 fragments (16 of W, 16 + 16 of X) in LDS with
 // direct global-to-LDS loads (each wave-wide load lands as one 1 KiB piece),
 // three stages deep: blocks kb + 1 and kb + 2 are in flight while the matrix
-// cores work on block kb. Epilogues: fp32 store, residual add, or GELU
-// written back as hi/lo fragment planes for the next GEMM.
+// cores work on block kb. Epilogues: fp32 store, residual add, GELU written
+// back as hi/lo fragment planes for the next GEMM, or the Q/K/V split (Q
+// rows fp32, K and V rounded to bf16 straight into the cache).
 #include "df_device.h"
 #include "df_internal.h"
 #include "mfma_tile.h"
@@ -48,10 +49,12 @@ struct GemmParams {
     const bf16_t* xl;
     const bf16_t* w;    // [N][K] fragment layout
     int R, N, K;
-    int epi;            // GEMM_STORE / GEMM_RESID: y fp32 [R][N]; GEMM_GELU_SPLIT: yh / yl planes [R16][N]
+    int epi;            // GEMM_STORE / GEMM_RESID: y fp32 [R][N]; GEMM_GELU_SPLIT: yh / yl planes [R16][N];
+                        // GEMM_QKV: y fp32 Q rows [R][N/3], K/V to the cache
     float* y;
     bf16_t* yh;
     bf16_t* yl;
+    QkvStore kv;
 };
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
@@ -142,7 +145,25 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
             const int r = (r0 + wr * 4 + mt) * 16 + li;
             if (r >= p.R || n >= p.N) continue;
             float4 v = make_float4(acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
-            if (p.epi == GEMM_GELU_SPLIT) {
+            if (p.epi == GEMM_QKV) {
+                const int d = p.N / 3;
+                if (n < d) {
+                    *reinterpret_cast<float4*>(p.y + (size_t)r * d + n) = v;
+                    continue;
+                }
+                // K / V columns: rounded to bf16 into the cache of sequence
+                // b = r / Tc at position len[b] + t0 + r % Tc
+                const QkvStore& q = p.kv;
+                const int b = r / q.Tc, pos = q.len[b] + q.t0 + (r - b * q.Tc);
+                if (pos < 0 || pos >= q.S_max) {
+                    if (q.status) q.status[0] |= 1;
+                    continue;
+                }
+                const int j = n - d - (n >= 2 * d ? d : 0), hh = j / q.Dh, e = j - hh * q.Dh;
+                bf16_t* cache = n >= 2 * d ? q.vc : q.kc;
+                *reinterpret_cast<uint2*>(cache + (((size_t)b * q.H + hh) * q.S_max + pos) * q.Dh + e) =
+                    make_uint2(df::pack_bf16x2(v.x, v.y), df::pack_bf16x2(v.z, v.w));
+            } else if (p.epi == GEMM_GELU_SPLIT) {
                 v.x = gelu(v.x); v.y = gelu(v.y); v.z = gelu(v.z); v.w = gelu(v.w);
                 uint2 hv, lv;
                 df::split_hi_lo(v, hv, lv);
@@ -181,12 +202,14 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float* x, int R, 
 }  // namespace
 
 hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
-                void* yl, hipStream_t s) {
+                void* yl, hipStream_t s, const QkvStore* kv) {
     if (R < 1 || N < 16 || N % 16 || K < 32 || K % 32) return hipErrorInvalidValue;
     if (epi == GEMM_GELU_SPLIT ? (!yh || !yl || N % 32) : !y) return hipErrorInvalidValue;
+    if (epi == GEMM_QKV && (!kv || N % 3 || (N / 3) % 16 || kv->Dh % 4 || kv->Tc < 1 || R % kv->Tc))
+        return hipErrorInvalidValue;
     GemmParams p{reinterpret_cast<const bf16_t*>(xh), reinterpret_cast<const bf16_t*>(xl),
                  reinterpret_cast<const bf16_t*>(w), R, N, K, epi, y, reinterpret_cast<bf16_t*>(yh),
-                 reinterpret_cast<bf16_t*>(yl)};
+                 reinterpret_cast<bf16_t*>(yl), kv ? *kv : QkvStore{}};
     hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&gemm_bf16), kGemmLds);
     if (e != hipSuccess) return e;
     (void)hipGetLastError();

@@ -39,31 +39,35 @@ __device__ __forceinline__ size_t frag_off(int r, int k, int K) {
     return ((size_t)((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
 }
 
-// LN(h[r]; g) for R rows of width d as hi / lo fragment planes: one block
-// per row, each thread up to two runs of eight columns held in registers.
-__global__ __launch_bounds__(256) void prefill_ln(const float* h, const float* g, float eps, int d, bf16_t* xh,
-                                                  bf16_t* xl) {
-    __shared__ float red[16];
-    const int r = blockIdx.x;
+// LN(h[r]; g) for R rows of width d as hi / lo fragment planes: one wave
+// per row (four rows per block), each lane up to eight runs of eight
+// columns held in registers, wave-level reductions only.
+constexpr int LN_RUNS = 8;   // d <= 64 lanes * 8 runs * 8 columns
+__global__ __launch_bounds__(256) void prefill_ln(const float* h, const float* g, float eps, int R, int d,
+                                                  bf16_t* xh, bf16_t* xl) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R) return;
     const float* hr = h + (size_t)r * d;
-    float4 v[2][2];
+    const int nrun = d >> 3;
+    float4 v[LN_RUNS][2];
     float s = 0.f;
     #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int k = 8 * (threadIdx.x + 256 * e);
-        if (k < d) {
-            v[e][0] = *reinterpret_cast<const float4*>(hr + k);
-            v[e][1] = *reinterpret_cast<const float4*>(hr + k + 4);
+    for (int e = 0; e < LN_RUNS; ++e) {
+        const int c = lane + 64 * e;
+        if (c < nrun) {
+            v[e][0] = *reinterpret_cast<const float4*>(hr + 8 * c);
+            v[e][1] = *reinterpret_cast<const float4*>(hr + 8 * c + 4);
         } else {
             v[e][0] = v[e][1] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         s += (v[e][0].x + v[e][0].y + v[e][0].z + v[e][0].w) + (v[e][1].x + v[e][1].y + v[e][1].z + v[e][1].w);
     }
-    const float mean = df::block_sum(s, red) / (float)d;
+    const float mean = df::wave_sum(s) / (float)d;
     float q = 0.f;
     #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        if (8 * (threadIdx.x + 256 * e) >= d) continue;
+    for (int e = 0; e < LN_RUNS; ++e) {
+        if (lane + 64 * e >= nrun) continue;
         #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const float4 t = v[e][u];
@@ -73,11 +77,12 @@ __global__ __launch_bounds__(256) void prefill_ln(const float* h, const float* g
             q = fmaf(t.w - mean, t.w - mean, q);
         }
     }
-    const float rstd = 1.0f / sqrtf(df::block_sum(q, red) / (float)d + eps);
+    const float rstd = 1.0f / sqrtf(df::wave_sum(q) / (float)d + eps);
     #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int k = 8 * (threadIdx.x + 256 * e);
-        if (k >= d) continue;
+    for (int e = 0; e < LN_RUNS; ++e) {
+        const int c = lane + 64 * e;
+        if (c >= nrun) continue;
+        const int k = 8 * c;
         const float4 g0 = *reinterpret_cast<const float4*>(g + k);
         const float4 g1 = *reinterpret_cast<const float4*>(g + k + 4);
         const float4 a = make_float4((v[e][0].x - mean) * rstd * g0.x, (v[e][0].y - mean) * rstd * g0.y,
@@ -90,26 +95,6 @@ __global__ __launch_bounds__(256) void prefill_ln(const float* h, const float* g
         const size_t o = frag_off(r, k, d);
         *reinterpret_cast<u32x4*>(xh + o) = (u32x4){h0.x, h0.y, h1.x, h1.y};
         *reinterpret_cast<u32x4*>(xl + o) = (u32x4){l0.x, l0.y, l1.x, l1.y};
-    }
-}
-
-// K/V columns of the QKV rows to the cache at position len[b] + t0 + t,
-// rounded to bf16; positions at or past S_max are skipped and flagged.
-__global__ __launch_bounds__(256) void prefill_kv_store(const float* qkv, int Tc, int t0, const int32_t* len,
-                                                        int H, int Dh, int S_max, bf16_t* kc, bf16_t* vc,
-                                                        int32_t* status) {
-    const int r = blockIdx.x, b = r / Tc, t = r - b * Tc;
-    const int d = H * Dh;
-    const int pos = len[b] + t0 + t;
-    if (pos < 0 || pos >= S_max) {
-        if (status && threadIdx.x == 0) status[0] |= 1;
-        return;
-    }
-    const float* row = qkv + (size_t)r * 3 * d;
-    for (int i = threadIdx.x; i < 2 * d; i += blockDim.x) {
-        const int kv = i / d, j = i - kv * d, hh = j / Dh, e = j - hh * Dh;
-        bf16_t* cache = kv == 0 ? kc : vc;
-        cache[(((size_t)b * H + hh) * S_max + pos) * Dh + e] = df::f32_to_bf16(row[d + i]);
     }
 }
 
@@ -140,7 +125,7 @@ __device__ __forceinline__ int vt_col(int j) {
     return c * 32 + g * 8 + o * 4 + (j & 3);
 }
 
-__global__ __launch_bounds__(256) void attn_prefill(const float* qkv, int Tc, int t0, const int32_t* len, int H,
+__global__ __launch_bounds__(256) void attn_prefill(const float* q, int Tc, int t0, const int32_t* len, int H,
                                                     int S_max, const bf16_t* kc, const bf16_t* vc, float scale_log2,
                                                     bf16_t* oh, bf16_t* ol) {
     __shared__ bf16_t Ks[AKB * KSP];
@@ -163,7 +148,7 @@ __global__ __launch_bounds__(256) void attn_prefill(const float* qkv, int Tc, in
         t_q[qt] = tw0 + qt * 16 + li;
         const int tq = min(t_q[qt], Tc - 1);
         qpos[qt] = pos0 + tq;
-        const float* qr = qkv + (size_t)(b * Tc + tq) * 3 * d + h * ADH;
+        const float* qr = q + (size_t)(b * Tc + tq) * d + h * ADH;
         #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const float4 a = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8);
@@ -320,26 +305,18 @@ hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_
 
 hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, void* xh, void* xl,
                               hipStream_t s) {
-    if (d > 16 * 256 || d % 32) return hipErrorInvalidValue;
+    if (d > 64 * LN_RUNS * 8 || d % 32) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(prefill_ln, dim3(R), dim3(256), 0, s, h, g, eps, d, reinterpret_cast<bf16_t*>(xh),
-                       reinterpret_cast<bf16_t*>(xl));
+    hipLaunchKernelGGL(prefill_ln, dim3((R + 3) / 4), dim3(256), 0, s, h, g, eps, R, d,
+                       reinterpret_cast<bf16_t*>(xh), reinterpret_cast<bf16_t*>(xl));
     return hipGetLastError();
 }
 
-hipError_t prefill_kv(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
-                      void* kc, void* vc, int32_t* status, hipStream_t s) {
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(prefill_kv_store, dim3(B * Tc), dim3(256), 0, s, qkv, Tc, t0, len, H, Dh, S_max,
-                       reinterpret_cast<bf16_t*>(kc), reinterpret_cast<bf16_t*>(vc), status);
-    return hipGetLastError();
-}
-
-hipError_t prefill_attention(const float* qkv, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
+hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
                              const void* kc, const void* vc, void* oh, void* ol, hipStream_t s) {
     if (Dh != ADH) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(attn_prefill, dim3((Tc + AQG - 1) / AQG, H, B), dim3(256), 0, s, qkv, Tc, t0, len, H, S_max,
+    hipLaunchKernelGGL(attn_prefill, dim3((Tc + AQG - 1) / AQG, H, B), dim3(256), 0, s, q, Tc, t0, len, H, S_max,
                        reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
                        df::kLog2e / sqrtf((float)Dh), reinterpret_cast<bf16_t*>(oh), reinterpret_cast<bf16_t*>(ol));
     return hipGetLastError();

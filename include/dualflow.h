@@ -169,7 +169,7 @@ int df_decode_step(const df_config* cfg, const df_weights* w, const df_kv* kv,
 
 /* Bytes of workspace df_prefill_primary needs (>= df_workspace_bytes):
  * dense bf16 models with head_dim 128 add room for one chunk of R prompt
- * rows, about R * (5 d + ffn) * 4 bytes (fp32 residual and Q/K/V rows, the
+ * rows, about R * (3 d + ffn) * 4 bytes (fp32 residual and query rows, the
  * GEMM operands as bf16 hi/lo planes). 0 when the config is invalid. */
 size_t df_prefill_workspace_bytes(const df_config* cfg);
 

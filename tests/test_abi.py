@@ -52,7 +52,7 @@ def test_workspace_query():
     base = _abi.df_workspace_bytes(good_config())
     for rows, tc in ((0, 64), (96, 32), (2, 1)):
         extra = _abi.df_prefill_workspace_bytes(good_config(prefill_rows=rows)) - base
-        assert extra >= 3 * tc * (5 * 256 + 1024) * 4
+        assert extra >= 3 * tc * (3 * 256 + 1024) * 4
     assert _abi.df_prefill_workspace_bytes(good_config(dtype=_abi.DF_F32, batch=2)) == \
         _abi.df_workspace_bytes(good_config(dtype=_abi.DF_F32, batch=2))            # one position at a time
     assert _abi.df_attention_workspace_bytes(32, 32, 4096, 128) > 0

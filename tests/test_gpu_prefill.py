@@ -144,7 +144,7 @@ def test_prefill_workspace_query():
     gm = DecodeModel(cfg, fill="host")
     need = _abi.df_prefill_workspace_bytes(gm.config)
     rows = cfg.B * min(cfg.S_max, 16384 // cfg.B)
-    assert need >= _abi.df_workspace_bytes(gm.config) + rows * (5 * cfg.d + cfg.F) * 4
+    assert need >= _abi.df_workspace_bytes(gm.config) + rows * (3 * cfg.d + cfg.F) * 4
     rc = _abi.df_prefill_primary(gm.config, gm.weights, gm.kv, gm.tokens(np.zeros((cfg.B, 2), np.int64)).data_ptr(),
                                  2, gm.ws.data_ptr(), need - 256, 0)
     assert rc == _abi.DF_ERR_WORKSPACE
