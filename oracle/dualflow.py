@@ -1,4 +1,5 @@
-"""Float64 CPU oracle of the Dual-Flow Transformer grouped decode step.
+"""Float64 CPU oracle of the Dual-Flow Transformer grouped decode step, the
+primary prefill and the full-sequence dual forward.
 
 TEST INFRASTRUCTURE: only tests, the smoke check and the benchmark's CPU
 baseline may use this module. It is deliberately plain: one row at a time,
@@ -609,6 +610,106 @@ def prefill_primary(model: Model, cache: Cache, prompt: np.ndarray):
         out[i] = layer_norm(h, model.lnf(), c.eps) @ model.w_out().T
     cache.lens = cache.lens + T
     return out
+
+
+# --------------------------------------------------------------------------
+# Full-sequence dual forward (both flows at every position)
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class ForwardResult:
+    logits: np.ndarray                    # [nb, T, 2, V]
+    p_mix: np.ndarray                     # [nb, T, V]
+    alpha: np.ndarray                     # [nb, T]
+    next_tok: np.ndarray                  # [nb, T]
+
+
+def forward_dual(model: Model, cache: Cache, tokens: np.ndarray) -> ForwardResult:
+    """Both flows over a whole token sequence, as in training, where both
+    flows are evaluated along the full sequence ([ES] Costes de Inferencia
+    vs. Entrenamiento, training). tokens: [nb, T], sequence i at positions
+    lens[i] .. lens[i] + T - 1. Written per sequence in matrix form over
+    the T positions: the primary flow is the causal Transformer of the
+    prefill; the aux flow at position t forms its query from its own
+    normed row, Q2 = Q2raw + a * Q1, and attends the primary K1/V1 of
+    positions 0 .. t (shared K/V, causal); b_l and c_l couple the MLP rows
+    position by position; every position gets both flows' logits and the
+    mixture output ([ES] Arquitectura Central, Mecanismos Clave). The cache
+    receives rho(K1), rho(V1) of every position and lens advances by T.
+    Reading: the aux state at position t depends on positions <= t only
+    through the primary K/V, so the result is the one of T teacher-forced
+    dual steps. MoE layers route each position on its own (router replay
+    per row)."""
+    c = model.cfg
+    dt = c.dtype
+    couple = not (c.variant & 1)
+    mode = mix_mode(c.variant)
+    tokens = np.asarray(tokens)
+    nb, T = tokens.shape
+    if np.any(cache.lens + T > c.S_max):
+        raise ValueError("cache full")
+    d = c.d
+    h_all = np.zeros((nb, 2, T, d))
+    for i in range(nb):
+        pos = np.arange(int(cache.lens[i]), int(cache.lens[i]) + T)
+        for f in range(2):
+            h_all[i, f] = model.emb(f, tokens[i]) + model.pos(pos)
+    g_prev = None
+    for l in range(c.L):
+        p = model.layer(l)
+        K, V = cache.layer(l)
+        g_in = p["ln1"] if g_prev is None else g_prev
+        for i in range(nb):
+            p0 = int(cache.lens[i])
+            h = h_all[i]
+            u = [layer_norm(h[f], g_in, c.eps) for f in range(2)]
+            qkv1 = u[0] @ p["w_qkv"].T
+            q1 = qkv1[:, :d]
+            q2 = u[1] @ p["w_qkv"][:d].T
+            if couple:
+                q2 = q2 + p["a"][None, :] * q1
+            K[i, :, p0:p0 + T] = round_to(qkv1[:, d:2 * d], dt).reshape(T, c.H, c.Dh).transpose(1, 0, 2)
+            V[i, :, p0:p0 + T] = round_to(qkv1[:, 2 * d:], dt).reshape(T, c.H, c.Dh).transpose(1, 0, 2)
+            for t in range(T):
+                cache.appended[(l, cache.seqs[i], p0 + t)] = (K[i, :, p0 + t].copy(), V[i, :, p0 + t].copy())
+            for f, qf in enumerate((q1, q2)):
+                o = np.zeros((T, d))
+                for t in range(T):
+                    n = p0 + t + 1
+                    for hh in range(c.H):
+                        sl = slice(hh * c.Dh, (hh + 1) * c.Dh)
+                        o[t, sl], _ = attention_one(qf[t, sl], K[i, hh, :n], V[i, hh, :n])
+                h[f] = h[f] + o @ p["w_o"].T
+            v = np.stack([layer_norm(h[f], p["ln2"], c.eps) for f in range(2)])   # [2, T, d]
+            if c.moe:
+                for t in range(T):
+                    y, _, _ = _mlp_moe(p, v[:, t], 2, dt, c.top_k, None, None, c.top_k_aux, couple)
+                    for f in range(2):
+                        h[f, t] = h[f, t] + y[f]
+            else:
+                g = [gelu(v[f] @ p["w_up"].T) for f in range(2)]
+                if couple:
+                    g[1] = g[1] + p["b"][None, :] * g[0]
+                y = [g[f] @ p["w_down"].T for f in range(2)]
+                if couple:
+                    y[1] = y[1] + p["c"][None, :] * y[0]
+                for f in range(2):
+                    h[f] = h[f] + y[f]
+        g_prev = model.ln_next(l)
+        cache.release(l)
+    W_out = model.w_out()
+    logits = np.zeros((nb, T, 2, c.V))
+    p_mix = np.zeros((nb, T, c.V))
+    alpha = np.zeros((nb, T))
+    nxt = np.zeros((nb, T), dtype=np.int64)
+    for i in range(nb):
+        for f in range(2):
+            logits[i, :, f] = layer_norm(h_all[i, f], model.lnf(), c.eps) @ W_out.T
+        for t in range(T):
+            p_mix[i, t], alpha[i, t], nxt[i, t] = mix_head(logits[i, t, 0], logits[i, t, 1], mode)
+    cache.lens = cache.lens + T
+    return ForwardResult(logits, p_mix, alpha, nxt)
 
 
 # --------------------------------------------------------------------------

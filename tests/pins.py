@@ -600,6 +600,77 @@ def pin_fanout_closed_forms():
     assert np.max(np.abs(y[1] - want)) < 1e-12
 
 
+def _forward_vs_steps(cfg, T):
+    """forward_dual over T tokens and T teacher-forced dual decode steps
+    from the same cache: results and caches (oracle, both)."""
+    src = Inputs(cfg)
+    toks = np.stack([src.step_tokens(s) for s in range(T)], axis=1)      # [B, T]
+    ma, ca = _fresh(cfg, src)
+    fw = odf.forward_dual(ma, ca, toks)
+    mb, cb = _fresh(cfg, src)
+    steps = [odf.decode_step(mb, cb, toks[:, t], aux_on=True) for t in range(T)]
+    return fw, ca, steps, cb
+
+
+def pin_forward_equals_steps(cfg):
+    """The full-sequence dual forward is the run of teacher-forced dual decode
+    steps over the same tokens (the aux state at a position depends on
+    earlier positions only through the primary K/V): logits, p_mix, alpha
+    and next tokens of every position agree, and so do the caches. Covered
+    for the full method and the ablation switches (couplings off, aux
+    output, alpha = (1 + CP) / 2) and, in MoE models, the aux fan-out."""
+    variants = [cfg] + [cfg.replace(variant=v) for v in (1, 2, 4)]
+    if cfg.moe:
+        variants.append(cfg.replace(top_k_aux=cfg.E))
+    for c in variants:
+        T = 4
+        fw, ca, steps, cb = _forward_vs_steps(c, T)
+        for t, r in enumerate(steps):
+            assert np.max(np.abs(fw.logits[:, t] - r.logits)) < 1e-9
+            assert np.max(np.abs(fw.p_mix[:, t] - r.p_mix)) < 1e-12
+            assert np.max(np.abs(fw.alpha[:, t] - r.alpha)) < 1e-12
+            assert np.array_equal(fw.next_tok[:, t], r.next_tok)
+        ulp = 2.0 ** -7 if c.dtype == "bf16" else 2.0 ** -22
+        for l in range(c.L):
+            for x, y in zip(ca.layer(l), cb.layer(l)):
+                assert np.all(np.abs(x - y) <= ulp * np.abs(x) + 1e-30)
+        assert np.array_equal(ca.lens, cb.lens)
+
+
+def pin_forward_primary_is_prefill(cfg):
+    """The primary half of the dual forward is the prefill: the same primary
+    logits at every position and the same cache (the aux flow never feeds
+    back, [ES] Arquitectura Central)."""
+    c = cfg.replace(ctx=0)
+    src = Inputs(c)
+    prompt = src.prompt()
+    ma, ca = _fresh(c, src)
+    fw = odf.forward_dual(ma, ca, prompt)
+    mb, cb = _fresh(c, src)
+    lp = odf.prefill_primary(mb, cb, prompt)
+    assert np.max(np.abs(fw.logits[:, :, 0] - lp)) < 1e-9
+    for l in range(c.L):
+        for x, y in zip(ca.layer(l), cb.layer(l)):
+            assert np.array_equal(x, y)
+
+
+def pin_forward_causal(cfg):
+    """Both flows of the forward are causal: changing the last token changes
+    no earlier position's logits in either flow, and changes the last
+    position's."""
+    c = cfg.replace(ctx=0)
+    src = Inputs(c)
+    prompt = src.prompt()
+    p2 = prompt.copy()
+    p2[:, -1] = (p2[:, -1] + 1) % c.V
+    ma, ca = _fresh(c, src)
+    a = odf.forward_dual(ma, ca, prompt)
+    mb, cb = _fresh(c, src)
+    b = odf.forward_dual(mb, cb, p2)
+    assert np.max(np.abs(a.logits[:, :-1] - b.logits[:, :-1])) < 1e-12
+    assert np.min(np.max(np.abs(a.logits[:, -1] - b.logits[:, -1]), axis=-1)) > 1e-6
+
+
 ALL_BASIC = [pin_round_bf16, pin_layer_norm, pin_gelu, pin_attention_sdpa, pin_attention_closed_forms,
              pin_attention_dual, pin_mix_properties, pin_mix_golden, pin_topk, pin_mix_aux_mode,
              pin_mix_half_mode]
@@ -608,3 +679,4 @@ MODEL_PINS = [pin_aux_onoff, pin_tied_zero_coupling, pin_kv_sentinel, pin_prefil
 MOE_PINS = [pin_moe_single_expert_is_dense, pin_moe_all_experts_is_full_mixture, pin_moe_replay,
             pin_fanout_replay_and_primary, pin_fanout_closed_forms]
 VARIANT_PINS = [pin_no_coupling_tied, pin_variant_mix_in_step]
+FORWARD_PINS = [pin_forward_equals_steps, pin_forward_primary_is_prefill, pin_forward_causal]

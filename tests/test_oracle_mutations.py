@@ -218,3 +218,33 @@ def test_moe_aux_gates_from_primary_is_caught(monkeypatch):
     monkeypatch.setattr(odf, "_mlp_moe", wrong)
     with pytest.raises(AssertionError):
         pins.pin_moe_all_experts_is_full_mixture()
+
+
+def _mutated_forward(old, new):
+    """forward_dual with one line of its source replaced."""
+    import inspect
+    src = inspect.getsource(odf.forward_dual)
+    assert old in src, old
+    ns = dict(vars(odf))
+    exec(compile(src.replace(old, new), "<planted mistake>", "exec"), ns)
+    return ns["forward_dual"]
+
+
+FORWARD_MUTATIONS = [
+    ("aux_query_uncoupled", 'q2 = q2 + p["a"][None, :] * q1', "q2 = q2"),
+    ("aux_query_from_primary_row", 'q2 = u[1] @ p["w_qkv"][:d].T', 'q2 = u[0] @ p["w_qkv"][:d].T'),
+    ("attention_sees_next_position", "n = p0 + t + 1", "n = p0 + t + 2"),
+    ("mid_coupling_dropped", 'g[1] = g[1] + p["b"][None, :] * g[0]', "g[1] = g[1]"),
+    ("out_coupling_from_aux", 'y[1] = y[1] + p["c"][None, :] * y[0]', 'y[1] = y[1] + p["c"][None, :] * y[1]'),
+    ("aux_embedding_is_primary", "h_all[i, f] = model.emb(f, tokens[i])", "h_all[i, f] = model.emb(0, tokens[i])"),
+    ("kv_not_rounded", "round_to(qkv1[:, d:2 * d], dt)", "qkv1[:, d:2 * d]"),
+    ("mixture_swapped", "mix_head(logits[i, t, 0], logits[i, t, 1], mode)",
+     "mix_head(logits[i, t, 1], logits[i, t, 0], mode)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", FORWARD_MUTATIONS, ids=[m[0] for m in FORWARD_MUTATIONS])
+def test_forward_mutation_is_caught(monkeypatch, name, old, new):
+    monkeypatch.setattr(odf, "forward_dual", _mutated_forward(old, new))
+    with pytest.raises(AssertionError):
+        pins.pin_forward_equals_steps(pins.TINY_BF16)

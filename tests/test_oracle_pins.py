@@ -25,3 +25,9 @@ def test_moe_pins(pin):
 @pytest.mark.parametrize("pin", pins.VARIANT_PINS, ids=lambda f: f.__name__)
 def test_variant_pins(pin, cfg):
     pin(cfg)
+
+
+@pytest.mark.parametrize("cfg", [pins.TINY_F32, pins.TINY_BF16, pins.TINY_MOE], ids=lambda c: c.name)
+@pytest.mark.parametrize("pin", pins.FORWARD_PINS, ids=lambda f: f.__name__)
+def test_forward_pins(pin, cfg):
+    pin(cfg)
