@@ -29,7 +29,8 @@ DF_VARIANT_AUX_OUTPUT = 2
 DF_VARIANT_ALPHA_HALF = 4
 DF_MIX_PRIMARY, DF_MIX_COLLISION, DF_MIX_AUX, DF_MIX_HALF = 0, 1, 2, 3
 
-EXPORTS = ["df_workspace_bytes", "df_prefill_workspace_bytes", "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
+EXPORTS = ["df_workspace_bytes", "df_prefill_workspace_bytes", "df_forward_workspace_bytes", "df_forward_dual",
+           "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
            "df_attention_dual", "df_attention_workspace_bytes", "df_device_status", "df_status_str",
            "df_timing_enable", "df_timing_read", "df_stacked_gemv", "df_stacked_gemv_workspace_bytes",
            "df_pack_weights"]
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.df_workspace_bytes.argtypes = [P(df_config)]
         L.df_prefill_workspace_bytes.restype = sz
         L.df_prefill_workspace_bytes.argtypes = [P(df_config)]
+        L.df_forward_workspace_bytes.restype = sz
+        L.df_forward_workspace_bytes.argtypes = [P(df_config)]
+        L.df_forward_dual.restype = ctypes.c_int
+        L.df_forward_dual.argtypes = [P(df_config), P(df_weights), P(df_kv), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.df_decode_step.restype = ctypes.c_int
         L.df_decode_step.argtypes = [P(df_config), P(df_weights), P(df_kv), vp, i32, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
@@ -123,6 +128,15 @@ def df_workspace_bytes(cfg: df_config) -> int:
 
 def df_prefill_workspace_bytes(cfg: df_config) -> int:
     return int(lib().df_prefill_workspace_bytes(ctypes.byref(cfg)))
+
+
+def df_forward_workspace_bytes(cfg: df_config) -> int:
+    return int(lib().df_forward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def df_forward_dual(cfg, w, kv, d_tokens, T, d_logits, d_p_mix, d_alpha, d_next_tok, d_ws, ws_bytes, stream=0) -> int:
+    return lib().df_forward_dual(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), d_tokens, int(T), d_logits,
+                                 d_p_mix, d_alpha, d_next_tok, d_ws, ws_bytes, stream)
 
 
 def df_decode_step(cfg, w, kv, d_tokens, aux_on, d_router_logits, d_logits, d_p_mix, d_alpha, d_next_tok,

@@ -18,6 +18,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 size_t elem_size(int dtype) { return dtype == DF_BF16 ? 2 : 4; }
 
+typedef char* bf16p;   // byte pointer into bf16 hi / lo planes
+
 // Workspace regions (byte offsets from the workspace base).
 struct WsLayout {
     size_t status, h, xd, xo, xf, q, part, logits, r, ids, gates, offsets, perm, inv, grows, yrows, gpart, gcount,
@@ -104,6 +106,48 @@ PrefillLayout prefill_layout(const df_config& c) {
     P.fl = take(R16 * (size_t)c.ffn * 2);
     P.total = o;
     return P;
+}
+
+// Dual forward: chunks of Tc positions per sequence and both flows, the
+// stacked rows [primary 0..R-1 | pad | aux R16..R16+R-1] (R16 = R rounded up
+// to 16) in every two-flow buffer.
+int forward_chunk(const df_config& c) {
+    const int rows = (c.prefill_rows > 0 ? c.prefill_rows : DF_PREFILL_ROWS) / 2;
+    return std::max(1, std::min(c.max_seq, rows / c.batch));
+}
+struct ForwardLayout {
+    size_t h, xh, xl, q1, q2, fh, fl, keep, logits;   // fast path (byte offsets)
+    size_t pmix, alpha, tok;                        // per-position path
+    size_t total;
+};
+ForwardLayout forward_layout(const df_config& c) {
+    ForwardLayout F{};
+    size_t o = layout(c).total;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    if (fast_prefill(c)) {
+        const size_t R = (size_t)c.batch * forward_chunk(c), R16 = (R + 15) / 16 * 16, d = c.d_model;
+        F.h = take(2 * R16 * d * 4);
+        F.xh = take(2 * R16 * d * 2);
+        F.xl = take(2 * R16 * d * 2);
+        F.q1 = take(R * d * 4);
+        F.q2 = take(R * d * 4);
+        F.fh = take(2 * R16 * (size_t)c.ffn * 2);
+        F.fl = take(2 * R16 * (size_t)c.ffn * 2);
+        F.keep = take(R * d * 4);
+        F.logits = take(2 * R16 * (size_t)c.vocab * 4);
+    } else {
+        F.pmix = take((size_t)c.batch * c.vocab * 4);
+        F.alpha = take((size_t)c.batch * 4);
+        F.tok = take((size_t)c.batch * 4);
+    }
+    F.total = o;
+    return F;
+}
+
+int mix_mode_of(const df_config& c, int nflows) {
+    return nflows == 1 ? DF_MIX_PRIMARY
+           : (c.variant & DF_VARIANT_AUX_OUTPUT) ? DF_MIX_AUX
+           : (c.variant & DF_VARIANT_ALPHA_HALF) ? DF_MIX_HALF : DF_MIX_COLLISION;
 }
 
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15) == 0; }
@@ -321,9 +365,7 @@ struct Step {
             g.part = at<float>(L.gpart);
             set_x(g, w.lnf);   // final norm
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
-            const int mode = nflows == 1 ? DF_MIX_PRIMARY
-                             : (c.variant & DF_VARIANT_AUX_OUTPUT) ? DF_MIX_AUX
-                             : (c.variant & DF_VARIANT_ALPHA_HALF) ? DF_MIX_HALF : DF_MIX_COLLISION;
+            const int mode = mix_mode_of(c, nflows);
             if (dfk::mix_head(lg, B, c.vocab, mode, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
         }
         if (dfk::len_add(kv.len, B, 1, s) != hipSuccess) return DF_ERR_HIP;
@@ -435,6 +477,127 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
                 !ok(gemm(fh, fl, wdn, R, d, F, dfk::GEMM_RESID, h)))
                 return DF_ERR_HIP;
         }
+    }
+    return ok(dfk::len_add(kv->len, B, T, s)) ? DF_OK : DF_ERR_HIP;
+}
+
+size_t df_forward_workspace_bytes(const df_config* cfg) {
+    if (check_config(cfg) != DF_OK) return 0;
+    return forward_layout(*cfg).total;
+}
+
+int df_forward_dual(const df_config* cfg, const df_weights* w, const df_kv* kv, const int32_t* d_tokens,
+                    int32_t T, float* d_logits, float* d_p_mix, float* d_alpha, int32_t* d_next_tok, void* d_ws,
+                    size_t ws_bytes, void* stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_weights(*cfg, w))) return rc;
+    if ((rc = check_kv(kv))) return rc;
+    if (!d_tokens || !d_p_mix || !d_alpha) return DF_ERR_NULL;
+    if (T < 0 || T > cfg->max_seq) return DF_ERR_SHAPE;
+    if ((d_logits && !aligned16(d_logits)) || !aligned16(d_p_mix)) return DF_ERR_ALIGN;
+    if ((rc = check_ws(*cfg, d_ws, ws_bytes))) return rc;
+    if (ws_bytes < df_forward_workspace_bytes(cfg)) return DF_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const df_config& c = *cfg;
+    char* ws = reinterpret_cast<char*>(d_ws);
+    const ForwardLayout F = forward_layout(c);
+    const WsLayout L0 = layout(c);
+    const int B = c.batch, d = c.d_model, V = c.vocab;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    if (!fast_prefill(c)) {
+        // one dual step per position (the decode-step kernels), each row of
+        // outputs copied to its place in the [batch][T] buffers
+        Step st{c, *w, *kv, ws, L0, s};
+        float* lg = reinterpret_cast<float*>(ws + L0.logits);
+        float* pm = reinterpret_cast<float*>(ws + F.pmix);
+        float* al = reinterpret_cast<float*>(ws + F.alpha);
+        int32_t* tk = reinterpret_cast<int32_t*>(ws + F.tok);
+        for (int t = 0; t < T; ++t) {
+            rc = st.run(d_tokens + t, T, 2, nullptr, lg, pm, al, d_next_tok ? tk : nullptr, nullptr, true);
+            if (rc) return rc;
+            const size_t f4 = sizeof(float);
+            if (!ok(hipMemcpy2DAsync(d_p_mix + (size_t)t * V, (size_t)T * V * f4, pm, V * f4, V * f4, B,
+                                     hipMemcpyDeviceToDevice, s)) ||
+                !ok(hipMemcpy2DAsync(d_alpha + t, (size_t)T * f4, al, f4, f4, B, hipMemcpyDeviceToDevice, s)) ||
+                (d_next_tok && !ok(hipMemcpy2DAsync(d_next_tok + t, (size_t)T * 4, tk, 4, 4, B,
+                                                    hipMemcpyDeviceToDevice, s))) ||
+                (d_logits && !ok(hipMemcpy2DAsync(d_logits + (size_t)t * 2 * V, (size_t)T * 2 * V * f4, lg,
+                                                  2 * V * f4, 2 * V * f4, B, hipMemcpyDeviceToDevice, s))))
+                return DF_ERR_HIP;
+        }
+        return DF_OK;
+    }
+    // Both flows through the chunk rows: the primary rows are the prefill's;
+    // the aux rows take their query from the shared W_q rows, attend the
+    // primary K/V, and get the b / c couplings in the aux GEMM epilogues.
+    int32_t* status = reinterpret_cast<int32_t*>(ws + L0.status);
+    float* h = reinterpret_cast<float*>(ws + F.h);
+    bf16p xh = ws + F.xh, xl = ws + F.xl, fh = ws + F.fh, fl = ws + F.fl;
+    float* q1 = reinterpret_cast<float*>(ws + F.q1);
+    float* q2 = reinterpret_cast<float*>(ws + F.q2);
+    float* keep = reinterpret_cast<float*>(ws + F.keep);
+    float* lgt = reinterpret_cast<float*>(ws + F.logits);
+    const int H = c.n_heads, Dh = c.head_dim, Fd = c.ffn;
+    const bool couple = (c.variant & DF_VARIANT_NO_COUPLING) == 0;
+    const size_t es = 2;
+    const size_t kv_layer = (size_t)B * H * c.max_seq * Dh * es;
+    const int Tmax = forward_chunk(c);
+    auto timed = [&](int kclass, auto&& launch) -> hipError_t {
+        hipEvent_t e0, e1;
+        timing_events(kclass, &e0, &e1);
+        if (e0 && hipEventRecord(e0, s) != hipSuccess) return hipErrorUnknown;
+        const hipError_t e = launch();
+        if (e == hipSuccess && e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorUnknown;
+        return e;
+    };
+    auto gemm = [&](const void* ah, const void* al, const void* wt, int R, int N, int K, int epi, float* y, void* oh,
+                    void* ol, const dfk::QkvStore* qs = nullptr, const dfk::GemmCouple* cp = nullptr) {
+        return timed(1, [&] { return dfk::gemm(ah, al, wt, R, N, K, epi, y, oh, ol, s, qs, cp); });
+    };
+    for (int t0 = 0; t0 < T; t0 += Tmax) {
+        const int Tc = std::min(Tmax, T - t0), R = B * Tc, R16 = (R + 15) / 16 * 16, R2 = R16 + R;
+        const size_t xa = (size_t)R16 * d * es, fa = (size_t)R16 * Fd * es;   // byte offsets of the aux rows
+        float* h2 = h + (size_t)R16 * d;
+        if (!ok(dfk::prefill_embed_rows(w->tok_emb[0], w->pos_emb, d_tokens, T, t0, Tc, kv->len, B, d, c.max_seq,
+                                        V, h, status, s, w->tok_emb[1], R16)))
+            return DF_ERR_HIP;
+        for (int l = 0; l < c.n_layers; ++l) {
+            char* kc = reinterpret_cast<char*>(kv->k) + l * kv_layer;
+            char* vc = reinterpret_cast<char*>(kv->v) + l * kv_layer;
+            const char* wqkv = reinterpret_cast<const char*>(w->w_qkv) + (size_t)l * 3 * d * d * es;
+            const char* wo = reinterpret_cast<const char*>(w->w_o) + (size_t)l * d * d * es;
+            const char* wup = reinterpret_cast<const char*>(w->w_up) + (size_t)l * Fd * d * es;
+            const char* wdn = reinterpret_cast<const char*>(w->w_down) + (size_t)l * d * Fd * es;
+            const dfk::QkvStore st{reinterpret_cast<uint16_t*>(kc), reinterpret_cast<uint16_t*>(vc), kv->len, Tc,
+                                   t0, H, Dh, c.max_seq, status};
+            const dfk::GemmCouple cb{w->cpl_b + (size_t)l * Fd, reinterpret_cast<const uint16_t*>(fh),
+                                     reinterpret_cast<const uint16_t*>(fl), nullptr};
+            const dfk::GemmCouple cc{w->cpl_c + (size_t)l * d, nullptr, nullptr, keep};
+            if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R2, d, xh, xl, s)) ||
+                !ok(gemm(xh, xl, wqkv, R, 3 * d, d, dfk::GEMM_QKV, q1, nullptr, nullptr, &st)) ||
+                !ok(gemm(xh + xa, xl + xa, wqkv, R, d, d, dfk::GEMM_STORE, q2, nullptr, nullptr)) ||
+                !ok(timed(2, [&] {
+                    return dfk::prefill_attention(q1, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s, q2,
+                                                  couple ? w->cpl_a + (size_t)l * d : nullptr, R16);
+                })) ||
+                !ok(gemm(xh, xl, wo, R2, d, d, dfk::GEMM_RESID, h, nullptr, nullptr)) ||
+                !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R2, d, xh, xl, s)) ||
+                !ok(gemm(xh, xl, wup, R, Fd, d, dfk::GEMM_GELU_SPLIT, nullptr, fh, fl)) ||
+                !ok(gemm(xh + xa, xl + xa, wup, R, Fd, d, couple ? dfk::GEMM_GELU_SPLIT_CPL : dfk::GEMM_GELU_SPLIT,
+                         nullptr, fh + fa, fl + fa, nullptr, &cb)) ||
+                !ok(gemm(fh, fl, wdn, R, d, Fd, couple ? dfk::GEMM_RESID_KEEP : dfk::GEMM_RESID, h, nullptr, nullptr,
+                         nullptr, &cc)) ||
+                !ok(gemm(fh + fa, fl + fa, wdn, R, d, Fd, couple ? dfk::GEMM_RESID_CPL : dfk::GEMM_RESID, h2, nullptr,
+                         nullptr, nullptr, &cc)))
+                return DF_ERR_HIP;
+        }
+        // final norm, the shared LM head over both flows' rows, the mixture per position
+        if (!ok(dfk::prefill_layer_norm(h, w->lnf, c.ln_eps, R2, d, xh, xl, s)) ||
+            !ok(gemm(xh, xl, w->w_out, R2, V, d, dfk::GEMM_STORE, lgt, nullptr, nullptr)) ||
+            !ok(dfk::mix_rows(lgt, lgt + (size_t)R16 * V, R, V, mix_mode_of(c, 2), Tc, T, t0, d_logits, d_p_mix,
+                              d_alpha, d_next_tok, s)))
+            return DF_ERR_HIP;
     }
     return ok(dfk::len_add(kv->len, B, T, s)) ? DF_OK : DF_ERR_HIP;
 }

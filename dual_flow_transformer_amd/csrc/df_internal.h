@@ -37,6 +37,11 @@ hipError_t attention(const AttnArgs& a, hipStream_t s);
 // Mixture head over logits [B][2][V]; mode: DF_MIX_*.
 hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
                     int32_t* next_tok, hipStream_t s);
+// Mixture head over R row pairs (l1 + i V, l2 + i V) of a prefill-style
+// chunk (row i = b * Tc + t); outputs at row (b * T + t0 + t) of [B][T]
+// buffers; logits_out [B][T][2][V] may be NULL.
+hipError_t mix_rows(const float* l1, const float* l2, int R, int V, int mode, int Tc, int T, int t0,
+                    float* logits_out, float* p_mix, float* alpha, int32_t* next_tok, hipStream_t s);
 
 // K/V write at explicit positions (values fp32 [B][H][Dh]).
 hipError_t kv_append(int dtype, void* k, void* v, int B, int H, int S_max, int Dh,
@@ -124,6 +129,17 @@ enum GemmEpi {
     GEMM_GELU_SPLIT = 1,   // GELU(x w^T) as hi / lo fragment planes yh, yl [R16][N] (N % 32 == 0)
     GEMM_RESID = 2,        // y += x w^T (y: fp32 residual rows [R][N])
     GEMM_QKV = 3,          // N = 3 d: Q columns to y [R][d] (fp32), K / V columns into the bf16 cache
+    GEMM_GELU_SPLIT_CPL = 4,   // GELU(x w^T) + vec * (primary planes ph + pl at the same row), as planes
+    GEMM_RESID_KEEP = 5,   // keep[r] = x w^T and y += x w^T
+    GEMM_RESID_CPL = 6,    // y += x w^T + vec * keep[r]
+};
+// Coupling operands of the dual forward's aux-row epilogues (row r of the
+// aux GEMM pairs with row r of the primary one).
+struct GemmCouple {
+    const float* vec;     // b_l [N] or c_l [N]
+    const uint16_t* ph;   // primary GELU output planes [R16][N] (bf16 hi / lo)
+    const uint16_t* pl;
+    float* keep;          // primary MLP output [R][N] fp32
 };
 // Where GEMM_QKV puts K and V: row r = b * Tc + t goes to position
 // len[b] + t0 + t of sequence b; positions outside [0, S_max) are skipped
@@ -136,7 +152,7 @@ struct QkvStore {
     int32_t* status;
 };
 hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
-                void* yl, hipStream_t s, const QkvStore* kv = nullptr);
+                void* yl, hipStream_t s, const QkvStore* kv = nullptr, const GemmCouple* cp = nullptr);
 // fp32 rows [R][K] -> hi / lo fragment planes (K % 32 == 0).
 hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStream_t s);
 
@@ -144,18 +160,22 @@ hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStrea
 // Prefill row kernels (rows r = b * Tc + t of one chunk of Tc positions
 // t0 .. t0 + Tc - 1 per sequence, sequence b at position len[b] + t0 + t).
 // ---------------------------------------------------------------------------
-// h[r] = primary token embedding + position row (fp32).
+// h[r] = primary token embedding + position row (fp32); with emb_aux also
+// the aux rows h[R16 + r] from the aux embedding.
 hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_t* tok, int T, int t0, int Tc,
                               const int32_t* len, int B, int d, int S_max, int V, float* h, int32_t* status,
-                              hipStream_t s);
+                              hipStream_t s, const void* emb_aux = nullptr, int R16 = 0);
 // LayerNorm(h[r]) * g as hi / lo fragment planes xh, xl [R16][d]; d <= 4096, d % 32 == 0.
 hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, int d, void* xh, void* xl,
                               hipStream_t s);
 // Causal attention of the chunk queries q [R][H * Dh] (fp32) over the bf16
 // cache: row r, head h = softmax over keys 0 .. len[b] + t0 + t, written as
 // hi / lo fragment planes oh, ol [R16][H * Dh]. Dh == 128.
+// With q2 (aux raw queries [R][H * Dh]) both flows: the aux query is
+// q2 + a * q (a may be NULL) and its output rows sit at R16 + r.
 hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
-                             const void* kc, const void* vc, void* oh, void* ol, hipStream_t s);
+                             const void* kc, const void* vc, void* oh, void* ol, hipStream_t s,
+                             const float* q2 = nullptr, const float* a = nullptr, int R16 = 0);
 
 // ---------------------------------------------------------------------------
 // MoE with router replay

@@ -18,7 +18,9 @@
 // three stages deep: blocks kb + 1 and kb + 2 are in flight while the matrix
 // cores work on block kb. Epilogues: fp32 store, residual add, GELU written
 // back as hi/lo fragment planes for the next GEMM, or the Q/K/V split (Q
-// rows fp32, K and V rounded to bf16 straight into the cache).
+// rows fp32, K and V rounded to bf16 straight into the cache); for the aux
+// rows of the dual forward, the b coupling after the GELU and the c
+// coupling on the MLP output, each reading the primary row's value.
 #include "df_device.h"
 #include "df_internal.h"
 #include "mfma_tile.h"
@@ -55,6 +57,7 @@ struct GemmParams {
     bf16_t* yh;
     bf16_t* yl;
     QkvStore kv;
+    GemmCouple cp;
 };
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
@@ -163,16 +166,33 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
                 bf16_t* cache = n >= 2 * d ? q.vc : q.kc;
                 *reinterpret_cast<uint2*>(cache + (((size_t)b * q.H + hh) * q.S_max + pos) * q.Dh + e) =
                     make_uint2(df::pack_bf16x2(v.x, v.y), df::pack_bf16x2(v.z, v.w));
-            } else if (p.epi == GEMM_GELU_SPLIT) {
+            } else if (p.epi == GEMM_GELU_SPLIT || p.epi == GEMM_GELU_SPLIT_CPL) {
                 v.x = gelu(v.x); v.y = gelu(v.y); v.z = gelu(v.z); v.w = gelu(v.w);
+                const size_t o = frag_off(r, n, p.N);
+                if (p.epi == GEMM_GELU_SPLIT_CPL) {   // + b * the primary row's GELU output
+                    const uint2 qh = *reinterpret_cast<const uint2*>(p.cp.ph + o);
+                    const uint2 ql = *reinterpret_cast<const uint2*>(p.cp.pl + o);
+                    const float4 b = *reinterpret_cast<const float4*>(p.cp.vec + n);
+                    v.x = fmaf(b.x, df::bf16_lo(qh.x) + df::bf16_lo(ql.x), v.x);
+                    v.y = fmaf(b.y, df::bf16_hi(qh.x) + df::bf16_hi(ql.x), v.y);
+                    v.z = fmaf(b.z, df::bf16_lo(qh.y) + df::bf16_lo(ql.y), v.z);
+                    v.w = fmaf(b.w, df::bf16_hi(qh.y) + df::bf16_hi(ql.y), v.w);
+                }
                 uint2 hv, lv;
                 df::split_hi_lo(v, hv, lv);
-                const size_t o = frag_off(r, n, p.N);
                 *reinterpret_cast<uint2*>(p.yh + o) = hv;
                 *reinterpret_cast<uint2*>(p.yl + o) = lv;
             } else {
                 float4* dst = reinterpret_cast<float4*>(p.y + (size_t)r * p.N + n);
-                if (p.epi == GEMM_RESID) {
+                if (p.epi == GEMM_RESID_KEEP)        // the primary MLP output, kept for the c coupling
+                    *reinterpret_cast<float4*>(p.cp.keep + (size_t)r * p.N + n) = v;
+                if (p.epi == GEMM_RESID_CPL) {       // + c * the primary row's MLP output
+                    const float4 y1 = *reinterpret_cast<const float4*>(p.cp.keep + (size_t)r * p.N + n);
+                    const float4 c = *reinterpret_cast<const float4*>(p.cp.vec + n);
+                    v.x = fmaf(c.x, y1.x, v.x); v.y = fmaf(c.y, y1.y, v.y);
+                    v.z = fmaf(c.z, y1.z, v.z); v.w = fmaf(c.w, y1.w, v.w);
+                }
+                if (p.epi != GEMM_STORE) {
                     const float4 h = *dst;
                     v.x += h.x; v.y += h.y; v.z += h.z; v.w += h.w;
                 }
@@ -202,14 +222,19 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float* x, int R, 
 }  // namespace
 
 hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
-                void* yl, hipStream_t s, const QkvStore* kv) {
-    if (R < 1 || N < 16 || N % 16 || K < 32 || K % 32) return hipErrorInvalidValue;
-    if (epi == GEMM_GELU_SPLIT ? (!yh || !yl || N % 32) : !y) return hipErrorInvalidValue;
+                void* yl, hipStream_t s, const QkvStore* kv, const GemmCouple* cp) {
+    if (R < 1 || N < 16 || N % 16 || K < 32 || K % 32 || epi < GEMM_STORE || epi > GEMM_RESID_CPL)
+        return hipErrorInvalidValue;
+    const bool split = epi == GEMM_GELU_SPLIT || epi == GEMM_GELU_SPLIT_CPL;
+    if (split ? (!yh || !yl || N % 32) : !y) return hipErrorInvalidValue;
     if (epi == GEMM_QKV && (!kv || N % 3 || (N / 3) % 16 || kv->Dh % 4 || kv->Tc < 1 || R % kv->Tc))
+        return hipErrorInvalidValue;
+    if ((epi == GEMM_GELU_SPLIT_CPL && (!cp || !cp->vec || !cp->ph || !cp->pl)) ||
+        (epi == GEMM_RESID_KEEP && (!cp || !cp->keep)) || (epi == GEMM_RESID_CPL && (!cp || !cp->vec || !cp->keep)))
         return hipErrorInvalidValue;
     GemmParams p{reinterpret_cast<const bf16_t*>(xh), reinterpret_cast<const bf16_t*>(xl),
                  reinterpret_cast<const bf16_t*>(w), R, N, K, epi, y, reinterpret_cast<bf16_t*>(yh),
-                 reinterpret_cast<bf16_t*>(yl), kv ? *kv : QkvStore{}};
+                 reinterpret_cast<bf16_t*>(yl), kv ? *kv : QkvStore{}, cp ? *cp : GemmCouple{}};
     hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&gemm_bf16), kGemmLds);
     if (e != hipSuccess) return e;
     (void)hipGetLastError();

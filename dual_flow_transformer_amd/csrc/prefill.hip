@@ -19,10 +19,12 @@ using tile::u32x4;
 
 // h[r] = E_primary[tok[b][t0 + t]] + P[len[b] + t0 + t] (fp32), r = b * Tc + t.
 // Token ids outside [0, V) are clamped and flagged (status bit 1).
-__global__ __launch_bounds__(256) void prefill_embed(const bf16_t* emb, const bf16_t* pos_emb, const int32_t* tok,
-                                                     int T, int t0, int Tc, const int32_t* len, int d, int S_max,
-                                                     int V, float* h, int32_t* status) {
+__global__ __launch_bounds__(256) void prefill_embed(const bf16_t* emb0, const bf16_t* emb1, const bf16_t* pos_emb,
+                                                     const int32_t* tok, int T, int t0, int Tc, const int32_t* len,
+                                                     int d, int S_max, int V, int R16, float* h, int32_t* status) {
     const int r = blockIdx.x, b = r / Tc, t = r - b * Tc;
+    const bf16_t* emb = blockIdx.y ? emb1 : emb0;       // flow blockIdx.y, rows at flow * R16 + r
+    h += (size_t)blockIdx.y * R16 * d;
     int id = tok[(size_t)b * T + t0 + t];
     if (id < 0 || id >= V) {
         if (status && threadIdx.x == 0) status[0] |= 2;
@@ -125,7 +127,15 @@ __device__ __forceinline__ int vt_col(int j) {
     return c * 32 + g * 8 + o * 4 + (j & 3);
 }
 
-__global__ __launch_bounds__(256) void attn_prefill(const float* q, int Tc, int t0, const int32_t* len, int H,
+struct AttnRows {
+    const float* q1;    // [R][H * Dh] primary queries
+    const float* q2;    // [R][H * Dh] aux raw queries (two flows) or NULL
+    const float* a;     // [H * Dh] query coupling (Q2 = Q2raw + a * Q1) or NULL
+    int nflows;         // 1: prefill; 2: dual forward (flow f output rows at f * R16 + r)
+    int R16;
+};
+
+__global__ __launch_bounds__(256) void attn_prefill(AttnRows qs, int Tc, int t0, const int32_t* len, int H,
                                                     int S_max, const bf16_t* kc, const bf16_t* vc, float scale_log2,
                                                     bf16_t* oh, bf16_t* ol) {
     __shared__ bf16_t Ks[AKB * KSP];
@@ -135,9 +145,13 @@ __global__ __launch_bounds__(256) void attn_prefill(const float* q, int Tc, int 
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int d = H * ADH;
     const int pos0 = len[b] + t0;                            // position of chunk row t = 0
-    const int tw0 = qb * AQG + wv * AQW;                     // first query (chunk row) of this wave
+    // one flow: 128 positions per workgroup, 32 per wave; two flows: 64
+    // positions, waves 0-1 take the primary queries and waves 2-3 the aux
+    // queries of the same positions, sharing every staged key block
+    const int QG = AQG / qs.nflows, flow = qs.nflows == 2 ? wv >> 1 : 0;
+    const int tw0 = qb * QG + (qs.nflows == 2 ? (wv & 1) : wv) * AQW;   // first query (chunk row) of this wave
     const int wave_last = tw0 < Tc ? pos0 + min(Tc - 1, tw0 + AQW - 1) : -1;
-    const int last_key = min(pos0 + min(Tc, qb * AQG + AQG) - 1, S_max - 1);
+    const int last_key = min(pos0 + min(Tc, qb * QG + QG) - 1, S_max - 1);
     const size_t head = ((size_t)b * H + h) * S_max * ADH;
 
     // the wave's queries as bf16 hi/lo B operands, scaled by log2(e)/sqrt(Dh)
@@ -148,11 +162,23 @@ __global__ __launch_bounds__(256) void attn_prefill(const float* q, int Tc, int 
         t_q[qt] = tw0 + qt * 16 + li;
         const int tq = min(t_q[qt], Tc - 1);
         qpos[qt] = pos0 + tq;
-        const float* qr = q + (size_t)(b * Tc + tq) * d + h * ADH;
+        const size_t qo = (size_t)(b * Tc + tq) * d + h * ADH;
+        const float* qr = (flow ? qs.q2 : qs.q1) + qo;
         #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const float4 a = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8);
-            const float4 c = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8 + 4);
+            float4 a = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8);
+            float4 c = *reinterpret_cast<const float4*>(qr + ks * 32 + lg * 8 + 4);
+            if (flow && qs.a) {   // Q2 = Q2raw + a * Q1
+                const int e = h * ADH + ks * 32 + lg * 8;
+                const float4 a0 = *reinterpret_cast<const float4*>(qs.a + e);
+                const float4 a1 = *reinterpret_cast<const float4*>(qs.a + e + 4);
+                const float4 p0 = *reinterpret_cast<const float4*>(qs.q1 + qo + ks * 32 + lg * 8);
+                const float4 p1 = *reinterpret_cast<const float4*>(qs.q1 + qo + ks * 32 + lg * 8 + 4);
+                a = make_float4(fmaf(a0.x, p0.x, a.x), fmaf(a0.y, p0.y, a.y), fmaf(a0.z, p0.z, a.z),
+                                fmaf(a0.w, p0.w, a.w));
+                c = make_float4(fmaf(a1.x, p1.x, c.x), fmaf(a1.y, p1.y, c.y), fmaf(a1.z, p1.z, c.z),
+                                fmaf(a1.w, p1.w, c.w));
+            }
             uint2 h0, l0, h1, l1;
             df::split_hi_lo(make_float4(a.x * scale_log2, a.y * scale_log2, a.z * scale_log2, a.w * scale_log2),
                             h0, l0);
@@ -278,7 +304,7 @@ __global__ __launch_bounds__(256) void attn_prefill(const float* q, int Tc, int 
         lt += __shfl_xor(lt, 32, 64);
         if (t_q[qt] >= Tc) continue;
         const float inv = 1.0f / lt;
-        const int row = b * Tc + t_q[qt];
+        const int row = flow * qs.R16 + b * Tc + t_q[qt];
         #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const float4 v = make_float4(oacc[qt][dt][0] * inv, oacc[qt][dt][1] * inv, oacc[qt][dt][2] * inv,
@@ -296,10 +322,11 @@ __global__ __launch_bounds__(256) void attn_prefill(const float* q, int Tc, int 
 
 hipError_t prefill_embed_rows(const void* emb, const void* pos_emb, const int32_t* tok, int T, int t0, int Tc,
                               const int32_t* len, int B, int d, int S_max, int V, float* h, int32_t* status,
-                              hipStream_t s) {
+                              hipStream_t s, const void* emb_aux, int R16) {
     (void)hipGetLastError();
-    hipLaunchKernelGGL(prefill_embed, dim3(B * Tc), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(emb),
-                       reinterpret_cast<const bf16_t*>(pos_emb), tok, T, t0, Tc, len, d, S_max, V, h, status);
+    hipLaunchKernelGGL(prefill_embed, dim3(B * Tc, emb_aux ? 2 : 1), dim3(256), 0, s,
+                       reinterpret_cast<const bf16_t*>(emb), reinterpret_cast<const bf16_t*>(emb_aux),
+                       reinterpret_cast<const bf16_t*>(pos_emb), tok, T, t0, Tc, len, d, S_max, V, R16, h, status);
     return hipGetLastError();
 }
 
@@ -313,10 +340,13 @@ hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, 
 }
 
 hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
-                             const void* kc, const void* vc, void* oh, void* ol, hipStream_t s) {
+                             const void* kc, const void* vc, void* oh, void* ol, hipStream_t s, const float* q2,
+                             const float* a, int R16) {
     if (Dh != ADH) return hipErrorInvalidValue;
+    const AttnRows qs{q, q2, a, q2 ? 2 : 1, R16};
+    const int QG = AQG / qs.nflows;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(attn_prefill, dim3((Tc + AQG - 1) / AQG, H, B), dim3(256), 0, s, q, Tc, t0, len, H, S_max,
+    hipLaunchKernelGGL(attn_prefill, dim3((Tc + QG - 1) / QG, H, B), dim3(256), 0, s, qs, Tc, t0, len, H, S_max,
                        reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
                        df::kLog2e / sqrtf((float)Dh), reinterpret_cast<bf16_t*>(oh), reinterpret_cast<bf16_t*>(ol));
     return hipGetLastError();

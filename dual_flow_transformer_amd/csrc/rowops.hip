@@ -128,16 +128,36 @@ __global__ void len_add_kernel(int32_t* len, int B, int inc) {
     if (b < B) len[b] += inc;
 }
 
-// Mixture head: one block of 1024 threads per sequence. mode: DF_MIX_*.
-__global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int V, int mode,
-                                                        float* p_mix, float* alpha, int32_t* next_tok) {
+// Mixture head: one block of 1024 threads per output row. mode: DF_MIX_*.
+// Input row i: l1 = m.l1 + i * m.stride, l2 = m.l2 + i * m.stride; output
+// row i, or with m.Tc > 0 the row (i / Tc) * T + t0 + i % Tc of [B][T]
+// outputs (chunk row i = b * Tc + t); m.logits_out, if set, receives both
+// logit rows there ([row][2][V]).
+struct MixRows {
+    const float* l1;
+    const float* l2;
+    size_t stride;
+    int Tc, T, t0;
+    float* logits_out;
+};
+
+__global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mode, float* p_mix, float* alpha,
+                                                        int32_t* next_tok) {
     const int aux_on = mode != DF_MIX_PRIMARY;
     __shared__ float red[16];
     __shared__ float bv[16];
     __shared__ int bi[16];
-    const int b = blockIdx.x;
-    const float* l1 = logits + (size_t)b * 2 * V;
-    const float* l2 = l1 + V;
+    const int i = blockIdx.x;
+    const float* l1 = m.l1 + (size_t)i * m.stride;
+    const float* l2 = m.l2 + (size_t)i * m.stride;
+    const int b = m.Tc > 0 ? (i / m.Tc) * m.T + m.t0 + i % m.Tc : i;
+    if (m.logits_out) {
+        float* lo = m.logits_out + (size_t)b * 2 * V;
+        for (int v = threadIdx.x; v < V; v += blockDim.x) {
+            lo[v] = l1[v];
+            lo[V + v] = l2[v];
+        }
+    }
     float mx1 = -INFINITY, mx2 = -INFINITY;
     for (int v = threadIdx.x; v < V; v += blockDim.x) {
         mx1 = fmaxf(mx1, l1[v]);
@@ -193,8 +213,17 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(const float* logits, int
 
 hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
                     int32_t* next_tok, hipStream_t s) {
+    const MixRows m{logits, logits + V, (size_t)2 * V, 0, 0, 0, nullptr};
     (void)hipGetLastError();
-    hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, logits, V, mode, p_mix, alpha, next_tok);
+    hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, m, V, mode, p_mix, alpha, next_tok);
+    return hipGetLastError();
+}
+
+hipError_t mix_rows(const float* l1, const float* l2, int R, int V, int mode, int Tc, int T, int t0,
+                    float* logits_out, float* p_mix, float* alpha, int32_t* next_tok, hipStream_t s) {
+    const MixRows m{l1, l2, (size_t)V, Tc, T, t0, logits_out};
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(mix_head_kernel, dim3(R), dim3(1024), 0, s, m, V, mode, p_mix, alpha, next_tok);
     return hipGetLastError();
 }
 

@@ -211,6 +211,27 @@ class DecodeModel:
                                      self.ws_bytes, _stream())
         _abi.check(rc, "df_prefill_primary")
 
+    def forward(self, tokens_bt: torch.Tensor, logits: bool = True, next_tok: bool = True):
+        """Full-sequence dual forward over tokens [B][T]; returns (logits
+        [B][T][2][V] or None, p_mix [B][T][V], alpha [B][T], next_tok [B][T]
+        or None). Grows the workspace on first use."""
+        c = self.cfg
+        T = tokens_bt.shape[1]
+        need = _abi.df_forward_workspace_bytes(self.config)
+        if need > self.ws_bytes:
+            ws = torch.zeros(need, dtype=torch.uint8, device=self.dev)
+            ws[:256].copy_(self.ws[:256])             # device status word
+            self.ws, self.ws_bytes = ws, need
+        lg = torch.empty(c.B, T, 2, c.V, dtype=torch.float32, device=self.dev) if logits else None
+        pm = torch.empty(c.B, T, c.V, dtype=torch.float32, device=self.dev)
+        al = torch.empty(c.B, T, dtype=torch.float32, device=self.dev)
+        nt = torch.empty(c.B, T, dtype=torch.int32, device=self.dev) if next_tok else None
+        rc = _abi.df_forward_dual(self.config, self.weights, self.kv, tokens_bt.data_ptr(), T, _ptr(lg),
+                                  pm.data_ptr(), al.data_ptr(), _ptr(nt), self.ws.data_ptr(), self.ws_bytes,
+                                  _stream())
+        _abi.check(rc, "df_forward_dual")
+        return lg, pm, al, nt
+
     def status(self) -> int:
         rc, v = _abi.df_device_status(self.ws.data_ptr(), _stream())
         _abi.check(rc, "df_device_status")

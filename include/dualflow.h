@@ -196,6 +196,36 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
                        const int32_t* d_tokens, int32_t T, void* d_ws, size_t ws_bytes,
                        void* stream);
 
+/* Bytes of workspace df_forward_dual needs (>= df_workspace_bytes). Dense
+ * bf16 models with head_dim 128 add one chunk of both flows' rows, about
+ * 2 R (3 d + ffn + vocab) * 4 bytes for R = batch * Tc; others a few rows
+ * of outputs. 0 when the config is invalid. */
+size_t df_forward_workspace_bytes(const df_config* cfg);
+
+/* Full-sequence dual forward: both flows at every position of T tokens per
+ * sequence (d_tokens [batch][T]) at positions len[b] .. len[b]+T-1, as both
+ * flows are evaluated along the whole sequence in training (section "Costes
+ * de Inferencia vs. Entrenamiento"). The primary flow is the causal
+ * Transformer of the prefill and writes K/V of every position; the aux flow
+ * forms Q2 = Q2raw + a * Q1 and attends the primary K/V of positions up to
+ * its own, with the b / c couplings of each position (sections "Arquitectura
+ * Central", "Mecanismos Clave"). Equals T teacher-forced df_decode_step
+ * calls with aux_on = 1 (up to rounding order). Advances len[b] by T.
+ *  d_logits [batch][T][2][vocab] or NULL; d_p_mix [batch][T][vocab];
+ *  d_alpha [batch][T]; d_next_tok [batch][T] or NULL (argmax of p_mix).
+ *  Model variants (cfg->variant) apply as in the decode step; MoE models
+ *  route every position with the primary router (replay for the aux row).
+ *  Dense bf16 models with head_dim 128: chunks of Tc = max(1, min(max_seq,
+ *    rows / 2 / batch)) positions (rows = cfg->prefill_rows or
+ *    DF_PREFILL_ROWS) through tiled matrix-core GEMMs over the stacked rows
+ *    of both flows and one causal attention pass for both query sets.
+ *  Other models: one dual step per position with the decode-step kernels.
+ * ws_bytes must be at least df_forward_workspace_bytes(cfg). */
+int df_forward_dual(const df_config* cfg, const df_weights* w, const df_kv* kv,
+                    const int32_t* d_tokens, int32_t T, float* d_logits, float* d_p_mix,
+                    float* d_alpha, int32_t* d_next_tok, void* d_ws, size_t ws_bytes,
+                    void* stream);
+
 /* Write K/V entries of one layer at explicit positions: for each sequence b
  * and head h, k[layer][b][h][d_pos[b]][:] = round(d_k[b][h][:]) (same for v),
  * d_k, d_v fp32 [batch][n_heads][head_dim], rounded to the storage dtype.
