@@ -54,9 +54,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "prefill"],
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5", "prefill", "forward"],
                     help="c5 (default) / c3 / c4: full decode step; c2: the shared-K/V attention kernel alone; "
-                         "prefill: primary prefill of 16 x 2048 tokens through the 1.3B dense model")
+                         "prefill: primary prefill of 16 x 2048 tokens through the 1.3B dense model; "
+                         "forward: full-sequence dual forward of the same model and tokens")
     ap.add_argument("--variant", type=int, default=0,
                     help="model variant switches: 1 couplings off, 2 aux output (no mixture), 4 alpha=(1+CP)/2")
     ap.add_argument("--top-k-aux", type=int, default=0,
@@ -349,6 +350,136 @@ def bench_prefill(args):
     print(json.dumps(out), flush=True)
 
 
+def forward_flops(cfg, T: int) -> dict:
+    """Algorithmic flops of the dual forward of T positions per sequence from
+    an empty cache: the primary flow as in the prefill; the aux flow's Q,
+    O, up and down projections (its K/V columns are not formed); both
+    flows' causal attention; the LM head of both flows at every position."""
+    pri = prefill_flops(cfg, T)
+    aux_proj = 2 * cfg.B * T * (2 * cfg.d * cfg.d + 2 * cfg.d * cfg.F) * cfg.L
+    head = 2 * 2 * cfg.B * T * cfg.d * cfg.V
+    proj = pri["projections"] + aux_proj + head
+    attn = 2 * pri["attention"]
+    return {"projections": proj, "attention": attn, "total": proj + attn}
+
+
+def forward_cpu_baseline(cfg, T: int, n_layers: int = 1, min_seconds: float = 10.0):
+    """The oracle's dual forward on a bounded sample: sequence 0's T tokens
+    through the first n_layers layers plus the LM head and mixture of every
+    position, repeated until min_seconds; the layer part scaled to full
+    depth."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import dualflow as odf
+    from synth.workloads import Inputs
+
+    sub = cfg.replace(L=n_layers, B=1)
+    src = Inputs(sub)
+    model = odf.Model(src, keep_layers=True)
+    for l in range(n_layers):
+        model.layer(l)
+    model.w_out()
+    model.lnf()
+    toks = Inputs(cfg).prompt()[:1, :T]
+    t, reps = 0.0, 0
+    while t < min_seconds or reps < 1:
+        cache = odf.Cache(sub, [0], src)
+        cache.lens[:] = 0
+        t0 = time.perf_counter()
+        odf.forward_dual(model, cache, toks)
+        t += time.perf_counter() - t0
+        reps += 1
+    # the head part (final norm, LM head of both flows, mixture per position) timed alone
+    h = np.zeros((T, cfg.d))
+    t0 = time.perf_counter()
+    lg = [odf.layer_norm(h, model.lnf(), cfg.eps) @ model.w_out().T for _ in range(2)]
+    for i in range(T):
+        odf.mix_head(lg[0][i], lg[1][i])
+    t_head = time.perf_counter() - t0
+    t_tok = ((t / reps - t_head) / n_layers * cfg.L + t_head) / T
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": 1.0 / t_tok, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"sequence 0 of {cfg.B}: its {T} tokens through the first {n_layers} of {cfg.L} layers "
+                       f"and the LM head + mixture of every position, {reps} repetitions ({t:.1f} s); layer time "
+                       f"scaled to {cfg.L} layers"), "host_cpus": os.cpu_count()}
+
+
+def bench_forward(args):
+    """Dual forward workload: 16 sequences of 2048 tokens through the 24-layer
+    d 2048 dense model, both flows at every position, empty cache. A step is
+    one df_forward_dual call (len reset to 0 before it) producing p_mix and
+    alpha of every position. Value: tokens/s (positions, both flows each);
+    roofline: the tiled GEMM against the dense bf16 matrix-core peak."""
+    import torch
+
+    from dual_flow_transformer_amd import _abi
+    from dual_flow_transformer_amd.runtime import DecodeModel
+    from synth.workloads import FORWARD_DENSE, Inputs
+
+    cfg = FORWARD_DENSE
+    T = cfg.prompt_len
+    log(f"[bench] forward workload {cfg.name}: filling device inputs")
+    gm = DecodeModel(cfg, fill="device")
+    tok = gm.tokens(Inputs(cfg).prompt()).contiguous()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gm.len.zero_()
+        gm.forward(tok, logits=False, next_tok=False)
+
+    W, K = args.warmup, args.steps
+    for _ in range(max(W, 1)):
+        step()
+    torch.cuda.synchronize()
+    res = {}
+    for kclass in (1, 2):
+        _abi.check(_abi.df_timing_enable(kclass), "df_timing_enable")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rc, kms, kn = _abi.df_timing_read()
+        _abi.check(rc, "df_timing_read")
+        res[kclass] = (e0.elapsed_time(e1) / K, kms, kn)
+    ms = min(res[1][0], res[2][0])
+    status = gm.status()
+    fl = forward_flops(cfg, T)
+    tok_s = cfg.B * T / (ms / 1e3)
+    gemm_ms, gemm_n = res[1][1], res[1][2]
+    attn_ms, attn_n = res[2][1], res[2][2]
+    gemm_tf = fl["projections"] / (gemm_ms / K / 1e3) / 1e12
+    attn_tf = fl["attention"] / (attn_ms / K / 1e3) / 1e12
+    log(f"[bench] forward {ms:.2f} ms/step, {tok_s:.0f} tok/s; GEMM {gemm_ms / K:.2f} ms/step ({gemm_tf:.0f} TF/s), "
+        f"attention {attn_ms / K:.2f} ms/step ({attn_tf:.0f} TF/s); status {status}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        del gm
+        torch.cuda.empty_cache()
+        cpu = forward_cpu_baseline(cfg, T)
+        log(f"[bench] oracle forward: {cpu['value']:.2f} tok/s")
+    out = {
+        "metric": "dual-flow full-sequence forward tokens/s at 1 GPU; GEMM TFLOP/s vs dense bf16 matrix-core peak",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded random-init weights, uniform random tokens)",
+        "config": {"workload": cfg.name, "layers": cfg.L, "d_model": cfg.d, "heads": cfg.H, "head_dim": cfg.Dh,
+                   "ffn": cfg.F, "vocab": cfg.V, "global_batch": cfg.B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "gemm_bf16 (projections and LM head of both flows)", "bound": "mfma",
+                     "achieved": gemm_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": gemm_tf / PEAK_BF16_TFLOPS,
+                     "traffic": None, "avg_launch_ms": gemm_ms / max(gemm_n, 1), "launches": gemm_n,
+                     "algorithmic_flops_per_launch": fl["projections"] * K / max(gemm_n, 1)},
+        "attention": {"kernel": "attn_prefill (both query sets)", "achieved_TFLOPs": attn_tf,
+                      "avg_launch_ms": attn_ms / max(attn_n, 1), "launches": attn_n,
+                      "algorithmic_flops_per_step": fl["attention"]},
+        "flops_per_step": fl, "device_status": status, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -360,6 +491,9 @@ def main():
         return
     if args.workload == "prefill":
         bench_prefill(args)
+        return
+    if args.workload == "forward":
+        bench_forward(args)
         return
     import numpy as np
     import torch

@@ -102,6 +102,8 @@ PRESETS = {"c1": C1_TINY, "c2": C2_ATTN, "c3": C3_DENSE, "c4": C4_MOE, "c5": C5_
 # Primary prefill of the 1.3B dense model: the 2048-position prompts whose
 # cache the dense decode workload starts from (16 sequences, empty cache).
 PREFILL_DENSE = C3_DENSE.replace(name="prefill_dense_1p3b_b16_t2048", ctx=0, S_max=2048, prompt_len=2048)
+# Full-sequence dual forward of the same model over the same 16 x 2048 tokens.
+FORWARD_DENSE = C3_DENSE.replace(name="forward_dual_dense_1p3b_b16_t2048", ctx=0, S_max=2048, prompt_len=2048)
 
 
 def normal_quantiles(n: int) -> np.ndarray:
