@@ -32,6 +32,7 @@ namespace {
 using tile::bf16x8;
 using tile::f32x4;
 using tile::u32x4;
+using tile::frag_off;
 
 constexpr int TT = 256;                   // tile edge (weight rows and activation rows)
 constexpr int TT16 = TT / 16;             // 16-row fragments per tile edge
@@ -61,11 +62,6 @@ struct GemmParams {
 };
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
-
-// Offset of element (r, k) in the fragment layout of a [*][K] matrix.
-__device__ __forceinline__ size_t frag_off(int r, int k, int K) {
-    return ((size_t)((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
-}
 
 __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
     extern __shared__ u32x4 lds[];   // [stage][piece][lane]

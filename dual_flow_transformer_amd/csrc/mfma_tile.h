@@ -48,6 +48,11 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
     lo = (u32x4){l[0], l[1], l[2], l[3]};
 }
 
+// Offset of element (r, k) of a [*][K] matrix in the fragment layout.
+__device__ __forceinline__ size_t frag_off(int r, int k, int K) {
+    return ((size_t)((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 // Lane's base of 16-row tile t16 in the fragment layout (k-block 0).
 __device__ __forceinline__ const bf16_t* frag_tile(const bf16_t* w, int t16, int K, int lane) {
     return w + ((size_t)t16 * (K / 32) * 64 + lane) * 8;

@@ -16,6 +16,7 @@ namespace {
 using tile::bf16x8;
 using tile::f32x4;
 using tile::u32x4;
+using tile::frag_off;
 
 // h[r] = E_primary[tok[b][t0 + t]] + P[len[b] + t0 + t] (fp32), r = b * Tc + t.
 // Token ids outside [0, V) are clamped and flagged (status bit 1).
@@ -34,11 +35,6 @@ __global__ __launch_bounds__(256) void prefill_embed(const bf16_t* emb0, const b
     pos = pos < 0 ? 0 : (pos >= S_max ? S_max - 1 : pos);
     for (int i = threadIdx.x; i < d; i += blockDim.x)
         h[(size_t)r * d + i] = df::bf16_to_f32(emb[(size_t)id * d + i]) + df::bf16_to_f32(pos_emb[(size_t)pos * d + i]);
-}
-
-// Offset of element (r, k) in the fragment layout of a [*][K] matrix.
-__device__ __forceinline__ size_t frag_off(int r, int k, int K) {
-    return ((size_t)((r >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
 }
 
 // LN(h[r]; g) for R rows of width d as hi / lo fragment planes: one wave
