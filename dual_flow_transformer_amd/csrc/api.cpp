@@ -352,9 +352,8 @@ struct Step {
                 m.ids = at<int32_t>(L.ids); m.gates = at<float>(L.gates); m.offsets = at<int32_t>(L.offsets);
                 m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = at<float>(L.grows);
                 m.y_rows = at<float>(L.yrows);
+                m.g_next = g_next; m.eps = c.ln_eps; m.x_next = xd;   // next norm fused into the combine
                 if (dfk::moe(m, s) != hipSuccess) return DF_ERR_HIP;
-                if (dfk::layer_norm_rows(c.dtype, h, g_next, c.ln_eps, B, d, nflows, xd, s) != hipSuccess)
-                    return DF_ERR_HIP;
             }
         }
         if (head) {

@@ -58,10 +58,6 @@ hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* p
                     int V, int nflows, const float* g, float eps, float* h, void* x, int32_t* status,
                     hipStream_t s);
 
-// x[r] = LN(h[r]; g) (fp32) for the stacked rows in use.
-hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps, int B, int d,
-                           int nflows, void* x, hipStream_t s);
-
 // Residual rows are summarised per segment of kStatSeg columns as (mean, M2)
 // pairs, stats[(r * nseg + seg) * 2 + {0, 1}] for stacked row r, nseg =
 // ceil(d / kStatSeg); a LayerNorm then needs no further pass over the row.

@@ -16,8 +16,8 @@
 //    aux row where the primary also ran that expert.
 // 3. moe_expert (down): same grouping over the expert's down projection.
 // 4. moe_combine: gate-weighted sum over each flow's ranks in rank order, c
-//    coupling on the aux output, residual add. Integer work (ids, offsets,
-//    perm) is exact; no atomics.
+//    coupling on the aux output, residual add, then the next LayerNorm of the
+//    updated rows. Integer work (ids, offsets, perm) is exact; no atomics.
 #include <algorithm>
 
 #include "df_device.h"
@@ -50,20 +50,29 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route(const float* r, const
                                                            int32_t* ids_out, int32_t* offsets, int32_t* perm,
                                                            int32_t* inv) {
     __shared__ int32_t s_ids[64 * kMaxK];
-    __shared__ int32_t s_cnt[1025];
+    __shared__ int32_t s_cnt[1024];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int NWAVE = kRouteThreads / 64, SPW = 64 / NWAVE;   // sequences per wave (B <= 64)
     const int kr = max(k, ka), kk = nflows == 2 ? kr : k;
-    for (int b = wv; b < B; b += kRouteThreads / 64) {
+    // every logit row of the wave's sequences first: one memory latency for all
+    float v[SPW][kPerLane];
+    #pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+        const int b = wv + NWAVE * q;
         const float* r1 = r1_given ? r1_given + (size_t)b * E : r + (size_t)(2 * b) * E;
-        float v[kPerLane];
         #pragma unroll
         for (int i = 0; i < kPerLane; ++i) {
             const int e = lane + 64 * i;
-            v[i] = e < E ? r1[e] : -INFINITY;
+            v[q][i] = (b < B && e < E) ? r1[e] : -INFINITY;
         }
+    }
+    #pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+        const int b = wv + NWAVE * q;
+        if (b >= B) break;
         unsigned taken = 0;   // bit i: entry lane + 64 i already ranked
-        int sel[kMaxK];
-        float val[kMaxK];
+        float my_val = -INFINITY;
+        int my_sel = 0;       // lane j ends with rank j's expert and logit
         for (int j = 0; j < kr; ++j) {
             // lane-local best (largest value, then lowest id), then the wave's
             float bv = -INFINITY;
@@ -71,56 +80,71 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route(const float* r, const
             #pragma unroll
             for (int i = 0; i < kPerLane; ++i) {
                 const int e = lane + 64 * i;
-                if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) { bv = v[i]; bi = e; }
+                if (e < E && !((taken >> i) & 1u) && (v[q][i] > bv || bi == 0x7fffffff)) { bv = v[q][i]; bi = e; }
             }
             for (int o = 32; o > 0; o >>= 1) {
                 const float ov = __shfl_xor(bv, o, 64);
                 const int oi = __shfl_xor(bi, o, 64);
                 if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
             }
-            sel[j] = bi;
-            val[j] = bv;
+            if (lane == j) { my_val = bv; my_sel = bi; }
             if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
         }
-        if (lane == 0) {
-            // gates: softmax over each flow's ranks, zero beyond its fan-out
-            float mx = val[0], s = 0.f;
-            for (int j = 1; j < k; ++j) mx = fmaxf(mx, val[j]);
-            float e1[kMaxK];
-            for (int j = 0; j < k; ++j) { e1[j] = expf(val[j] - mx); s += e1[j]; }
-            for (int j = 0; j < kr; ++j) {
-                gates[((size_t)b * 2) * kr + j] = j < k ? e1[j] / s : 0.f;
-                ids[(size_t)b * kr + j] = sel[j];
-                if (ids_out) ids_out[(size_t)b * kr + j] = sel[j];
-            }
-            for (int j = 0; j < kk; ++j) s_ids[b * kk + j] = sel[j];
-            if (nflows == 2) {
-                const float* r2 = r + (size_t)(2 * b + 1) * E;
-                float mx2 = r2[sel[0]], s2 = 0.f;
-                for (int j = 1; j < ka; ++j) mx2 = fmaxf(mx2, r2[sel[j]]);
-                float e2[kMaxK];
-                for (int j = 0; j < ka; ++j) { e2[j] = expf(r2[sel[j]] - mx2); s2 += e2[j]; }
-                for (int j = 0; j < kr; ++j) gates[((size_t)b * 2 + 1) * kr + j] = j < ka ? e2[j] / s2 : 0.f;
-            }
+        // gates: softmax over each flow's ranks (lanes = ranks), zero beyond its fan-out
+        const float top = __shfl(my_val, 0, 64);   // rank 0 holds the largest logit
+        const float e1 = lane < k ? expf(my_val - top) : 0.f;
+        const float s1 = df::wave_sum(e1);
+        if (lane < kr) {
+            gates[((size_t)b * 2) * kr + lane] = lane < k ? e1 / s1 : 0.f;
+            ids[(size_t)b * kr + lane] = my_sel;
+            if (ids_out) ids_out[(size_t)b * kr + lane] = my_sel;
+        }
+        if (lane < kk) s_ids[b * kk + lane] = my_sel;
+        if (nflows == 2) {
+            const float* r2 = r + (size_t)(2 * b + 1) * E;
+            const float l2 = lane < ka ? r2[my_sel] : -INFINITY;
+            const float m2 = df::wave_max(l2);
+            const float e2 = lane < ka ? expf(l2 - m2) : 0.f;
+            const float s2 = df::wave_sum(e2);
+            if (lane < kr) gates[((size_t)b * 2 + 1) * kr + lane] = lane < ka ? e2 / s2 : 0.f;
         }
     }
     __syncthreads();
+    // stable counting sort of the P pairs by expert
     const int P = B * kk;
     for (int e = tid; e < E; e += blockDim.x) {
         int c = 0;
+        #pragma unroll 8
         for (int t = 0; t < P; ++t) c += (s_ids[t] == e);
         s_cnt[e] = c;
     }
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int e = 0; e < E; ++e) { const int c = s_cnt[e]; offsets[e] = acc; s_cnt[e] = acc; acc += c; }
-        offsets[E] = acc;
+    if (wv == 0) {   // exclusive prefix over the experts: 16 per lane, then across lanes
+        int loc[kPerLane], run = 0;
+        #pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = lane * kPerLane + i;
+            loc[i] = run;
+            run += e < E ? s_cnt[e] : 0;
+        }
+        int incl = run;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        const int base = incl - run;
+        #pragma unroll
+        for (int i = 0; i < kPerLane; ++i) {
+            const int e = lane * kPerLane + i;
+            if (e < E) { offsets[e] = base + loc[i]; s_cnt[e] = base + loc[i]; }
+        }
+        if (lane == 63) offsets[E] = incl;
     }
     __syncthreads();
     for (int t = tid; t < P; t += blockDim.x) {
         const int e = s_ids[t];
         int rank = 0;
+        #pragma unroll 8
         for (int u = 0; u < t; ++u) rank += (s_ids[u] == e);
         const int slot = s_cnt[e] + rank;
         perm[slot] = t;
@@ -203,26 +227,68 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
 
 // y_1[b] = sum_{j < k} gate_1[b][j] * y(slot of (b, j))_1, y_2 likewise over
 // j < ka; y2 += c * y1; h += y.
-__global__ __launch_bounds__(256) void moe_combine(const float* y_rows, const float* gates, const int32_t* inv,
-                                                   const float* cpl_c, int d, int k, int ka, int kr, int kk,
-                                                   int nflows, float* h) {
-    const int b = blockIdx.x;
-    for (int n = threadIdx.x; n < d; n += blockDim.x) {
+// One workgroup per sequence: both flows' gate-weighted sums over their
+// ranks (rank order), the c coupling, the residual add; then, with g_next,
+// the LayerNorm of the updated rows into x_next (the next projection's
+// input), the rows being at hand.
+constexpr int kCombThreads = 1024;
+constexpr int kCombCols = 4;   // d <= kCombThreads * kCombCols
+__global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows, const float* gates, const int32_t* inv,
+                                                            const float* cpl_c, int d, int k, int ka, int kr, int kk,
+                                                            int nflows, float* h, const float* g_next, float eps,
+                                                            float* x_next) {
+    __shared__ int s_slot[kMaxK];
+    __shared__ float s_g[2][kMaxK];
+    __shared__ float red[16];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const bool dual = nflows == 2;
+    if (tid < kk) s_slot[tid] = inv[(size_t)b * kk + tid];
+    if (tid < kr) {
+        s_g[0][tid] = gates[((size_t)b * 2) * kr + tid];
+        s_g[1][tid] = dual ? gates[((size_t)b * 2 + 1) * kr + tid] : 0.f;
+    }
+    __syncthreads();
+    float v1[kCombCols], v2[kCombCols];
+    float s1 = 0.f, s2 = 0.f;
+    #pragma unroll
+    for (int c = 0; c < kCombCols; ++c) {
+        const int n = tid + kCombThreads * c;
+        v1[c] = v2[c] = 0.f;
+        if (n >= d) continue;
         float y1 = 0.f, y2 = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const size_t s = inv[(size_t)b * kk + j];
-            y1 = fmaf(gates[((size_t)b * 2) * kr + j], y_rows[(s * 2) * d + n], y1);
-        }
-        if (nflows == 2)
-            for (int j = 0; j < ka; ++j) {
-                const size_t s = inv[(size_t)b * kk + j];
-                y2 = fmaf(gates[((size_t)b * 2 + 1) * kr + j], y_rows[(s * 2 + 1) * d + n], y2);
-            }
-        h[(size_t)(2 * b) * d + n] += y1;
-        if (nflows == 2) {
+        for (int j = 0; j < k; ++j) y1 = fmaf(s_g[0][j], y_rows[((size_t)s_slot[j] * 2) * d + n], y1);
+        if (dual)
+            for (int j = 0; j < ka; ++j) y2 = fmaf(s_g[1][j], y_rows[((size_t)s_slot[j] * 2 + 1) * d + n], y2);
+        float* h1 = h + (size_t)(2 * b) * d + n;
+        v1[c] = *h1 + y1;
+        *h1 = v1[c];
+        s1 += v1[c];
+        if (dual) {
             if (cpl_c) y2 = fmaf(cpl_c[n], y1, y2);   // output coupling c_l
-            h[(size_t)(2 * b + 1) * d + n] += y2;
+            float* h2 = h1 + d;
+            v2[c] = *h2 + y2;
+            *h2 = v2[c];
+            s2 += v2[c];
         }
+    }
+    if (!x_next) return;
+    const float mean1 = df::block_sum(s1, red) / (float)d;
+    const float mean2 = dual ? df::block_sum(s2, red) / (float)d : 0.f;
+    float q1 = 0.f, q2 = 0.f;
+    #pragma unroll
+    for (int c = 0; c < kCombCols; ++c) {
+        if (tid + kCombThreads * c >= d) continue;
+        q1 = fmaf(v1[c] - mean1, v1[c] - mean1, q1);
+        q2 = fmaf(v2[c] - mean2, v2[c] - mean2, q2);
+    }
+    const float rstd1 = 1.0f / sqrtf(df::block_sum(q1, red) / (float)d + eps);
+    const float rstd2 = dual ? 1.0f / sqrtf(df::block_sum(q2, red) / (float)d + eps) : 0.f;
+    #pragma unroll
+    for (int c = 0; c < kCombCols; ++c) {
+        const int n = tid + kCombThreads * c;
+        if (n >= d) continue;
+        x_next[(size_t)(2 * b) * d + n] = (v1[c] - mean1) * rstd1 * g_next[n];
+        if (dual) x_next[(size_t)(2 * b + 1) * d + n] = (v2[c] - mean2) * rstd2 * g_next[n];
     }
 }
 
@@ -263,8 +329,9 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     dn.N = a.d; dn.K = a.Fe; dn.g_out = nullptr; dn.y_out = a.y_rows; dn.up = false;
     e = launch_expert<2>(dn, a.E, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(256), 0, s, a.y_rows, a.gates, a.inv, a.cpl_c, a.d, a.k, ka,
-                       kr, kk, a.nflows, a.h);
+    if (a.d > kCombThreads * kCombCols) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(kCombThreads), 0, s, a.y_rows, a.gates, a.inv, a.cpl_c, a.d, a.k,
+                       ka, kr, kk, a.nflows, a.h, a.g_next, a.eps, a.x_next);
     return hipGetLastError();
 }
 

@@ -70,22 +70,6 @@ __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
     }
 }
 
-__global__ __launch_bounds__(kRowThreads) void ln_rows_kernel(const float* h, const float* g, float eps,
-                                                              int d, int nflows, float* x) {
-    __shared__ float red[16];
-    const int b = blockIdx.x;
-    for (int f = 0; f < nflows; ++f) {
-        const size_t row = (size_t)(2 * b + f) * d;
-        float xv[kMaxPerThread];
-        #pragma unroll
-        for (int k = 0; k < kMaxPerThread; ++k) {
-            const int i = threadIdx.x + k * kRowThreads;
-            xv[k] = i < d ? h[row + i] : 0.f;
-        }
-        ln_store(xv, d, g, eps, x + row, red);
-    }
-}
-
 // x[r] = LN(h[r]; g) from the per-segment statistics of h: block (segment,
 // sequence), thread per column, both flows.
 __global__ __launch_bounds__(kStatSeg) void ln_apply_kernel(const float* h, const float* stats, const float* g,
@@ -268,12 +252,5 @@ hipError_t ln_apply(const float* h, const float* stats, const float* g, float ep
     return hipGetLastError();
 }
 
-hipError_t layer_norm_rows(int dtype, const float* h, const float* g, float eps, int B, int d, int nflows,
-                           void* x, hipStream_t s) {
-    (void)dtype;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(ln_rows_kernel, dim3(B), dim3(kRowThreads), 0, s, h, g, eps, d, nflows, (float*)x);
-    return hipGetLastError();
-}
 
 }  // namespace dfk
