@@ -45,6 +45,7 @@ constexpr int kMaxK = 16;
 constexpr int kRouteThreads = 1024;
 constexpr int kPerLane = 16;   // E <= 64 * kPerLane
 
+template <int NPL>   // logits per lane: E <= 64 NPL
 __global__ __launch_bounds__(kRouteThreads) void moe_route(const float* r, const float* r1_given, int B, int E,
                                                            int k, int ka, int nflows, int32_t* ids, float* gates,
                                                            int32_t* ids_out, int32_t* offsets, int32_t* perm,
@@ -54,55 +55,83 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route(const float* r, const
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     constexpr int NWAVE = kRouteThreads / 64, SPW = 64 / NWAVE;   // sequences per wave (B <= 64)
     const int kr = max(k, ka), kk = nflows == 2 ? kr : k;
-    // every logit row of the wave's sequences first: one memory latency for all
-    float v[SPW][kPerLane];
+    // every logit row of the wave's sequences first (both flows): one memory
+    // latency for all; the SPW sequences are then ranked side by side, so
+    // their shuffle chains overlap
+    float v[SPW][NPL], w2[SPW][NPL];
+    const int nper = (E + 63) / 64;   // logits per lane in use
     #pragma unroll
     for (int q = 0; q < SPW; ++q) {
         const int b = wv + NWAVE * q;
         const float* r1 = r1_given ? r1_given + (size_t)b * E : r + (size_t)(2 * b) * E;
+        const float* r2 = r + (size_t)(2 * b + 1) * E;
         #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+        for (int i = 0; i < NPL; ++i) {
             const int e = lane + 64 * i;
-            v[q][i] = (b < B && e < E) ? r1[e] : -INFINITY;
+            const bool ok = b < B && e < E;
+            v[q][i] = ok ? r1[e] : -INFINITY;
+            w2[q][i] = (ok && nflows == 2) ? r2[e] : -INFINITY;
         }
     }
+    unsigned taken[SPW];
+    float my_val[SPW];
+    int my_sel[SPW];   // lane j ends with rank j's expert and logit
+    #pragma unroll
+    for (int q = 0; q < SPW; ++q) { taken[q] = 0; my_val[q] = -INFINITY; my_sel[q] = 0; }
+    for (int j = 0; j < kr; ++j) {
+        float bv[SPW];
+        int bi[SPW];
+        #pragma unroll
+        for (int q = 0; q < SPW; ++q) {   // lane-local best (largest value, then lowest id)
+            bv[q] = -INFINITY;
+            bi[q] = 0x7fffffff;
+            #pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                const int e = lane + 64 * i;
+                if (i < nper && e < E && !((taken[q] >> i) & 1u) && (v[q][i] > bv[q] || bi[q] == 0x7fffffff)) {
+                    bv[q] = v[q][i];
+                    bi[q] = e;
+                }
+            }
+        }
+        for (int o = 32; o > 0; o >>= 1) {   // the wave's best, SPW chains side by side
+            #pragma unroll
+            for (int q = 0; q < SPW; ++q) {
+                const float ov = __shfl_xor(bv[q], o, 64);
+                const int oi = __shfl_xor(bi[q], o, 64);
+                if (ov > bv[q] || (ov == bv[q] && oi < bi[q])) { bv[q] = ov; bi[q] = oi; }
+            }
+        }
+        #pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+            if (lane == j) { my_val[q] = bv[q]; my_sel[q] = bi[q]; }
+            if ((bi[q] & 63) == lane) taken[q] |= 1u << (bi[q] >> 6);
+        }
+    }
+    // gates: softmax over each flow's ranks (lanes = ranks), zero beyond its fan-out
     #pragma unroll
     for (int q = 0; q < SPW; ++q) {
         const int b = wv + NWAVE * q;
         if (b >= B) break;
-        unsigned taken = 0;   // bit i: entry lane + 64 i already ranked
-        float my_val = -INFINITY;
-        int my_sel = 0;       // lane j ends with rank j's expert and logit
-        for (int j = 0; j < kr; ++j) {
-            // lane-local best (largest value, then lowest id), then the wave's
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            #pragma unroll
-            for (int i = 0; i < kPerLane; ++i) {
-                const int e = lane + 64 * i;
-                if (e < E && !((taken >> i) & 1u) && (v[q][i] > bv || bi == 0x7fffffff)) { bv = v[q][i]; bi = e; }
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-            }
-            if (lane == j) { my_val = bv; my_sel = bi; }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        }
-        // gates: softmax over each flow's ranks (lanes = ranks), zero beyond its fan-out
-        const float top = __shfl(my_val, 0, 64);   // rank 0 holds the largest logit
-        const float e1 = lane < k ? expf(my_val - top) : 0.f;
+        const float top = __shfl(my_val[q], 0, 64);   // rank 0 holds the largest logit
+        const float e1 = lane < k ? expf(my_val[q] - top) : 0.f;
         const float s1 = df::wave_sum(e1);
         if (lane < kr) {
             gates[((size_t)b * 2) * kr + lane] = lane < k ? e1 / s1 : 0.f;
-            ids[(size_t)b * kr + lane] = my_sel;
-            if (ids_out) ids_out[(size_t)b * kr + lane] = my_sel;
+            ids[(size_t)b * kr + lane] = my_sel[q];
+            if (ids_out) ids_out[(size_t)b * kr + lane] = my_sel[q];
         }
-        if (lane < kk) s_ids[b * kk + lane] = my_sel;
+        if (lane < kk) s_ids[b * kk + lane] = my_sel[q];
         if (nflows == 2) {
-            const float* r2 = r + (size_t)(2 * b + 1) * E;
-            const float l2 = lane < ka ? r2[my_sel] : -INFINITY;
+            // the aux logit of rank `lane`'s expert, from the lane holding it
+            float l2 = -INFINITY;
+            #pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                if (i >= nper) break;
+                const float t = __shfl(w2[q][i], my_sel[q] & 63, 64);
+                if ((my_sel[q] >> 6) == i) l2 = t;
+            }
+            l2 = lane < ka ? l2 : -INFINITY;
             const float m2 = df::wave_max(l2);
             const float e2 = lane < ka ? expf(l2 - m2) : 0.f;
             const float s2 = df::wave_sum(e2);
@@ -312,7 +341,8 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     const int kr = std::max(a.k, ka), kk = a.nflows == 2 ? kr : a.k;
     if (kr > kMaxK || a.B > 64 || a.E > 64 * kPerLane || a.dtype != DF_BF16) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(moe_route, dim3(1), dim3(kRouteThreads), 0, s, a.r, a.r1_given, a.B, a.E, a.k, ka, a.nflows,
+    const auto route = a.E <= 64 ? moe_route<1> : a.E <= 256 ? moe_route<4> : moe_route<kPerLane>;
+    hipLaunchKernelGGL(route, dim3(1), dim3(kRouteThreads), 0, s, a.r, a.r1_given, a.B, a.E, a.k, ka, a.nflows,
                        a.ids, a.gates, a.ids_out, a.offsets, a.perm, a.inv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

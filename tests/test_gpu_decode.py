@@ -259,3 +259,23 @@ def test_moe_aux_fanout_leaves_primary_bitwise():
         assert torch.equal(a.logits[:, 0], b.logits[:, 0])
         assert torch.equal(a.expert_ids, b.expert_ids)
     assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+
+
+@pytest.mark.parametrize("E", [128, 320], ids=["e128", "e320"])
+def test_moe_routing_many_experts(E):
+    """Routing with more experts than lanes (2 and 5 logits per lane of the
+    ranking wave): ranking bit-exact, outputs within the bars."""
+    cfg = SMALL_MOE.replace(name=f"gpu_moe_e{E}", E=E, top_k_aux=8)
+    say(f"moe routing E={E}")
+    gm = DecodeModel(cfg, fill="host")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    for step in range(2):
+        tok = src.step_tokens(step)
+        rl = gm.router_logits(step)
+        gm.decode_step(gm.tokens(tok), router_logits=rl)
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True, router_logits=rl.cpu().numpy())
+        assert np.array_equal(gm.expert_ids.cpu().numpy(), r.ids), "expert ranking differs"
+        _compare_step(cfg, gm, r)
