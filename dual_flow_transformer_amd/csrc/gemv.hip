@@ -516,8 +516,13 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M) {
     if (dtype != DF_BF16 || M < 1 || M > 128 || N < 16 || N % 16 || K < 256 || K % 256) return pl;
     const int mt = (M + 15) / 16;
     pl.MT = mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
-    pl.variant = (pl.MT <= 2 && N < 8192) ? VAR_B : VAR_A;
-    const int ks_max = pl.variant == VAR_B ? 512 : (pl.MT <= 2 ? 1024 : pl.MT == 4 ? 512 : 256);
+    // shapes from a plan sweep on the box (weights rotated past the MALL):
+    // 32-row tiles up to 16M weights or below 8192 rows, 256-wide k slices for
+    // the smallest matrices
+    const long nk = (long)N * K;
+    pl.variant = (pl.MT <= 2 && (N < 8192 || nk <= (16L << 20))) ? VAR_B : VAR_A;
+    const int ks_max = pl.variant == VAR_B ? (nk <= (4L << 20) ? 256 : 512)
+                                           : (pl.MT <= 2 ? 1024 : pl.MT == 4 ? 512 : 256);
     int ks = 256;
     for (int c = ks_max; c >= 256; c /= 2)
         if (K % c == 0) { ks = c; break; }
@@ -527,7 +532,7 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M) {
     // one or two resident workgroups per CU (LDS permitting), split over the
     // k-slices; no more row groups than row tiles
     const size_t lds_static = (size_t)ks * 4 + 2 * 16 * pl.MT * 4;   // gains, row mean and rstd
-    const int wg_per_cu = pl.lds + lds_static <= 80 * 1024 ? 2 : 1;
+    const int wg_per_cu = pl.variant == VAR_A && pl.lds + lds_static <= 80 * 1024 ? 2 : 1;
     const int rt = pl.variant == VAR_B ? 2 : 1;
     const int n_tiles = (N + 16 * rt - 1) / (16 * rt);
     int ngrp = std::max(1, kCUs * wg_per_cu / pl.S);
