@@ -31,10 +31,10 @@ PEAK_HBM_GBS = 8000.0
 # write). Reported only while the kernel sources are the ones they were measured on.
 COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "4140c1ef04b656a90ad4e2cace72ce53214a667ef07bf0258373feedd5521a7d",
-    "attention_traffic_bytes_per_launch": 2.1524e9,
-    "library_sources_sha256": "b935a3c7ed15e071b646e00936122e74d9939f0e36d5d981a7030cb266c4e333",
-    "step_traffic_bytes": {"dual": 84.842e9, "primary_only": 83.382e9},
+    "attention_source_sha256": "210e88f75d16717f5d313f6fc42d3b4666ff6fffcbfd0d5e3abe19e6e09d442e",
+    "attention_traffic_bytes_per_launch": 2.1532e9,
+    "library_sources_sha256": "2f8b57b821d0134e14040f4519b09eb28cfa7895d84f0a74e6d2bf73f4da150a",
+    "step_traffic_bytes": {"dual": 84.880e9, "primary_only": 83.405e9},
 }
 
 
