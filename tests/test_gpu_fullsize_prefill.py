@@ -1,0 +1,116 @@
+"""Full-size prefill and dual forward: 16 sequences x 2048 tokens through the
+dense 1.3B model, in the launch configuration the benchmark times (default
+chunk rows: two prefill chunks of 1024 positions, four forward chunks of 512).
+
+The oracle recomputes sampled cache entries one by one: for a sampled
+sequence it forms every layer-0 K/V of the prompt (one matrix product), then
+for sampled positions p the layer-0 attention over 0..p, the MLP and the
+layer-1 K/V at p. Bars as in the small prefill tests: one bf16 ulp + 5e-4,
+plus 3 D_1 in layer 1 (D_1 measured on the oracle with every layer-0 K/V
+value perturbed by a seeded relative +-2^-17 before its rounding). The dual
+forward's primary half is the prefill computed by the same kernels row by
+row, so its cache must equal the prefill's bit for bit (a property at any
+size); its p_mix rows must sum to 1 and alpha lie in [0.5, 1]."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from dual_flow_transformer_amd.runtime import DecodeModel
+from gpu_util import bits_to_f64, say
+from oracle import dualflow as odf
+from synth.workloads import FORWARD_DENSE, PREFILL_DENSE, Inputs
+
+pytestmark = pytest.mark.gpu
+KV_ABS = 5e-4
+SEQS = [0, 15]
+POS = [0, 1, 511, 512, 1023, 1024, 2047]
+
+
+def _oracle_sampled(cfg, src, toks, perturb):
+    """{(layer, position): (K [H, Dh], V [H, Dh])} for layers 0 and 1."""
+    m = odf.Model(src, keep_layers=True)
+    d, H, Dh, T = cfg.d, cfg.H, cfg.Dh, len(toks)
+    rng = np.random.default_rng(cfg.seed)
+
+    def rnd(x):
+        if perturb:
+            x = x * (1.0 + rng.uniform(-2.0 ** -17, 2.0 ** -17, np.shape(x)))
+        return odf.round_to(x, cfg.dtype)
+
+    p0, p1 = m.layer(0), m.layer(1)
+    h = m.emb(0, toks) + m.pos(np.arange(T))
+    qkv = odf.layer_norm(h, p0["ln1"], cfg.eps) @ p0["w_qkv"].T
+    K0 = rnd(qkv[:, d:2 * d]).reshape(T, H, Dh)
+    V0 = rnd(qkv[:, 2 * d:]).reshape(T, H, Dh)
+    out = {}
+    for p in POS:
+        out[(0, p)] = (K0[p], V0[p])
+        o = np.concatenate([odf.attention_one(qkv[p, hh * Dh:(hh + 1) * Dh], K0[:p + 1, hh], V0[:p + 1, hh])[0]
+                            for hh in range(H)])
+        x = h[p] + p0["w_o"] @ o
+        v = odf.layer_norm(x, p0["ln2"], cfg.eps)
+        x = x + p0["w_down"] @ odf.gelu(p0["w_up"] @ v)
+        q1 = p1["w_qkv"] @ odf.layer_norm(x, p1["ln1"], cfg.eps)
+        out[(1, p)] = (odf.round_to(q1[d:2 * d], cfg.dtype).reshape(H, Dh),
+                       odf.round_to(q1[2 * d:], cfg.dtype).reshape(H, Dh))
+    return out
+
+
+def _excess(got, want):
+    return np.abs(got - want) - 2.0 ** -7 * np.abs(want)
+
+
+def test_prefill_full_size_sampled():
+    cfg = PREFILL_DENSE
+    say(f"full-size prefill {cfg.name}")
+    src = Inputs(cfg)
+    prompt = src.prompt()
+    gm = DecodeModel(cfg, fill="device")
+    gm.len.zero_()
+    gm.prefill(gm.tokens(prompt).contiguous())
+    torch.cuda.synchronize()
+    assert gm.status() == 0
+    assert torch.all(gm.len == cfg.prompt_len)
+    got = {(l, b): (gm.k[l, b].cpu(), gm.v[l, b].cpu()) for l in (0, 1) for b in SEQS}
+    del gm
+    torch.cuda.empty_cache()
+    for b in SEQS:
+        say(f"  oracle, sequence {b}")
+        ref = _oracle_sampled(cfg, src, prompt[b], False)
+        alt = _oracle_sampled(cfg, src, prompt[b], True)
+        d1 = max(_excess(alt[(1, p)][i], ref[(1, p)][i]).max() for p in POS for i in (0, 1))
+        say(f"  D_1 = {d1:.2e}")
+        for (l, p), (kr, vr) in ref.items():
+            for i, want in enumerate((kr, vr)):
+                g = bits_to_f64(got[(l, b)][i][:, p], cfg.dtype)
+                err = _excess(g, want) - (KV_ABS + (3 * d1 if l else 0.0))
+                assert np.all(err <= 0), f"l={l} b={b} p={p} {'kv'[i]}: worst excess {err.max():.3e}"
+
+
+def test_forward_full_size_primary_is_prefill():
+    cfg = FORWARD_DENSE
+    say(f"full-size dual forward {cfg.name}")
+    toks = Inputs(cfg).prompt()
+    a = DecodeModel(cfg, fill="device")
+    a.len.zero_()
+    _, pm, al, nt = a.forward(a.tokens(toks).contiguous(), logits=False)
+    torch.cuda.synchronize()
+    assert a.status() == 0
+    s = pm.sum(dim=-1)
+    assert torch.all((s - 1).abs() < 1e-4), f"p_mix sums {s.min().item()}..{s.max().item()}"
+    assert torch.all((al >= 0.5) & (al <= 1.0))
+    assert torch.equal(nt.long(), pm.argmax(dim=-1))
+    del pm, al, nt
+    k_fw, v_fw = a.k.clone(), a.v.clone()
+    del a
+    torch.cuda.empty_cache()
+    b = DecodeModel(PREFILL_DENSE, fill="device")
+    b.len.zero_()
+    b.prefill(b.tokens(toks).contiguous())
+    torch.cuda.synchronize()
+    same_k = torch.equal(k_fw, b.k)
+    same_v = torch.equal(v_fw, b.v)
+    say(f"  cache bitwise equal: K {same_k} V {same_v}")
+    assert same_k and same_v
