@@ -116,6 +116,26 @@ def test_other_entry_points_reject_bad_arguments():
     kv = _abi.df_kv(0x20000, 0x30000, 0x40000)
     assert _abi.df_prefill_primary(cfg, fake_weights(), kv, None, 4, 0x80000, 1 << 40) == _abi.DF_ERR_NULL
     assert _abi.df_prefill_primary(cfg, fake_weights(), kv, 0x50000, 65, 0x80000, 1 << 40) == _abi.DF_ERR_SHAPE
+    ws = 0x80000
+    pw = _abi.df_prefill_workspace_bytes(cfg)
+    assert _abi.df_prefill_primary(cfg, fake_weights(), kv, 0x50000, 4, ws, pw - 256) == _abi.DF_ERR_WORKSPACE
+    assert _abi.df_prefill_primary(cfg, fake_weights(), kv, 0x50000, -1, ws, pw) == _abi.DF_ERR_SHAPE
+    # full-sequence dual forward: host checks before any launch
+    fw = _abi.df_forward_workspace_bytes(cfg)
+    assert fw >= _abi.df_workspace_bytes(cfg)
+    f = lambda **k: _abi.df_forward_dual(k.get("cfg", cfg), fake_weights(), kv, k.get("tok", 0x50000), k.get("T", 4),
+                                         k.get("lg", None), k.get("pm", 0x60000), k.get("al", 0x70000), None,
+                                         k.get("ws", ws), k.get("wsb", fw))
+    assert f(tok=None) == _abi.DF_ERR_NULL
+    assert f(pm=None) == _abi.DF_ERR_NULL
+    assert f(al=None) == _abi.DF_ERR_NULL
+    assert f(T=65) == _abi.DF_ERR_SHAPE
+    assert f(T=-1) == _abi.DF_ERR_SHAPE
+    assert f(lg=0x90008) == _abi.DF_ERR_ALIGN
+    assert f(pm=0x60008) == _abi.DF_ERR_ALIGN
+    assert f(ws=0x80010) == _abi.DF_ERR_ALIGN
+    assert f(wsb=fw - 256) == _abi.DF_ERR_WORKSPACE
+    assert f(cfg=good_config(dtype=7)) == _abi.DF_ERR_DTYPE
     assert _abi.df_kv_append(cfg, kv, 2, 0x1000, 0x2000, 0x3000) == _abi.DF_ERR_SHAPE
     assert _abi.df_kv_append(cfg, kv, 0, None, 0x2000, 0x3000) == _abi.DF_ERR_NULL
     assert _abi.df_mix_head(None, 1, 10, 1, 0x1000, 0x2000) == _abi.DF_ERR_NULL
