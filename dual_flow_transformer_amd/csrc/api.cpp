@@ -22,7 +22,7 @@ typedef char* bf16p;   // byte pointer into bf16 hi / lo planes
 
 // Workspace regions (byte offsets from the workspace base).
 struct WsLayout {
-    size_t status, h, xd, xo, xf, q, part, logits, r, ids, gates, offsets, perm, inv, grows, yrows, gpart, gcount,
+    size_t status, h, xd, xo, xf, q, part, logits, ids, gates, grows, yrows, gpart, gcount,
         stats, total;
 };
 
@@ -30,7 +30,7 @@ struct WsLayout {
 void gemv_scratch(const df_config& c, size_t* part_floats, size_t* blocks) {
     const bool moe = c.n_experts > 0;
     const int d = c.d_model;
-    const int shapes[5][2] = {{3 * d, d}, {d, d}, {moe ? c.n_experts : c.ffn, d}, {d, moe ? 0 : c.ffn},
+    const int shapes[5][2] = {{3 * d, d}, {d, d}, {moe ? 0 : c.ffn, d}, {d, moe ? 0 : c.ffn},
                               {c.vocab, d}};
     *part_floats = 0;
     *blocks = 0;
@@ -61,12 +61,8 @@ WsLayout layout(const df_config& c) {
     L.q = take(M * c.d_model * 4);
     L.part = take(dfk::attention_part_floats(c.batch, c.n_heads, c.max_seq, c.head_dim) * 4);
     L.logits = take(M * (size_t)c.vocab * 4);
-    L.r = take(moe ? M * c.n_experts * 4 : 0);
     L.ids = take(P * 4);
     L.gates = take(P * 2 * 4);
-    L.offsets = take(moe ? (size_t)(c.n_experts + 1) * 4 : 0);
-    L.perm = take(P * 4);
-    L.inv = take(P * 4);
     L.grows = take(P * 2 * (size_t)c.expert_ffn * 4);
     L.yrows = take(P * 2 * (size_t)c.d_model * 4);
     size_t gp = 0, gb = 0;
@@ -332,28 +328,23 @@ struct Step {
                 pending = true;
                 if (!apply_norm(g_next)) return DF_ERR_HIP;
             } else {
-                // router and experts read LN2(h) rows
-                if (dfk::ln_apply(h, stats, g_ln2, c.ln_eps, B, d, nflows, xd, s) != hipSuccess) return DF_ERR_HIP;
-                pending = false;
+                // one kernel per sequence normalises the rows (LN2) and routes them
                 const int E = c.n_experts;
-                g.x = xd; g.x_stats = nullptr; g.x_gain = nullptr;
-                g.w = reinterpret_cast<const char*>(w.w_router) + (size_t)l * E * d * es;
-                g.N = E; g.K = d; g.epi = dfk::EPI_STORE; g.out_f32 = at<float>(L.r);
-                if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
                 dfk::MoeArgs m{};
-                m.dtype = c.dtype; m.x = xd; m.r = at<float>(L.r);
+                m.dtype = c.dtype; m.h = h; m.stats = stats; m.g_ln = g_ln2;
+                m.w_router = reinterpret_cast<const char*>(w.w_router) + (size_t)l * E * d * es;
                 m.r1_given = router_logits ? router_logits + (size_t)l * B * E : nullptr;
                 m.w_up = reinterpret_cast<const char*>(w.w_exp_up) + (size_t)l * E * ffn * d * es;
                 m.w_down = reinterpret_cast<const char*>(w.w_exp_down) + (size_t)l * E * d * ffn * es;
                 m.cpl_b = cb; m.cpl_c = cc; m.B = B; m.d = d; m.E = E; m.k = c.top_k; m.Fe = (int)ffn;
                 m.ka = c.top_k_aux > 0 ? c.top_k_aux : c.top_k;
-                m.nflows = nflows; m.h = h;
+                m.nflows = nflows;
                 m.ids_out = expert_ids ? expert_ids + (size_t)l * B * kr : nullptr;
-                m.ids = at<int32_t>(L.ids); m.gates = at<float>(L.gates); m.offsets = at<int32_t>(L.offsets);
-                m.perm = at<int32_t>(L.perm); m.inv = at<int32_t>(L.inv); m.g_rows = at<float>(L.grows);
+                m.x = xd; m.ids = at<int32_t>(L.ids); m.gates = at<float>(L.gates); m.g_rows = at<float>(L.grows);
                 m.y_rows = at<float>(L.yrows);
                 m.g_next = g_next; m.eps = c.ln_eps; m.x_next = xd;   // next norm fused into the combine
                 if (dfk::moe(m, s) != hipSuccess) return DF_ERR_HIP;
+                pending = false;
             }
         }
         if (head) {

@@ -178,8 +178,10 @@ hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_
 // ---------------------------------------------------------------------------
 struct MoeArgs {
     int dtype;
-    const float* x;         // [2B][d] LN2(h) rows (fp32)
-    const float* r;         // [2B][E] router logits (computed)
+    float* h;               // [2B][d] residual rows: normalised for the router, then updated
+    const float* stats;     // per-segment statistics of h
+    const float* g_ln;      // gain of the norm before the MoE MLP
+    const void* w_router;   // [E][d] (fragment layout)
     const float* r1_given;  // [B][E] primary logits supplied, or nullptr
     const void* w_up;       // [E][Fe][d]  (fragment layout per expert)
     const void* w_down;     // [E][d][Fe]  (fragment layout per expert)
@@ -189,17 +191,14 @@ struct MoeArgs {
     int ka;                 // aux fan-out: first ka experts of the primary ranking
     float eps;
     const float* g_next;    // gain of the next norm
-    float* h;               // [2B][d] residual (updated)
     float* x_next;          // [2B][d] LN(h; g_next)
     int32_t* ids_out;       // [B][max(k, ka)] or nullptr
-    // workspace (kr = max(k, ka) ranks per sequence)
+    // workspace (kr = max(k, ka) ranks per sequence, kk of them in use)
+    float* x;               // [2B][d] LN(h; g_ln) rows (the experts' input)
     int32_t* ids;           // [B][kr]
     float* gates;           // [B][2][kr], zero beyond a flow's fan-out
-    int32_t* offsets;       // [E+1]
-    int32_t* perm;          // [B*kr]: sorted slot -> b*kk + j (kk ranks in use)
-    int32_t* inv;           // [B*kr]: b*kk + j -> sorted slot
-    float* g_rows;          // [B*kr][2][Fe] fp32
-    float* y_rows;          // [B*kr][2][d]
+    float* g_rows;          // [B*kk][2][Fe] fp32, row 2 (b kk + j) + f
+    float* y_rows;          // [B*kk][2][d]
 };
 hipError_t moe(const MoeArgs& a, hipStream_t s);
 

@@ -3,21 +3,22 @@
 // aux flow reuses the set of experts the primary router picked, applying
 // them with its own mixture weights).
 //
-// 1. moe_route (one workgroup): the primary ranking per sequence
-//    (descending logit, ties to the lower expert id), softmax gates of each
-//    flow over its fan-out (k primary ranks; the aux flow may take more or
-//    fewer of the primary's ranks: independent fan-outs, "Contribuciones
-//    Clave" item 3), then a stable counting sort of the (sequence, rank)
-//    pairs by expert: offsets[E+1], perm (sorted slot -> pair), inv.
+// 1. moe_gate (one workgroup per sequence): LayerNorm of the sequence's
+//    stacked rows, the router logits of each row, the primary ranking
+//    (descending logit, ties to the lower expert id) and the softmax gates
+//    of each flow over its fan-out (k primary ranks; the aux flow may take
+//    more or fewer of the primary's ranks: independent fan-outs,
+//    "Contribuciones Clave" item 3).
 // 2. moe_expert (up): one workgroup per (expert, 32 rows of the expert FFN);
-//    the expert's stacked rows are the primary and aux rows of its pairs, so
-//    each touched expert's weights are read once for both flows; untouched
-//    experts exit without reading. Epilogue: GELU, then the b coupling on the
-//    aux row where the primary also ran that expert.
+//    it finds the (sequence, rank) pairs that chose its expert, in pair
+//    order, and stacks their primary and aux rows, so each touched expert's
+//    weights are read once for both flows; untouched experts exit without
+//    reading. Epilogue: GELU, then the b coupling on the aux row where the
+//    primary also ran that expert. Outputs are indexed by pair.
 // 3. moe_expert (down): same grouping over the expert's down projection.
 // 4. moe_combine: gate-weighted sum over each flow's ranks in rank order, c
 //    coupling on the aux output, residual add, then the next LayerNorm of the
-//    updated rows. Integer work (ids, offsets, perm) is exact; no atomics.
+//    updated rows. Integer work (ids, pair lists) is exact; no atomics.
 #include <algorithm>
 
 #include "df_device.h"
@@ -29,176 +30,218 @@ namespace dfk {
 namespace {
 
 using tile::f32x4;
+using tile::u32x4;
 using tile::RT;
 using tile::ROWS;
 
 constexpr int kMaxK = 16;
-
-// Routing: the primary ranking (top-kr of the primary router logits by
-// descending value, ties to the lower id), gates of each flow over its
-// fan-out (primary: the first k ranks, aux: the first ka), then a stable
-// counting sort of the (sequence, rank) pairs in use by expert. kk ranks per
-// sequence are in use: kr with both flows, k for the primary alone.
-// One workgroup of 1024 threads: wave w ranks sequences w, w + 16, ... by kr
-// rounds of a wave-wide argmax over the logits held in registers (E <= 1024,
-// 16 per lane); then thread e counts expert e's pairs, thread t places pair t.
-constexpr int kRouteThreads = 1024;
 constexpr int kPerLane = 16;   // E <= 64 * kPerLane
 
+// Router of one sequence per workgroup: LayerNorm of its stacked rows from
+// their per-segment statistics (to x, the experts' input, and to LDS), the
+// router logits of each row, then on wave 0 the primary ranking (kr rounds
+// of a wave-wide argmax over the logits held in registers, NPL per lane)
+// and the gates of both flows. Logits: item (16-expert group g, k-split q)
+// goes to one wave, whose lane l reads 16 B of each 1 KiB weight fragment
+// of the item (expert 16 g + l % 16, k = 32 kb + 8 (l / 16) + i); all of a
+// wave's weight loads are issued before the LayerNorm, so the two overlap.
+// The four lanes of an expert, then its k-splits in order, are added.
+struct GateParams {
+    const float* h;          // [2B][d] residual rows
+    const float* stats;      // their per-segment statistics
+    const float* g;          // LN gain [d]
+    float eps;
+    int d, E, k, ka, kr, nflows;
+    int ns;                  // k-splits per 16-expert group
+    const bf16_t* wr;        // router [E][d], fragment layout
+    const float* r1_given;   // [B][E] primary logits supplied, or nullptr
+    float* x;                // [2B][d] LN(h) rows
+    int32_t* ids;            // [B][kr]
+    float* gates;            // [B][2][kr], zero beyond a flow's fan-out
+    int32_t* ids_out;        // [B][kr] or nullptr
+};
+constexpr int kGateThreads = 1024;
+constexpr int kGateWaves = kGateThreads / 64;
+constexpr int kGateFrags = 16;   // weight fragments per lane in flight
+
 template <int NPL>   // logits per lane: E <= 64 NPL
-__global__ __launch_bounds__(kRouteThreads) void moe_route(const float* r, const float* r1_given, int B, int E,
-                                                           int k, int ka, int nflows, int32_t* ids, float* gates,
-                                                           int32_t* ids_out, int32_t* offsets, int32_t* perm,
-                                                           int32_t* inv) {
-    __shared__ int32_t s_ids[64 * kMaxK];
-    __shared__ int32_t s_cnt[1024];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    constexpr int NWAVE = kRouteThreads / 64, SPW = 64 / NWAVE;   // sequences per wave (B <= 64)
-    const int kr = max(k, ka), kk = nflows == 2 ? kr : k;
-    // every logit row of the wave's sequences first (both flows): one memory
-    // latency for all; the SPW sequences are then ranked side by side, so
-    // their shuffle chains overlap
-    float v[SPW][NPL], w2[SPW][NPL];
-    const int nper = (E + 63) / 64;   // logits per lane in use
-    #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        const int b = wv + NWAVE * q;
-        const float* r1 = r1_given ? r1_given + (size_t)b * E : r + (size_t)(2 * b) * E;
-        const float* r2 = r + (size_t)(2 * b + 1) * E;
+__global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
+    extern __shared__ float s_x[];   // [2][d] normalised rows, then [2][E / 16][ns][16] logit parts
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int d = p.d, E = p.E, nseg = stat_segs(d), KB = d / 32, ns = p.ns, kbs = KB / ns;
+    const int items = (E / 16) * ns;
+    float* s_part = s_x + 2 * d;
+    const bool dual = p.nflows == 2;
+    // first chunk of the wave's first item: loads in flight during the norm
+    int it = wv;
+    u32x4 w[kGateFrags];
+    auto load = [&](int item, int kb0) {
+        const int grp = min(item, items - 1) / ns;
+        const int q = min(item, items - 1) - grp * ns;
+        const bf16_t* wp = p.wr + ((size_t)(grp * KB + q * kbs) * 64 + lane) * 8;
         #pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const int e = lane + 64 * i;
-            const bool ok = b < B && e < E;
-            v[q][i] = ok ? r1[e] : -INFINITY;
-            w2[q][i] = (ok && nflows == 2) ? r2[e] : -INFINITY;
+        for (int u = 0; u < kGateFrags; ++u)
+            w[u] = *reinterpret_cast<const u32x4*>(wp + (size_t)min(kb0 + u, kbs - 1) * 512);
+    };
+    load(it, 0);
+    for (int f = 0; f < p.nflows; ++f) {
+        const int row = 2 * b + f;
+        const float2 mr = df::row_norm_from_segments(reinterpret_cast<const float2*>(p.stats) + (size_t)row * nseg,
+                                                     nseg, kStatSeg, d, p.eps);
+        for (int k = tid * 4; k < d; k += kGateThreads * 4) {
+            const float4 hv = *reinterpret_cast<const float4*>(p.h + (size_t)row * d + k);
+            const float4 gv = *reinterpret_cast<const float4*>(p.g + k);
+            const float4 v = make_float4((hv.x - mr.x) * mr.y * gv.x, (hv.y - mr.x) * mr.y * gv.y,
+                                         (hv.z - mr.x) * mr.y * gv.z, (hv.w - mr.x) * mr.y * gv.w);
+            *reinterpret_cast<float4*>(p.x + (size_t)row * d + k) = v;
+            *reinterpret_cast<float4*>(s_x + f * d + k) = v;
         }
     }
-    unsigned taken[SPW];
-    float my_val[SPW];
-    int my_sel[SPW];   // lane j ends with rank j's expert and logit
-    #pragma unroll
-    for (int q = 0; q < SPW; ++q) { taken[q] = 0; my_val[q] = -INFINITY; my_sel[q] = 0; }
-    for (int j = 0; j < kr; ++j) {
-        float bv[SPW];
-        int bi[SPW];
-        #pragma unroll
-        for (int q = 0; q < SPW; ++q) {   // lane-local best (largest value, then lowest id)
-            bv[q] = -INFINITY;
-            bi[q] = 0x7fffffff;
+    __syncthreads();
+    for (; it < items; it += kGateWaves) {
+        const int grp = it / ns, q = it - (it / ns) * ns;
+        const float* x1 = s_x + 32 * q * kbs + 8 * (lane >> 4);
+        const float* x2 = x1 + d;
+        float a1 = 0.f, a2 = 0.f;
+        for (int kb0 = 0; kb0 < kbs; kb0 += kGateFrags) {
+            if (kb0 > 0) load(it, kb0);
             #pragma unroll
-            for (int i = 0; i < NPL; ++i) {
-                const int e = lane + 64 * i;
-                if (i < nper && e < E && !((taken[q] >> i) & 1u) && (v[q][i] > bv[q] || bi[q] == 0x7fffffff)) {
-                    bv[q] = v[q][i];
-                    bi[q] = e;
+            for (int u = 0; u < kGateFrags; ++u) {
+                if (kb0 + u >= kbs) break;
+                const int kb = kb0 + u;
+                const float wf[8] = {df::bf16_lo(w[u][0]), df::bf16_hi(w[u][0]), df::bf16_lo(w[u][1]),
+                                     df::bf16_hi(w[u][1]), df::bf16_lo(w[u][2]), df::bf16_hi(w[u][2]),
+                                     df::bf16_lo(w[u][3]), df::bf16_hi(w[u][3])};
+                #pragma unroll
+                for (int i = 0; i < 8; ++i) a1 = fmaf(wf[i], x1[32 * kb + i], a1);
+                if (dual) {
+                    #pragma unroll
+                    for (int i = 0; i < 8; ++i) a2 = fmaf(wf[i], x2[32 * kb + i], a2);
                 }
             }
         }
-        for (int o = 32; o > 0; o >>= 1) {   // the wave's best, SPW chains side by side
-            #pragma unroll
-            for (int q = 0; q < SPW; ++q) {
-                const float ov = __shfl_xor(bv[q], o, 64);
-                const int oi = __shfl_xor(bi[q], o, 64);
-                if (ov > bv[q] || (ov == bv[q] && oi < bi[q])) { bv[q] = ov; bi[q] = oi; }
+        a1 += __shfl_xor(a1, 16, 64);
+        a1 += __shfl_xor(a1, 32, 64);
+        a2 += __shfl_xor(a2, 16, 64);
+        a2 += __shfl_xor(a2, 32, 64);
+        if (lane < 16) {
+            s_part[(grp * ns + q) * 16 + lane] = a1;
+            s_part[(items + grp * ns + q) * 16 + lane] = a2;
+        }
+        if (it + kGateWaves < items) load(it + kGateWaves, 0);
+    }
+    __syncthreads();
+    // logits of both rows (k-splits in order) into the first 2 E floats of
+    // LDS, once every part has been read (E <= kGateThreads)
+    float l1 = 0.f, l2 = 0.f;
+    const int e = tid;
+    if (e < E) {
+        const int grp = e / 16, j = e - (e / 16) * 16;
+        for (int q = 0; q < ns; ++q) {
+            l1 += s_part[(grp * ns + q) * 16 + j];
+            l2 += s_part[(items + grp * ns + q) * 16 + j];
+        }
+    }
+    __syncthreads();
+    float* s_r = s_x;
+    if (e < E) { s_r[e] = l1; s_r[E + e] = l2; }
+    __syncthreads();
+    if (wv != 0) return;
+    const float* r1 = p.r1_given ? p.r1_given + (size_t)b * E : s_r;
+    float v[NPL];
+    #pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? r1[e] : -INFINITY;
+    }
+    unsigned taken = 0;
+    float my_val = -INFINITY;
+    int my_sel = 0;   // lane j ends with rank j's expert and logit
+    for (int j = 0; j < p.kr; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        #pragma unroll
+        for (int i = 0; i < NPL; ++i) {   // lane-local best (largest value, then lowest id)
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
+                bv = v[i];
+                bi = e;
             }
         }
-        #pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-            if (lane == j) { my_val[q] = bv[q]; my_sel[q] = bi[q]; }
-            if ((bi[q] & 63) == lane) taken[q] |= 1u << (bi[q] >> 6);
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
         }
+        if (lane == j) { my_val = bv; my_sel = bi; }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     }
     // gates: softmax over each flow's ranks (lanes = ranks), zero beyond its fan-out
-    #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        const int b = wv + NWAVE * q;
-        if (b >= B) break;
-        const float top = __shfl(my_val[q], 0, 64);   // rank 0 holds the largest logit
-        const float e1 = lane < k ? expf(my_val[q] - top) : 0.f;
-        const float s1 = df::wave_sum(e1);
-        if (lane < kr) {
-            gates[((size_t)b * 2) * kr + lane] = lane < k ? e1 / s1 : 0.f;
-            ids[(size_t)b * kr + lane] = my_sel[q];
-            if (ids_out) ids_out[(size_t)b * kr + lane] = my_sel[q];
-        }
-        if (lane < kk) s_ids[b * kk + lane] = my_sel[q];
-        if (nflows == 2) {
-            // the aux logit of rank `lane`'s expert, from the lane holding it
-            float l2 = -INFINITY;
-            #pragma unroll
-            for (int i = 0; i < NPL; ++i) {
-                if (i >= nper) break;
-                const float t = __shfl(w2[q][i], my_sel[q] & 63, 64);
-                if ((my_sel[q] >> 6) == i) l2 = t;
-            }
-            l2 = lane < ka ? l2 : -INFINITY;
-            const float m2 = df::wave_max(l2);
-            const float e2 = lane < ka ? expf(l2 - m2) : 0.f;
-            const float s2 = df::wave_sum(e2);
-            if (lane < kr) gates[((size_t)b * 2 + 1) * kr + lane] = lane < ka ? e2 / s2 : 0.f;
-        }
+    const float top = __shfl(my_val, 0, 64);   // rank 0 holds the largest logit
+    const float e1 = lane < p.k ? expf(my_val - top) : 0.f;
+    const float s1 = df::wave_sum(e1);
+    if (lane < p.kr) {
+        p.gates[((size_t)b * 2) * p.kr + lane] = lane < p.k ? e1 / s1 : 0.f;
+        p.ids[(size_t)b * p.kr + lane] = my_sel;
+        if (p.ids_out) p.ids_out[(size_t)b * p.kr + lane] = my_sel;
     }
-    __syncthreads();
-    // stable counting sort of the P pairs by expert
-    const int P = B * kk;
-    for (int e = tid; e < E; e += blockDim.x) {
-        int c = 0;
-        #pragma unroll 8
-        for (int t = 0; t < P; ++t) c += (s_ids[t] == e);
-        s_cnt[e] = c;
-    }
-    __syncthreads();
-    if (wv == 0) {   // exclusive prefix over the experts: 16 per lane, then across lanes
-        int loc[kPerLane], run = 0;
-        #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = lane * kPerLane + i;
-            loc[i] = run;
-            run += e < E ? s_cnt[e] : 0;
-        }
-        int incl = run;
-        for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
-        }
-        const int base = incl - run;
-        #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = lane * kPerLane + i;
-            if (e < E) { offsets[e] = base + loc[i]; s_cnt[e] = base + loc[i]; }
-        }
-        if (lane == 63) offsets[E] = incl;
-    }
-    __syncthreads();
-    for (int t = tid; t < P; t += blockDim.x) {
-        const int e = s_ids[t];
-        int rank = 0;
-        #pragma unroll 8
-        for (int u = 0; u < t; ++u) rank += (s_ids[u] == e);
-        const int slot = s_cnt[e] + rank;
-        perm[slot] = t;
-        inv[t] = slot;
+    if (dual) {
+        // the aux router's logit of rank `lane`'s expert
+        const float l2 = lane < p.ka ? s_r[E + my_sel] : -INFINITY;
+        const float m2 = df::wave_max(l2);
+        const float e2 = lane < p.ka ? expf(l2 - m2) : 0.f;
+        const float s2 = df::wave_sum(e2);
+        if (lane < p.kr) p.gates[((size_t)b * 2 + 1) * p.kr + lane] = lane < p.ka ? e2 / s2 : 0.f;
     }
 }
 
+// The pairs t = b kk + j (rank j < kk of sequence b) whose expert is e, in
+// increasing t, into s_pairs (at most one per sequence: a sequence's ranks
+// are distinct experts); returns their count. Ballots per wave, then the
+// counts of the lower waves.
+constexpr int kMaxPairs = 64;   // sequences per step at most
+__device__ int expert_pairs(const int32_t* ids, int kr, int kk, int P, int e, int* s_pairs, int* s_wc) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int base = 0;
+    for (int t0 = 0; t0 < P; t0 += blockDim.x) {
+        const int t = t0 + threadIdx.x;
+        const bool hit = t < P && ids[(size_t)(t / kk) * kr + t % kk] == e;
+        const unsigned long long m = __ballot(hit);
+        if (lane == 0) s_wc[wv] = __popcll(m);
+        __syncthreads();
+        int before = base, total = base;
+        for (int w = 0; w < nw; ++w) {
+            before += w < wv ? s_wc[w] : 0;
+            total += s_wc[w];
+        }
+        const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
+        if (hit && pos < kMaxPairs) s_pairs[pos] = t;
+        __syncthreads();   // s_wc is rewritten by the next chunk
+        base = total;
+    }
+    return min(base, kMaxPairs);
+}
+
 struct ExpParams {
-    const float* x;        // up: [2B][d] rows; down: g_rows [P][2][Fe] (fp32)
+    const float* x;        // up: [2B][d] rows; down: g rows [P][2][Fe] (fp32)
     const bf16_t* w;       // [E][N][K], each expert matrix in the fragment layout
     int N, K, kk, kp, nflows, kw;   // kk: ranks in use per sequence; kp: primary fan-out
-    const int32_t* offsets;
-    const int32_t* perm;
+    const int32_t* ids;    // [B][kr] expert of each rank
+    int kr, P;             // ids row length; pairs in use (B kk)
     const float* cpl_b;
-    float* g_out;          // up: [P][2][Fe]
-    float* y_out;          // down: [P][2][d]
+    float* g_out;          // up: [P][2][Fe], row 2 t + f
+    float* y_out;          // down: [P][2][d], row 2 t + f
     bool up;
 };
 
-// Stacked row m of an expert: slot s = off + m / nflows, flow f = m % nflows.
+// Stacked row m of an expert: pair t = s_pairs[m / nflows], flow f = m % nflows.
 template <int MT, int KU>
 __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
     extern __shared__ float red[];
+    __shared__ int s_pairs[kMaxPairs];
+    __shared__ int s_wc[16];
     const int e = blockIdx.y;
-    const int off = p.offsets[e], cnt = p.offsets[e + 1] - off;
+    const int cnt = expert_pairs(p.ids, p.kr, p.kk, p.P, e, s_pairs, s_wc);
     if (cnt == 0) return;   // untouched expert: its weights are never read
     const int M = cnt * p.nflows;
     const int mtiles = min((M + 15) / 16, MT);
@@ -216,10 +259,10 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
         #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = min(mbase + mt * 16 + li, M - 1);
-            const int s = off + m / p.nflows, f = m - (m / p.nflows) * p.nflows;
+            const int t = s_pairs[m / p.nflows], f = m - (m / p.nflows) * p.nflows;
             size_t row;
-            if (p.up) row = (size_t)(2 * (p.perm[s] / p.kk) + f);   // sequence b = pair / kk
-            else row = (size_t)s * 2 + f;                         // g_rows[slot][flow]
+            if (p.up) row = (size_t)(2 * (t / p.kk) + f);   // sequence b = pair / kk
+            else row = (size_t)t * 2 + f;                  // g rows [pair][flow]
             xrow[mt] = p.x + row * p.K + lg * 8;
         }
         f32x4 acc[RT][MT];
@@ -229,32 +272,32 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
         tile::to_lds<MT>(red, wv, lane, acc);
         __syncthreads();
         const int npairs = min(cnt - mbase / p.nflows, MT * 16 / p.nflows);
-        for (int t = threadIdx.x; t < ROWS * npairs; t += blockDim.x) {
-            const int nl = t % ROWS, q = t / ROWS;
+        for (int i = threadIdx.x; i < ROWS * npairs; i += blockDim.x) {
+            const int nl = i % ROWS, q = i / ROWS;
             const int n = n0 + nl;
             if (n >= p.N) continue;
             const int ml = q * p.nflows;   // local stacked row of the primary
             const float y1 = tile::lds_sum<MT>(red, NW, nl, ml);
             const float y2 = p.nflows == 2 ? tile::lds_sum<MT>(red, NW, nl, ml + 1) : 0.f;
-            const int s = off + mbase / p.nflows + q;
+            const int t = s_pairs[mbase / p.nflows + q];
             if (p.up) {
                 const float g1 = 0.5f * y1 * (1.0f + erff(y1 * 0.70710678118654752f));
-                p.g_out[((size_t)s * 2) * p.N + n] = g1;
+                p.g_out[((size_t)t * 2) * p.N + n] = g1;
                 if (p.nflows == 2) {
                     float g2 = 0.5f * y2 * (1.0f + erff(y2 * 0.70710678118654752f));
                     // intermediate coupling b_l, per expert the primary also ran (rank < kp)
-                    if (p.cpl_b && p.perm[s] % p.kk < p.kp) g2 = fmaf(p.cpl_b[n], g1, g2);
-                    p.g_out[((size_t)s * 2 + 1) * p.N + n] = g2;
+                    if (p.cpl_b && t % p.kk < p.kp) g2 = fmaf(p.cpl_b[n], g1, g2);
+                    p.g_out[((size_t)t * 2 + 1) * p.N + n] = g2;
                 }
             } else {
-                p.y_out[((size_t)s * 2) * p.N + n] = y1;
-                if (p.nflows == 2) p.y_out[((size_t)s * 2 + 1) * p.N + n] = y2;
+                p.y_out[((size_t)t * 2) * p.N + n] = y1;
+                if (p.nflows == 2) p.y_out[((size_t)t * 2 + 1) * p.N + n] = y2;
             }
         }
     }
 }
 
-// y_1[b] = sum_{j < k} gate_1[b][j] * y(slot of (b, j))_1, y_2 likewise over
+// y_1[b] = sum_{j < k} gate_1[b][j] * y(pair (b, j))_1, y_2 likewise over
 // j < ka; y2 += c * y1; h += y.
 // One workgroup per sequence: both flows' gate-weighted sums over their
 // ranks (rank order), the c coupling, the residual add; then, with g_next,
@@ -262,8 +305,7 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
 // input), the rows being at hand.
 constexpr int kCombThreads = 1024;
 constexpr int kCombCols = 4;   // d <= kCombThreads * kCombCols
-__global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows, const float* gates, const int32_t* inv,
-                                                            const float* cpl_c, int d, int k, int ka, int kr, int kk,
+__global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows, const float* gates, const float* cpl_c, int d, int k, int ka, int kr, int kk,
                                                             int nflows, float* h, const float* g_next, float eps,
                                                             float* x_next) {
     __shared__ int s_slot[kMaxK];
@@ -271,7 +313,7 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows,
     __shared__ float red[16];
     const int b = blockIdx.x, tid = threadIdx.x;
     const bool dual = nflows == 2;
-    if (tid < kk) s_slot[tid] = inv[(size_t)b * kk + tid];
+    if (tid < kk) s_slot[tid] = b * kk + tid;
     if (tid < kr) {
         s_g[0][tid] = gates[((size_t)b * 2) * kr + tid];
         s_g[1][tid] = dual ? gates[((size_t)b * 2 + 1) * kr + tid] : 0.f;
@@ -339,17 +381,27 @@ hipError_t launch_expert(ExpParams& p, int E, hipStream_t s) {
 hipError_t moe(const MoeArgs& a, hipStream_t s) {
     const int ka = a.ka > 0 ? a.ka : a.k;
     const int kr = std::max(a.k, ka), kk = a.nflows == 2 ? kr : a.k;
-    if (kr > kMaxK || a.B > 64 || a.E > 64 * kPerLane || a.dtype != DF_BF16) return hipErrorInvalidValue;
+    if (kr > kMaxK || a.k < 1 || a.B < 1 || a.B > kMaxPairs || a.E < 16 || a.E % 16 || a.E > 64 * kPerLane ||
+        a.d < 32 || a.d % 32 || a.d > kMaxSeg * kStatSeg || a.dtype != DF_BF16 || (a.nflows != 1 && a.nflows != 2))
+        return hipErrorInvalidValue;
+    GateParams gp;
+    gp.h = a.h; gp.stats = a.stats; gp.g = a.g_ln; gp.eps = a.eps; gp.d = a.d; gp.E = a.E; gp.k = a.k; gp.ka = ka;
+    gp.kr = kr; gp.nflows = a.nflows; gp.wr = reinterpret_cast<const bf16_t*>(a.w_router); gp.r1_given = a.r1_given;
+    gp.x = a.x; gp.ids = a.ids; gp.gates = a.gates; gp.ids_out = a.ids_out;
+    // k-splits: about one item per wave
+    gp.ns = 1;
+    while ((a.E / 16) * gp.ns * 2 <= kGateWaves && (a.d / 32) % (gp.ns * 2) == 0) gp.ns *= 2;
+    const size_t glds = (2 * (size_t)a.d + 2 * (size_t)a.E * gp.ns) * sizeof(float);
     (void)hipGetLastError();
-    const auto route = a.E <= 64 ? moe_route<1> : a.E <= 256 ? moe_route<4> : moe_route<kPerLane>;
-    hipLaunchKernelGGL(route, dim3(1), dim3(kRouteThreads), 0, s, a.r, a.r1_given, a.B, a.E, a.k, ka, a.nflows,
-                       a.ids, a.gates, a.ids_out, a.offsets, a.perm, a.inv);
+    const auto gate = a.E <= 64 ? moe_gate<1> : a.E <= 256 ? moe_gate<4> : moe_gate<kPerLane>;
+    hipLaunchKernelGGL(gate, dim3(a.B), dim3(kGateThreads), glds, s, gp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ExpParams up;
     up.x = a.x;
     up.w = reinterpret_cast<const bf16_t*>(a.w_up);
-    up.N = a.Fe; up.K = a.d; up.kk = kk; up.kp = a.k; up.nflows = a.nflows; up.offsets = a.offsets; up.perm = a.perm;
+    up.N = a.Fe; up.K = a.d; up.kk = kk; up.kp = a.k; up.nflows = a.nflows; up.ids = a.ids; up.kr = kr;
+    up.P = a.B * kk;
     up.cpl_b = a.cpl_b; up.g_out = a.g_rows; up.y_out = nullptr; up.up = true;
     e = launch_expert<2>(up, a.E, s);
     if (e != hipSuccess) return e;
@@ -360,7 +412,7 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     e = launch_expert<2>(dn, a.E, s);
     if (e != hipSuccess) return e;
     if (a.d > kCombThreads * kCombCols) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(kCombThreads), 0, s, a.y_rows, a.gates, a.inv, a.cpl_c, a.d, a.k,
+    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(kCombThreads), 0, s, a.y_rows, a.gates, a.cpl_c, a.d, a.k,
                        ka, kr, kk, a.nflows, a.h, a.g_next, a.eps, a.x_next);
     return hipGetLastError();
 }
