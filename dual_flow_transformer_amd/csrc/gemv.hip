@@ -329,24 +329,29 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
 }
 
 // Sums of the S k-slice partials of logical rows m1 and m2 (m2 < 0: none),
-// column n, in slice order; sixteen loads in flight at a time.
+// column n, in slice order; the loads of sixteen slices (32 values) are in
+// flight together.
 __device__ __forceinline__ void sum_slices(const GParams& p, int S, int m1, int m2, int n, float& y1, float& y2) {
+    constexpr int SB = 16;
     const float* q1 = p.part + (size_t)m1 * p.N + n;
     const float* q2 = p.part + (size_t)(m2 < 0 ? m1 : m2) * p.N + n;
     const size_t stride = (size_t)p.M * p.N;
     float v1 = 0.f, v2 = 0.f;
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-        float t1[8], t2[8];
+    for (int s = 0; s < S; s += SB) {
+        float t1[SB], t2[SB];
         #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            t1[u] = q1[(size_t)(s + u) * stride];
-            t2[u] = q2[(size_t)(s + u) * stride];
+        for (int u = 0; u < SB; ++u) {
+            const size_t o = (size_t)min(s + u, S - 1) * stride;
+            t1[u] = q1[o];
+            t2[u] = q2[o];
         }
         #pragma unroll
-        for (int u = 0; u < 8; ++u) { v1 += t1[u]; v2 += t2[u]; }
+        for (int u = 0; u < SB; ++u) {
+            if (s + u >= S) break;
+            v1 += t1[u];
+            v2 += t2[u];
+        }
     }
-    for (; s < S; ++s) { v1 += q1[(size_t)s * stride]; v2 += q2[(size_t)s * stride]; }
     y1 = v1;
     y2 = m2 < 0 ? 0.f : v2;
 }
