@@ -33,8 +33,8 @@ COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
     "attention_source_sha256": "210e88f75d16717f5d313f6fc42d3b4666ff6fffcbfd0d5e3abe19e6e09d442e",
     "attention_traffic_bytes_per_launch": 2.1532e9,
-    "library_sources_sha256": "2f8b57b821d0134e14040f4519b09eb28cfa7895d84f0a74e6d2bf73f4da150a",
-    "step_traffic_bytes": {"dual": 84.880e9, "primary_only": 83.405e9},
+    "library_sources_sha256": "200ffa9aed2beff64cc55bff022637a0e4b91d35e8a289a657f72a068e31eda1",
+    "step_traffic_bytes": {"dual": 84.882e9, "primary_only": 83.406e9},
 }
 
 
