@@ -261,6 +261,31 @@ def test_moe_aux_fanout_leaves_primary_bitwise():
     assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
 
 
+def test_moe_computed_router_matches_oracle():
+    """Primary router logits computed from the router weights (none supplied):
+    the ranking bit-exact against the oracle and the outputs within the bars.
+    Precondition checked on the oracle: its ranked primary logits (the kr
+    chosen and the next one) are at least 1e-4 apart, far above the fp32
+    error of the GPU's router products, so both sides must rank alike."""
+    cfg = SMALL_MOE.replace(name="gpu_moe_router_computed", top_k_aux=6)
+    say("moe computed router")
+    kr = max(cfg.top_k, cfg.top_k_aux)
+    gm = DecodeModel(cfg, fill="host")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    for step in range(2):
+        tok = src.step_tokens(step)
+        gm.decode_step(gm.tokens(tok), router_logits=None)
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True, router_logits=None, trace=True)
+        for l in range(cfg.L):
+            ranked = -np.sort(-r.trace[f"router.{l}"][:, 0], axis=1)[:, :kr + 1]
+            assert np.diff(-ranked, axis=1).min() > 1e-4, "seed gives a near-tie: choose another"
+        assert np.array_equal(gm.expert_ids.cpu().numpy(), r.ids), "expert ranking differs"
+        _compare_step(cfg, gm, r)
+
+
 @pytest.mark.parametrize("E", [128, 320], ids=["e128", "e320"])
 def test_moe_routing_many_experts(E):
     """Routing with more experts than lanes (2 and 5 logits per lane of the

@@ -21,9 +21,12 @@ pytestmark = pytest.mark.gpu
 KV_REL, KV_ABS = 2.0 ** -7, 5e-4
 
 
-@pytest.mark.parametrize("name,seqs", [("c3", [0, 15]), ("c4", [0, 41]), ("c5", [0])])
-def test_full_size_sampled(name, seqs):
-    cfg = PRESETS[name]
+@pytest.mark.parametrize("name,seqs,ka", [("c3", [0, 15], 0), ("c4", [0, 41], 0), ("c4", [7, 63], 16), ("c5", [0], 0)],
+                         ids=["c3", "c4", "c4_aux_fanout16", "c5"])
+def test_full_size_sampled(name, seqs, ka):
+    """ka > 0: the aux flow takes the first ka experts of the primary ranking
+    (1024 (sequence, rank) pairs at batch 64)."""
+    cfg = PRESETS[name] if not ka else PRESETS[name].replace(top_k_aux=ka)
     say(f"full-size {cfg.name}: GPU step, oracle on sequences {seqs}")
     gm = DecodeModel(cfg, fill="device")
     src = Inputs(cfg)
