@@ -382,7 +382,8 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     const int ka = a.ka > 0 ? a.ka : a.k;
     const int kr = std::max(a.k, ka), kk = a.nflows == 2 ? kr : a.k;
     if (kr > kMaxK || a.k < 1 || a.B < 1 || a.B > kMaxPairs || a.E < 16 || a.E % 16 || a.E > 64 * kPerLane ||
-        a.d < 32 || a.d % 32 || a.d > kMaxSeg * kStatSeg || a.dtype != DF_BF16 || (a.nflows != 1 && a.nflows != 2))
+        a.d < 32 || a.d % 32 || a.d > kMaxSeg * kStatSeg || a.d > kCombThreads * kCombCols || a.dtype != DF_BF16 ||
+        (a.nflows != 1 && a.nflows != 2))
         return hipErrorInvalidValue;
     GateParams gp;
     gp.h = a.h; gp.stats = a.stats; gp.g = a.g_ln; gp.eps = a.eps; gp.d = a.d; gp.E = a.E; gp.k = a.k; gp.ka = ka;
@@ -411,7 +412,6 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     dn.N = a.d; dn.K = a.Fe; dn.g_out = nullptr; dn.y_out = a.y_rows; dn.up = false;
     e = launch_expert<2>(dn, a.E, s);
     if (e != hipSuccess) return e;
-    if (a.d > kCombThreads * kCombCols) return hipErrorInvalidValue;
     hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(kCombThreads), 0, s, a.y_rows, a.gates, a.cpl_c, a.d, a.k,
                        ka, kr, kk, a.nflows, a.h, a.g_next, a.eps, a.x_next);
     return hipGetLastError();
