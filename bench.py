@@ -31,10 +31,10 @@ PEAK_HBM_GBS = 8000.0
 # write). Reported only while the kernel sources are the ones they were measured on.
 COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "210e88f75d16717f5d313f6fc42d3b4666ff6fffcbfd0d5e3abe19e6e09d442e",
-    "attention_traffic_bytes_per_launch": 2.1532e9,
-    "library_sources_sha256": "200ffa9aed2beff64cc55bff022637a0e4b91d35e8a289a657f72a068e31eda1",
-    "step_traffic_bytes": {"dual": 84.882e9, "primary_only": 83.406e9},
+    "attention_source_sha256": "7277cb595fad56cc8d11cc9a5b71f022e2dc91e6a0dd49a77b18e3054f2d2c3d",
+    "attention_traffic_bytes_per_launch": 2.1502e9,
+    "library_sources_sha256": "c27f1286f175c53cb2c5b8d4314160ede5356655b1a3ac2b6f038c84320cbca7",
+    "step_traffic_bytes": {"dual": 84.713e9, "primary_only": 83.320e9},
 }
 
 
