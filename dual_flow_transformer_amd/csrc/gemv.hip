@@ -467,7 +467,8 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
 // Kernel shapes: A = 16-row tiles, 8 waves, batches of 8 fragments (4 with 64
 // stacked rows, 2 with 128), two batches ahead (one with 128 rows);
 // B = 32-row tiles, 4 waves, batches of 4 fragments per tile, one batch ahead
-// (matrices with fewer than 8192 rows; two waves per SIMD need the registers).
+// (up to 32 stacked rows, for matrices with fewer than 8192 rows or at most
+// 16 M weights; plan_gemv holds the choice).
 enum Variant { VAR_A = 0, VAR_B = 1 };
 
 template <int MT, int RT, int KU, int NW, int KS, int NBUF>
