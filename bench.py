@@ -33,7 +33,7 @@ COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
     "attention_source_sha256": "7277cb595fad56cc8d11cc9a5b71f022e2dc91e6a0dd49a77b18e3054f2d2c3d",
     "attention_traffic_bytes_per_launch": 2.1502e9,
-    "library_sources_sha256": "c27f1286f175c53cb2c5b8d4314160ede5356655b1a3ac2b6f038c84320cbca7",
+    "library_sources_sha256": "227cd5cff9fb9e3e37b2559c04788bc71b6b4111e6afc704c2ab207a03a0b979",
     "step_traffic_bytes": {"dual": 84.713e9, "primary_only": 83.320e9},
 }
 
