@@ -125,8 +125,14 @@ struct MixRows {
     float* logits_out;
 };
 
+// NPT > 0: the row's logits are read once into registers (NPT per thread and
+// flow, V <= 1024 NPT) and every pass runs from there; NPT == 0: each pass
+// reads them again (any V). Both visit logit v = tid + 1024 j in increasing
+// j, so their sums, and so their results, are the same bit for bit.
+template <int NPT>
 __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mode, float* p_mix, float* alpha,
                                                         int32_t* next_tok) {
+    constexpr int NR = NPT > 0 ? NPT : 1;
     const int aux_on = mode != DF_MIX_PRIMARY;
     __shared__ float red[16];
     __shared__ float bv[16];
@@ -135,26 +141,47 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
     const float* l1 = m.l1 + (size_t)i * m.stride;
     const float* l2 = m.l2 + (size_t)i * m.stride;
     const int b = m.Tc > 0 ? (i / m.Tc) * m.T + m.t0 + i % m.Tc : i;
+    float x1[NR], x2[NR];
+    if constexpr (NPT > 0) {
+        #pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const int v = min((int)threadIdx.x + 1024 * j, V - 1);
+            x1[j] = l1[v];
+            x2[j] = l2[v];
+        }
+    }
+    // logit v of flow f: from the registers or from memory
+    auto L1 = [&](int j, int v) { if constexpr (NPT > 0) return x1[j]; else return l1[v]; };
+    auto L2 = [&](int j, int v) { if constexpr (NPT > 0) return x2[j]; else return l2[v]; };
+    const int nj = NPT > 0 ? NPT : (V + 1023) / 1024;
     if (m.logits_out) {
         float* lo = m.logits_out + (size_t)b * 2 * V;
-        for (int v = threadIdx.x; v < V; v += blockDim.x) {
-            lo[v] = l1[v];
-            lo[V + v] = l2[v];
+        for (int j = 0; j < nj; ++j) {
+            const int v = threadIdx.x + 1024 * j;
+            if (v >= V) break;
+            lo[v] = L1(j, v);
+            lo[V + v] = L2(j, v);
         }
     }
     float mx1 = -INFINITY, mx2 = -INFINITY;
-    for (int v = threadIdx.x; v < V; v += blockDim.x) {
-        mx1 = fmaxf(mx1, l1[v]);
-        if (aux_on) mx2 = fmaxf(mx2, l2[v]);
+    #pragma unroll
+    for (int j = 0; j < nj; ++j) {
+        const int v = threadIdx.x + 1024 * j;
+        if (v >= V) break;
+        mx1 = fmaxf(mx1, L1(j, v));
+        if (aux_on) mx2 = fmaxf(mx2, L2(j, v));
     }
     mx1 = df::block_max(mx1, red);
     if (aux_on) mx2 = df::block_max(mx2, red);
     float s1 = 0.f, c1 = 0.f, s2 = 0.f;
-    for (int v = threadIdx.x; v < V; v += blockDim.x) {
-        const float e1 = __builtin_amdgcn_exp2f((l1[v] - mx1) * df::kLog2e);
+    #pragma unroll
+    for (int j = 0; j < nj; ++j) {
+        const int v = threadIdx.x + 1024 * j;
+        if (v >= V) break;
+        const float e1 = __builtin_amdgcn_exp2f((L1(j, v) - mx1) * df::kLog2e);
         s1 += e1;
         c1 = fmaf(e1, e1, c1);
-        if (aux_on) s2 += __builtin_amdgcn_exp2f((l2[v] - mx2) * df::kLog2e);
+        if (aux_on) s2 += __builtin_amdgcn_exp2f((L2(j, v) - mx2) * df::kLog2e);
     }
     s1 = df::block_sum(s1, red);
     c1 = df::block_sum(c1, red);
@@ -168,9 +195,12 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
     float best = -1.f;
     int besti = 0x7fffffff;
     float* out = p_mix + (size_t)b * V;
-    for (int v = threadIdx.x; v < V; v += blockDim.x) {
-        float p = __builtin_amdgcn_exp2f((l1[v] - mx1) * df::kLog2e) * w1;
-        if (aux_on) p = fmaf(__builtin_amdgcn_exp2f((l2[v] - mx2) * df::kLog2e), w2, p);
+    #pragma unroll
+    for (int j = 0; j < nj; ++j) {
+        const int v = threadIdx.x + 1024 * j;
+        if (v >= V) break;
+        float p = __builtin_amdgcn_exp2f((L1(j, v) - mx1) * df::kLog2e) * w1;
+        if (aux_on) p = fmaf(__builtin_amdgcn_exp2f((L2(j, v) - mx2) * df::kLog2e), w2, p);
         out[v] = p;
         if (p > best) { best = p; besti = v; }
     }
@@ -193,22 +223,31 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
     }
 }
 
+// Rows through the mixture head, the register-resident kernel when V allows.
+hipError_t launch_mix(const MixRows& m, int R, int V, int mode, float* p_mix, float* alpha, int32_t* next_tok,
+                      hipStream_t s) {
+    (void)hipGetLastError();
+    const dim3 g(R), t(1024);
+    if (V <= 4 * 1024) hipLaunchKernelGGL(mix_head_kernel<4>, g, t, 0, s, m, V, mode, p_mix, alpha, next_tok);
+    else if (V <= 8 * 1024) hipLaunchKernelGGL(mix_head_kernel<8>, g, t, 0, s, m, V, mode, p_mix, alpha, next_tok);
+    else if (V <= 16 * 1024) hipLaunchKernelGGL(mix_head_kernel<16>, g, t, 0, s, m, V, mode, p_mix, alpha, next_tok);
+    else if (V <= 32 * 1024) hipLaunchKernelGGL(mix_head_kernel<32>, g, t, 0, s, m, V, mode, p_mix, alpha, next_tok);
+    else hipLaunchKernelGGL(mix_head_kernel<0>, g, t, 0, s, m, V, mode, p_mix, alpha, next_tok);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
                     int32_t* next_tok, hipStream_t s) {
     const MixRows m{logits, logits + V, (size_t)2 * V, 0, 0, 0, nullptr};
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(mix_head_kernel, dim3(B), dim3(1024), 0, s, m, V, mode, p_mix, alpha, next_tok);
-    return hipGetLastError();
+    return launch_mix(m, B, V, mode, p_mix, alpha, next_tok, s);
 }
 
 hipError_t mix_rows(const float* l1, const float* l2, int R, int V, int mode, int Tc, int T, int t0,
                     float* logits_out, float* p_mix, float* alpha, int32_t* next_tok, hipStream_t s) {
     const MixRows m{l1, l2, (size_t)V, Tc, T, t0, logits_out};
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(mix_head_kernel, dim3(R), dim3(1024), 0, s, m, V, mode, p_mix, alpha, next_tok);
-    return hipGetLastError();
+    return launch_mix(m, R, V, mode, p_mix, alpha, next_tok, s);
 }
 
 hipError_t kv_append(int dtype, void* k, void* v, int B, int H, int S_max, int Dh, const int32_t* pos,

@@ -33,8 +33,12 @@ def _mix(l, aux_on):
     return p.cpu().numpy(), a.cpu().numpy(), t.cpu().numpy()
 
 
+# vocabularies across the kernel's register-resident sizes (up to 4, 8, 16 and 32 Ki
+# logits per row) and past them (the path that re-reads the row)
 @pytest.mark.parametrize("V,scale,aux_on", [(32000, 1.0, 1), (517, 3.0, 1), (1000, 12.0, 1), (32000, 1.0, 0),
-                                            (32000, 1.0, 2), (1000, 12.0, 2), (32000, 1.0, 3), (1000, 12.0, 3)])
+                                            (32000, 1.0, 2), (1000, 12.0, 2), (32000, 1.0, 3), (1000, 12.0, 3),
+                                            (5000, 2.0, 1), (9000, 1.0, 1), (32768, 1.0, 1), (40000, 1.0, 1),
+                                            (40000, 4.0, 0)])
 def test_mix_head_random(V, scale, aux_on):
     say(f"mix head V={V} scale={scale} mode={aux_on}")
     B = 4
