@@ -356,7 +356,10 @@ struct Step {
             set_x(g, w.lnf);   // final norm
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             const int mode = mix_mode_of(c, nflows);
-            if (dfk::mix_head(lg, B, c.vocab, mode, p_mix, alpha, next_tok, s) != hipSuccess) return DF_ERR_HIP;
+            // the step's last kernel also advances len
+            if (dfk::mix_head(lg, B, c.vocab, mode, p_mix, alpha, next_tok, s, kv.len) != hipSuccess)
+                return DF_ERR_HIP;
+            return DF_OK;
         }
         if (dfk::len_add(kv.len, B, 1, s) != hipSuccess) return DF_ERR_HIP;
         return DF_OK;

@@ -34,9 +34,10 @@ hipError_t attention(const AttnArgs& a, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Row operations
 // ---------------------------------------------------------------------------
-// Mixture head over logits [B][2][V]; mode: DF_MIX_*.
+// Mixture head over logits [B][2][V]; mode: DF_MIX_*. With len_inc, also
+// len_inc[b] += 1 for each row once it is done.
 hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
-                    int32_t* next_tok, hipStream_t s);
+                    int32_t* next_tok, hipStream_t s, int32_t* len_inc = nullptr);
 // Mixture head over R row pairs (l1 + i V, l2 + i V) of a prefill-style
 // chunk (row i = b * Tc + t); outputs at row (b * T + t0 + t) of [B][T]
 // buffers; logits_out [B][T][2][V] may be NULL.

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
     const int32_t* len, int d, int S_max, int V, int nflows, const float* g, float eps, float* h, float* x,
     int32_t* status) {
     __shared__ float red[16];
-    const int b = blockIdx.x;
+    const int b = blockIdx.x, f = blockIdx.y;   // one workgroup per stacked row
     int pos = len[b];
     pos = pos < 0 ? 0 : (pos >= S_max ? S_max - 1 : pos);
     int t = tok[(size_t)b * tok_stride];
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
         if (status && threadIdx.x == 0) status[0] |= 2;
         t = t < 0 ? 0 : V - 1;
     }
-    for (int f = 0; f < nflows; ++f) {
+    {
         const T* e = (f == 0 ? emb0 : emb1) + (size_t)t * d;
         const T* pe = pos_emb + (size_t)pos * d;
         const size_t row = (size_t)(2 * b + f) * d;
@@ -123,6 +123,7 @@ struct MixRows {
     size_t stride;
     int Tc, T, t0;
     float* logits_out;
+    int32_t* len_inc;   // if set: len_inc[row] += 1 once the row is done (the step's last kernel)
 };
 
 // NPT > 0: the row's logits are read once into registers (NPT per thread and
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
             if (bv[k] > bb || (bv[k] == bb && bi[k] < ii)) { bb = bv[k]; ii = bi[k]; }
         if (next_tok) next_tok[b] = ii;
         alpha[b] = a;
+        if (m.len_inc) m.len_inc[b] += 1;
     }
 }
 
@@ -239,14 +241,14 @@ hipError_t launch_mix(const MixRows& m, int R, int V, int mode, float* p_mix, fl
 }  // namespace
 
 hipError_t mix_head(const float* logits, int B, int V, int mode, float* p_mix, float* alpha,
-                    int32_t* next_tok, hipStream_t s) {
-    const MixRows m{logits, logits + V, (size_t)2 * V, 0, 0, 0, nullptr};
+                    int32_t* next_tok, hipStream_t s, int32_t* len_inc) {
+    const MixRows m{logits, logits + V, (size_t)2 * V, 0, 0, 0, nullptr, len_inc};
     return launch_mix(m, B, V, mode, p_mix, alpha, next_tok, s);
 }
 
 hipError_t mix_rows(const float* l1, const float* l2, int R, int V, int mode, int Tc, int T, int t0,
                     float* logits_out, float* p_mix, float* alpha, int32_t* next_tok, hipStream_t s) {
-    const MixRows m{l1, l2, (size_t)V, Tc, T, t0, logits_out};
+    const MixRows m{l1, l2, (size_t)V, Tc, T, t0, logits_out, nullptr};
     return launch_mix(m, R, V, mode, p_mix, alpha, next_tok, s);
 }
 
@@ -274,11 +276,11 @@ hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* p
                     float eps, float* h, void* x, int32_t* status, hipStream_t s) {
     (void)hipGetLastError();
     if (dtype == DF_BF16)
-        hipLaunchKernelGGL(embed_ln_kernel<bf16_t>, dim3(B), dim3(kRowThreads), 0, s, (const bf16_t*)emb0,
+        hipLaunchKernelGGL(embed_ln_kernel<bf16_t>, dim3(B, nflows), dim3(kRowThreads), 0, s, (const bf16_t*)emb0,
                            (const bf16_t*)emb1, (const bf16_t*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
                            g, eps, h, (float*)x, status);
     else
-        hipLaunchKernelGGL(embed_ln_kernel<float>, dim3(B), dim3(kRowThreads), 0, s, (const float*)emb0,
+        hipLaunchKernelGGL(embed_ln_kernel<float>, dim3(B, nflows), dim3(kRowThreads), 0, s, (const float*)emb0,
                            (const float*)emb1, (const float*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
                            g, eps, h, (float*)x, status);
     return hipGetLastError();
