@@ -138,7 +138,10 @@ __global__ __launch_bounds__(256) void attn_prefill(AttnRows qs, int Tc, int t0,
     __shared__ bf16_t Vt[ADH * VSP];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // heaviest query blocks first: workgroups are dispatched with z slowest,
+    // so the blocks of the last positions (the most keys) go out first and
+    // the light ones fill in at the end
+    const int qb = gridDim.z - 1 - blockIdx.z, h = blockIdx.x, b = blockIdx.y;
     const int d = H * ADH;
     const int pos0 = len[b] + t0;                            // position of chunk row t = 0
     // one flow: 128 positions per workgroup, 32 per wave; two flows: 64
@@ -342,7 +345,7 @@ hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_
     const AttnRows qs{q, q2, a, q2 ? 2 : 1, R16};
     const int QG = AQG / qs.nflows;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(attn_prefill, dim3((Tc + QG - 1) / QG, H, B), dim3(256), 0, s, qs, Tc, t0, len, H, S_max,
+    hipLaunchKernelGGL(attn_prefill, dim3(H, B, (Tc + QG - 1) / QG), dim3(256), 0, s, qs, Tc, t0, len, H, S_max,
                        reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
                        df::kLog2e / sqrtf((float)Dh), reinterpret_cast<bf16_t*>(oh), reinterpret_cast<bf16_t*>(ol));
     return hipGetLastError();
