@@ -33,7 +33,7 @@ COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
     "attention_source_sha256": "7277cb595fad56cc8d11cc9a5b71f022e2dc91e6a0dd49a77b18e3054f2d2c3d",
     "attention_traffic_bytes_per_launch": 2.1502e9,
-    "library_sources_sha256": "ce482b913453f1a08b13fe295ac051a30bb9c28d57248966783ce7fd16a5b644",
+    "library_sources_sha256": "c096c0ecb86ff467a656fa7e95ebcc1f45dc8cdd45e12b64c91c96e8f8042487",
     "step_traffic_bytes": {"dual": 84.713e9, "primary_only": 83.322e9},
 }
 
