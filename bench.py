@@ -25,6 +25,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "dual-flow decode tokens/s at 1 GPU; achieved HBM GB/s vs peak; dual/primary byte ratio"
 PEAK_HBM_GBS = 8000.0
+# Decode attention launches timed inside the timed region: one in every 7 (a timed launch takes a
+# few microseconds more than an untimed one; 7 shares no factor with 16, 24 or 32 layers, so the
+# sample walks through every layer).
+TIMING_STRIDE = 7
 
 # HBM traffic measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on the dense 32-layer
 # workload (counters scaled by their reading for a plain 1 GiB copy: x2.0 fetch, x1.0
@@ -169,7 +173,7 @@ def bench_attention(args):
     for _ in range(W):
         call()
     torch.cuda.synchronize()
-    _abi.check(_abi.df_timing_enable(0), "df_timing_enable")
+    _abi.check(_abi.df_timing_enable(0, TIMING_STRIDE), "df_timing_enable")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(K):
@@ -216,7 +220,8 @@ def bench_attention(args):
                    "lengths": [int(lens.min()), int(lens.max())], "mean_length": float(lens.mean())},
         "roofline": {"kernel": "attn_partial (split-K pass)", "bound": "hbm", "achieved": part_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": part_gbs / PEAK_HBM_GBS, "traffic": None,
-                     "avg_launch_ms": part_avg, "launches": part_n, "algorithmic_bytes_per_launch": kv_bytes},
+                     "avg_launch_ms": part_avg, "launches": part_n, "timed_every": TIMING_STRIDE,
+                     "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -306,7 +311,7 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     res = {}
     for kclass in (1, 2):              # GEMM launches, then attention launches, each over the K steps
-        _abi.check(_abi.df_timing_enable(kclass), "df_timing_enable")
+        _abi.check(_abi.df_timing_enable(kclass, 1), "df_timing_enable")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(K):
@@ -435,7 +440,7 @@ def bench_forward(args):
     torch.cuda.synchronize()
     res = {}
     for kclass in (1, 2):
-        _abi.check(_abi.df_timing_enable(kclass), "df_timing_enable")
+        _abi.check(_abi.df_timing_enable(kclass, 1), "df_timing_enable")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(K):
@@ -532,7 +537,7 @@ def main():
     torch.cuda.synchronize()
     lens_start = gm.len.cpu().numpy().astype(np.int64)
     # timed region: K dual steps
-    _abi.check(_abi.df_timing_enable(0), "df_timing_enable")
+    _abi.check(_abi.df_timing_enable(0, TIMING_STRIDE), "df_timing_enable")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -552,10 +557,12 @@ def main():
     # algorithmic bytes over the timed steps
     es = 2 if cfg.dtype == "bf16" else 4
     kv_attn = 0
-    for i in range(K):
-        keys = int((lens_start + i + 1).sum())
-        kv_attn += cfg.L * cfg.H * keys * cfg.Dh * es * 2
-    attn_bytes_per_launch = kv_attn / (K * cfg.L)
+    sampled = range(0, K * cfg.L, TIMING_STRIDE)          # the launches df_timing_enable timed
+    assert len(sampled) == attn_n, (len(sampled), attn_n)
+    for i in sampled:
+        keys = int((lens_start + i // cfg.L + 1).sum())
+        kv_attn += cfg.H * keys * cfg.Dh * es * 2
+    attn_bytes_per_launch = kv_attn / len(sampled)
     attn_avg_ms = attn_ms / max(attn_n, 1)
     attn_gbs = attn_bytes_per_launch / (attn_avg_ms / 1e3) / 1e9
     gm.len.copy_(torch.from_numpy(lens_start + K // 2).to(gm.len.device))
@@ -615,7 +622,7 @@ def main():
         "roofline": {"kernel": "attn_partial (shared-K/V dual-query attention, split-K pass)", "bound": "hbm",
                      "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": attn_gbs / PEAK_HBM_GBS,
                      "traffic": traffic, "avg_launch_ms": attn_avg_ms, "launches": attn_n,
-                     "algorithmic_bytes_per_launch": attn_bytes_per_launch},
+                     "timed_every": TIMING_STRIDE, "algorithmic_bytes_per_launch": attn_bytes_per_launch},
         "step_bandwidth": {"algorithmic_bytes": ab_dual["total"], "achieved_GBs": step_gbs,
                            "frac": step_gbs / PEAK_HBM_GBS, "breakdown": ab_dual},
         "byte_ratio": {"analytic_dual_over_primary": ab_dual["total"] / ab_prim["total"], "counter": counter_ratio},

@@ -103,7 +103,7 @@ def lib() -> ctypes.CDLL:
         L.df_pack_weights.restype = ctypes.c_int
         L.df_pack_weights.argtypes = [i32, vp, vp, ctypes.c_int64, i32, i32, vp]
         L.df_timing_enable.restype = ctypes.c_int
-        L.df_timing_enable.argtypes = [i32]
+        L.df_timing_enable.argtypes = [i32, i32]
         L.df_timing_read.restype = ctypes.c_int
         L.df_timing_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]
         _lib = L
@@ -191,8 +191,8 @@ def df_pack_weights(dtype, d_src, d_dst, n_mats, rows, cols, stream=0) -> int:
     return lib().df_pack_weights(int(dtype), d_src, d_dst, int(n_mats), int(rows), int(cols), stream)
 
 
-def df_timing_enable(kclass: int = 0) -> int:
-    return lib().df_timing_enable(int(kclass))
+def df_timing_enable(kclass: int = 0, stride: int = 1) -> int:
+    return lib().df_timing_enable(int(kclass), int(stride))
 
 
 def df_timing_read():

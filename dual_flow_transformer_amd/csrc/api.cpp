@@ -218,6 +218,8 @@ int check_ws(const df_config& c, const void* ws, size_t ws_bytes) {
 struct Timing {
     std::mutex mu;
     int kclass = -1;
+    int64_t stride = 1;           // time one launch of the class in every `stride`
+    int64_t seen = 0;             // launches of the class since df_timing_enable
     std::vector<hipEvent_t> ev;   // pairs
     size_t used = 0;
 };
@@ -229,6 +231,7 @@ void timing_events(int kclass, hipEvent_t* start, hipEvent_t* stop) {
     *stop = nullptr;
     std::lock_guard<std::mutex> lk(g_timing.mu);
     if (g_timing.kclass != kclass || g_timing.used >= kMaxTimed) return;
+    if (g_timing.seen++ % g_timing.stride != 0) return;
     while (g_timing.ev.size() < 2 * (g_timing.used + 1)) {
         hipEvent_t e;
         if (hipEventCreate(&e) != hipSuccess) return;
@@ -433,17 +436,16 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
     const size_t kv_layer = (size_t)B * H * c.max_seq * Dh * es;
     const int Tmax = prefill_chunk(c);
     auto ok = [](hipError_t e) { return e == hipSuccess; };
-    auto timed = [&](int kclass, auto&& launch) -> hipError_t {   // HIP events around one launch
+    auto timed = [&](int kclass, auto&& launch) -> hipError_t {   // the launch takes its own timestamps
         hipEvent_t e0, e1;
         timing_events(kclass, &e0, &e1);
-        if (e0 && hipEventRecord(e0, s) != hipSuccess) return hipErrorUnknown;
-        const hipError_t e = launch();
-        if (e == hipSuccess && e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorUnknown;
-        return e;
+        return launch(e0, e1);
     };
     auto gemm = [&](const void* ah, const void* al, const char* wt, int R, int N, int K, int epi, float* y,
                     const dfk::QkvStore* st = nullptr) {
-        return timed(1, [&] { return dfk::gemm(ah, al, wt, R, N, K, epi, y, fh, fl, s, st); });
+        return timed(1, [&](hipEvent_t e0, hipEvent_t e1) {
+            return dfk::gemm(ah, al, wt, R, N, K, epi, y, fh, fl, s, st, nullptr, e0, e1);
+        });
     };
     for (int t0 = 0; t0 < T; t0 += Tmax) {
         const int Tc = std::min(Tmax, T - t0), R = B * Tc;
@@ -461,8 +463,9 @@ int df_prefill_primary(const df_config* cfg, const df_weights* w, const df_kv* k
                                    t0, H, Dh, c.max_seq, status};
             if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R, d, xh, xl, s)) ||
                 !ok(gemm(xh, xl, wqkv, R, 3 * d, d, dfk::GEMM_QKV, q, &st)) ||
-                !ok(timed(2, [&] {
-                    return dfk::prefill_attention(q, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s);
+                !ok(timed(2, [&](hipEvent_t e0, hipEvent_t e1) {
+                    return dfk::prefill_attention(q, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s,
+                                                  nullptr, nullptr, 0, e0, e1);
                 })) ||
                 !ok(gemm(xh, xl, wo, R, d, d, dfk::GEMM_RESID, h)) ||
                 !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R, d, xh, xl, s)) ||
@@ -536,17 +539,16 @@ int df_forward_dual(const df_config* cfg, const df_weights* w, const df_kv* kv, 
     const size_t es = 2;
     const size_t kv_layer = (size_t)B * H * c.max_seq * Dh * es;
     const int Tmax = forward_chunk(c);
-    auto timed = [&](int kclass, auto&& launch) -> hipError_t {
+    auto timed = [&](int kclass, auto&& launch) -> hipError_t {   // the launch takes its own timestamps
         hipEvent_t e0, e1;
         timing_events(kclass, &e0, &e1);
-        if (e0 && hipEventRecord(e0, s) != hipSuccess) return hipErrorUnknown;
-        const hipError_t e = launch();
-        if (e == hipSuccess && e1 && hipEventRecord(e1, s) != hipSuccess) return hipErrorUnknown;
-        return e;
+        return launch(e0, e1);
     };
     auto gemm = [&](const void* ah, const void* al, const void* wt, int R, int N, int K, int epi, float* y, void* oh,
                     void* ol, const dfk::QkvStore* qs = nullptr, const dfk::GemmCouple* cp = nullptr) {
-        return timed(1, [&] { return dfk::gemm(ah, al, wt, R, N, K, epi, y, oh, ol, s, qs, cp); });
+        return timed(1, [&](hipEvent_t e0, hipEvent_t e1) {
+            return dfk::gemm(ah, al, wt, R, N, K, epi, y, oh, ol, s, qs, cp, e0, e1);
+        });
     };
     for (int t0 = 0; t0 < T; t0 += Tmax) {
         const int Tc = std::min(Tmax, T - t0), R = B * Tc, R16 = (R + 15) / 16 * 16, R2 = R16 + R;
@@ -570,9 +572,9 @@ int df_forward_dual(const df_config* cfg, const df_weights* w, const df_kv* kv, 
             if (!ok(dfk::prefill_layer_norm(h, w->ln1 + (size_t)l * d, c.ln_eps, R2, d, xh, xl, s)) ||
                 !ok(gemm(xh, xl, wqkv, R, 3 * d, d, dfk::GEMM_QKV, q1, nullptr, nullptr, &st)) ||
                 !ok(gemm(xh + xa, xl + xa, wqkv, R, d, d, dfk::GEMM_STORE, q2, nullptr, nullptr)) ||
-                !ok(timed(2, [&] {
+                !ok(timed(2, [&](hipEvent_t e0, hipEvent_t e1) {
                     return dfk::prefill_attention(q1, B, Tc, t0, kv->len, H, Dh, c.max_seq, kc, vc, xh, xl, s, q2,
-                                                  couple ? w->cpl_a + (size_t)l * d : nullptr, R16);
+                                                  couple ? w->cpl_a + (size_t)l * d : nullptr, R16, e0, e1);
                 })) ||
                 !ok(gemm(xh, xl, wo, R2, d, d, dfk::GEMM_RESID, h, nullptr, nullptr)) ||
                 !ok(dfk::prefill_layer_norm(h, w->ln2 + (size_t)l * d, c.ln_eps, R2, d, xh, xl, s)) ||
@@ -726,10 +728,12 @@ const char* df_status_str(int code) {
     return "unknown status code";
 }
 
-int df_timing_enable(int32_t kclass) {
-    if (kclass < 0 || kclass > 2) return DF_ERR_ARG;
+int df_timing_enable(int32_t kclass, int32_t stride) {
+    if (kclass < 0 || kclass > 2 || stride < 1) return DF_ERR_ARG;
     std::lock_guard<std::mutex> lk(g_timing.mu);
     g_timing.kclass = kclass;
+    g_timing.stride = stride;
+    g_timing.seen = 0;
     g_timing.used = 0;
     return DF_OK;
 }

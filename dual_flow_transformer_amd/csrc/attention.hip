@@ -336,11 +336,9 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     p.B = a.B; p.H = a.H; p.S_max = a.S_max; p.nkeys_add = a.nkeys_add; p.nflows = a.nflows;
     p.waves = waves;
     p.scale_log2 = df::kLog2e / sqrtf((float)DH);
-    (void)hipGetLastError();
-    if (a.ev_start) (void)hipEventRecord(a.ev_start, s);
-    hipLaunchKernelGGL((attn_partial<T, DH, U>), dim3(waves / 4), dim3(256), 0, s, p);
-    if (a.ev_stop) (void)hipEventRecord(a.ev_stop, s);
-    hipError_t e = hipGetLastError();
+    void* args[] = {&p};
+    hipError_t e = launch_timed(reinterpret_cast<const void*>(&attn_partial<T, DH, U>), dim3(waves / 4), dim3(256),
+                                args, 0, s, a.ev_start, a.ev_stop);
     if (e != hipSuccess) return e;
     CombParams c;
     c.part_o = p.part_o; c.part_ml = p.part_ml; c.seq_tab = p.seq_tab; c.nkeys = a.nkeys; c.o_f32 = a.o_f32;

@@ -1,11 +1,22 @@
 // Host-side launchers of the dual-flow decode kernels (not exported).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dfk {
+
+// Launch kernel fn (its arguments given as pointers in args) on stream s.
+// With events, the dispatch itself takes the start and stop timestamps
+// (hipExtLaunchKernel), so timing adds no marker packets between kernels.
+inline hipError_t launch_timed(const void* fn, dim3 grid, dim3 block, void** args, size_t lds, hipStream_t s,
+                               hipEvent_t start, hipEvent_t stop) {
+    (void)hipGetLastError();
+    if (start || stop) return hipExtLaunchKernel(fn, grid, block, args, lds, s, start, stop, 0);
+    return hipLaunchKernel(fn, grid, block, args, lds, s);
+}
 
 // ---------------------------------------------------------------------------
 // Shared-K/V dual-query attention (split over key chunks, then merged).
@@ -25,7 +36,7 @@ struct AttnArgs {
     float* o_f32;             // [B][2][H][Dh] fp32 output or nullptr
     float* lse;               // [B][2][H] or nullptr
     float* o_rows;            // [2B][H*Dh] fp32 output rows (projection input), or nullptr
-    hipEvent_t ev_start;      // optional events around the partial pass
+    hipEvent_t ev_start;      // optional events: start and stop timestamps of the partial pass
     hipEvent_t ev_stop;
 };
 size_t attention_part_floats(int B, int H, int S_max, int Dh);
@@ -148,8 +159,10 @@ struct QkvStore {
     int Tc, t0, H, Dh, S_max;
     int32_t* status;
 };
+// With ev_start / ev_stop the launch takes its own start and stop timestamps.
 hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
-                void* yl, hipStream_t s, const QkvStore* kv = nullptr, const GemmCouple* cp = nullptr);
+                void* yl, hipStream_t s, const QkvStore* kv = nullptr, const GemmCouple* cp = nullptr,
+                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // fp32 rows [R][K] -> hi / lo fragment planes (K % 32 == 0).
 hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStream_t s);
 
@@ -172,7 +185,8 @@ hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, 
 // q2 + a * q (a may be NULL) and its output rows sit at R16 + r.
 hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
                              const void* kc, const void* vc, void* oh, void* ol, hipStream_t s,
-                             const float* q2 = nullptr, const float* a = nullptr, int R16 = 0);
+                             const float* q2 = nullptr, const float* a = nullptr, int R16 = 0,
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // ---------------------------------------------------------------------------
 // MoE with router replay

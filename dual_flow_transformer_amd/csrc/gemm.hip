@@ -218,7 +218,8 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float* x, int R, 
 }  // namespace
 
 hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int K, int epi, float* y, void* yh,
-                void* yl, hipStream_t s, const QkvStore* kv, const GemmCouple* cp) {
+                void* yl, hipStream_t s, const QkvStore* kv, const GemmCouple* cp, hipEvent_t ev_start,
+                hipEvent_t ev_stop) {
     if (R < 1 || N < 16 || N % 16 || K < 32 || K % 32 || epi < GEMM_STORE || epi > GEMM_RESID_CPL)
         return hipErrorInvalidValue;
     const bool split = epi == GEMM_GELU_SPLIT || epi == GEMM_GELU_SPLIT_CPL;
@@ -233,9 +234,9 @@ hipError_t gemm(const void* xh, const void* xl, const void* w, int R, int N, int
                  reinterpret_cast<bf16_t*>(yl), kv ? *kv : QkvStore{}, cp ? *cp : GemmCouple{}};
     hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(&gemm_bf16), kGemmLds);
     if (e != hipSuccess) return e;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(gemm_bf16, dim3((N + TT - 1) / TT, (R + TT - 1) / TT), dim3(NTHREADS), kGemmLds, s, p);
-    return hipGetLastError();
+    void* args[] = {&p};
+    return launch_timed(reinterpret_cast<const void*>(&gemm_bf16), dim3((N + TT - 1) / TT, (R + TT - 1) / TT),
+                        dim3(NTHREADS), args, kGemmLds, s, ev_start, ev_stop);
 }
 
 hipError_t split_rows(const float* x, int R, int K, void* xh, void* xl, hipStream_t s) {

@@ -340,15 +340,19 @@ hipError_t prefill_layer_norm(const float* h, const float* g, float eps, int R, 
 
 hipError_t prefill_attention(const float* q, int B, int Tc, int t0, const int32_t* len, int H, int Dh, int S_max,
                              const void* kc, const void* vc, void* oh, void* ol, hipStream_t s, const float* q2,
-                             const float* a, int R16) {
+                             const float* a, int R16, hipEvent_t ev_start, hipEvent_t ev_stop) {
     if (Dh != ADH) return hipErrorInvalidValue;
     const AttnRows qs{q, q2, a, q2 ? 2 : 1, R16};
     const int QG = AQG / qs.nflows;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(attn_prefill, dim3(H, B, (Tc + QG - 1) / QG), dim3(256), 0, s, qs, Tc, t0, len, H, S_max,
-                       reinterpret_cast<const bf16_t*>(kc), reinterpret_cast<const bf16_t*>(vc),
-                       df::kLog2e / sqrtf((float)Dh), reinterpret_cast<bf16_t*>(oh), reinterpret_cast<bf16_t*>(ol));
-    return hipGetLastError();
+    const bf16_t* kcb = reinterpret_cast<const bf16_t*>(kc);
+    const bf16_t* vcb = reinterpret_cast<const bf16_t*>(vc);
+    float scale_log2 = df::kLog2e / sqrtf((float)Dh);
+    bf16_t* ohb = reinterpret_cast<bf16_t*>(oh);
+    bf16_t* olb = reinterpret_cast<bf16_t*>(ol);
+    void* args[] = {(void*)&qs, &Tc, &t0, (void*)&len, &H, &S_max, (void*)&kcb, (void*)&vcb, &scale_log2, &ohb, &olb};
+    return launch_timed(reinterpret_cast<const void*>(&attn_prefill), dim3(H, B, (Tc + QG - 1) / QG), dim3(256), args,
+                        0, s, ev_start, ev_stop);
 }
 
 }  // namespace dfk

@@ -306,12 +306,19 @@ int df_device_status(void* d_ws, void* stream, int32_t* status_out);
 const char* df_status_str(int code);
 
 /* Kernel timing with HIP events on the launching stream. While enabled,
- * every launch of the kernels of class `kclass` is bracketed by a pair of
- * events: 0 = attention partial pass (decode), 1 = tiled GEMM (prefill
- * projections), 2 = causal prefill attention. df_timing_read synchronises
- * them and returns the summed duration (ms) and the launch count, then
- * disables timing. At most 65536 launches are recorded. */
-int df_timing_enable(int32_t kclass);
+ * launches of the kernels of class `kclass` (0 = attention partial pass
+ * of a decode step, 1 = tiled GEMM of the prefill projections, 2 = causal
+ * prefill attention) are counted from 0, and every launch whose count is
+ * a multiple of `stride` (>= 1) takes a pair of events as its own start
+ * and stop timestamps (hipExtLaunchKernel: no marker packets between
+ * kernels). Each timed launch costs a few microseconds more than an
+ * untimed one, so a stride above 1 keeps the timed work close to the
+ * untimed; a stride that shares no factor with the number of launches
+ * per step samples every layer in turn. df_timing_read synchronises the
+ * events and returns the summed duration (ms) and the number of timed
+ * launches, then disables timing. At most 65536 launches are timed.
+ * DF_ERR_ARG for an unknown class or a stride below 1. */
+int df_timing_enable(int32_t kclass, int32_t stride);
 int df_timing_read(double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus

@@ -150,6 +150,7 @@ def test_other_entry_points_reject_bad_arguments():
     assert a(ws=0x70010) == _abi.DF_ERR_ALIGN
     assert a(wsb=16) == _abi.DF_ERR_WORKSPACE
     assert _abi.df_timing_enable(5) == _abi.DF_ERR_ARG
+    assert _abi.df_timing_enable(0, 0) == _abi.DF_ERR_ARG
 
 
 def test_status_strings():

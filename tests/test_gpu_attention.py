@@ -100,3 +100,43 @@ def test_full_attention_workload_sampled():
                 worst = max(worst, max_abs(go[b, f, h], ro), abs(gl[b, f, h] - rl))
     say(f"  sampled max error {worst:.3e}")
     assert worst < TOL
+
+
+def test_sampled_launch_timing():
+    # kernel timing on every third partial-pass launch: 10 calls time calls 0, 3, 6 and 9,
+    # and the timed launches produce the same bits as untimed ones
+    B, H, S, Dh = 3, 2, 700, 128
+    say(f"timing case B={B} H={H} S={S} Dh={Dh} stride 3 over 10 calls")
+    K = synth.normal((B, H, S, Dh), 41, synth.stream_id("t_k"), 1.0, "bf16")
+    V = synth.normal((B, H, S, Dh), 41, synth.stream_id("t_v"), 1.0, "bf16")
+    q = synth.normal((B, 2, H, Dh), 41, synth.stream_id("t_q"), 1.0, "f32")
+    a = synth.normal((H * Dh,), 41, synth.stream_id("t_a"), 1.0, "f32")
+    dK, dV = dev_bf16(K), dev_bf16(V)
+    dq, da = torch.from_numpy(q).cuda(), torch.from_numpy(a).cuda()
+    dl = torch.tensor([700, 1, 333], dtype=torch.int32, device="cuda")
+    wsb = _abi.df_attention_workspace_bytes(B, H, S, Dh)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    outs = []
+
+    def call():
+        o = torch.empty((B, 2, H, Dh), device="cuda")
+        lse = torch.empty((B, 2, H), device="cuda")
+        rc = _abi.df_attention_dual(_abi.DF_BF16, dK.data_ptr(), dV.data_ptr(), B, H, S, Dh, dl.data_ptr(),
+                                    dq.data_ptr(), da.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb,
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, _abi.df_status_str(rc)
+        outs.append((o, lse))
+
+    call()
+    assert _abi.df_timing_enable(0, 3) == 0
+    for _ in range(10):
+        call()
+    rc, ms, n = _abi.df_timing_read()
+    assert rc == 0 and n == 4 and ms > 0.0
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    # reading disables timing
+    call()
+    rc, ms, n = _abi.df_timing_read()
+    assert rc == 0 and n == 0 and ms == 0.0
