@@ -276,6 +276,7 @@ struct Step {
         const bool couple = (c.variant & DF_VARIANT_NO_COUPLING) == 0;   // a, b, c applied
         const int kr = std::max(c.top_k, c.top_k_aux);                   // MoE ranking length
         float* stats = at<float>(L.stats);
+        const int qkv_slices = dfk::plan_gemv(c.dtype, 3 * d, d, nflows == 2 ? 2 * B : B).S;
         bool pending = false;   // h has fresh statistics whose norm has not been applied
         auto set_x = [&](dfk::GemvArgs& g, const float* gain) {
             if (pending && fused) { g.x = h; g.x_stats = stats; g.x_gain = gain; }
@@ -295,10 +296,14 @@ struct Step {
             dfk::GemvArgs g{};
             g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.H = c.n_heads; g.Dh = c.head_dim; g.S_max = c.max_seq;
             g.part = at<float>(L.gpart); g.eps = c.ln_eps;
-            // Q/K/V projection of LN1(h): Q coupling and primary K/V append fused
+            // Q/K/V projection of LN1(h). bf16: its k-slice partial sums go
+            // straight to the attention pass, which sums them, applies the Q
+            // coupling and appends the primary K/V; fp32: the projection's
+            // epilogue does both
             set_x(g, g_ln1);
+            const float* cpl_a = couple ? w.cpl_a + (size_t)l * d : nullptr;
             g.w = reinterpret_cast<const char*>(w.w_qkv) + (size_t)l * 3 * d * d * es;
-            g.N = 3 * d; g.K = d; g.epi = dfk::EPI_QKV; g.cpl = couple ? w.cpl_a + (size_t)l * d : nullptr; g.q_out = q;
+            g.N = 3 * d; g.K = d; g.epi = fused ? dfk::EPI_PART : dfk::EPI_QKV; g.cpl = cpl_a; g.q_out = q;
             g.kc = kc; g.vc = vc; g.len = kv.len; g.status = status;
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             // shared-K/V attention of both queries over positions 0..len[b]
@@ -306,6 +311,9 @@ struct Step {
             a.dtype = c.dtype; a.k = kc; a.v = vc; a.B = B; a.H = c.n_heads; a.S_max = c.max_seq; a.Dh = c.head_dim;
             a.q = q; a.a = nullptr; a.nkeys = kv.len; a.nkeys_add = 1; a.nflows = nflows;
             a.part = at<float>(L.part); a.o_rows = xo;
+            if (fused) {
+                a.qkv_part = g.part; a.qkv_S = qkv_slices; a.a = cpl_a; a.status = status;
+            }
             timing_events(0, &a.ev_start, &a.ev_stop);
             if (dfk::attention(a, s) != hipSuccess) return DF_ERR_HIP;
             // output projection + residual (statistics for LN2)

@@ -40,6 +40,11 @@ struct PartParams {
     int B, H, S_max, nkeys_add, nflows;
     int waves;         // G: waves of the launch
     float scale_log2;  // log2(e) / sqrt(Dh)
+    // fused finish of the Q/K/V projection: its k-slice partial sums
+    // [qkv_S][qkv_M][3 * H * Dh] (nullptr: q holds finished queries)
+    const float* qkv;
+    int qkv_S, qkv_M;
+    int32_t* status;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -58,6 +63,52 @@ __device__ __forceinline__ void unpack(const u32x4& r, float (&x)[EPL]) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sums over the S k-slices (stride floats apart) of EPL consecutive floats at
+// each of the R row pointers, each from 0 in slice order: the order of the
+// projection's own reduce, so the results are the same bits. Loads of four
+// slices of all R rows are in flight together.
+template <int EPL, int R>
+__device__ __forceinline__ void slice_sum(const float* const (&rp)[R], size_t stride, int S, float (&y)[R][EPL]) {
+    constexpr int SB = 4, C = EPL / 4;
+    #pragma unroll
+    for (int r = 0; r < R; ++r)
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) y[r][e] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += SB) {
+        float4 t[SB][R][C];
+        #pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const size_t o = (size_t)min(s0 + u, S - 1) * stride;
+            #pragma unroll
+            for (int r = 0; r < R; ++r)
+                #pragma unroll
+                for (int c = 0; c < C; ++c) t[u][r][c] = *reinterpret_cast<const float4*>(rp[r] + o + 4 * c);
+        }
+        #pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            if (s0 + u >= S) break;
+            #pragma unroll
+            for (int r = 0; r < R; ++r)
+                #pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    y[r][4 * c] += t[u][r][c].x; y[r][4 * c + 1] += t[u][r][c].y;
+                    y[r][4 * c + 2] += t[u][r][c].z; y[r][4 * c + 3] += t[u][r][c].w;
+                }
+        }
+    }
+}
+
+// EPL values rounded to the cache type, as one 16-byte word.
+template <typename T, int EPL>
+__device__ __forceinline__ u32x4 pack_row(const float (&x)[EPL]) {
+    if constexpr (sizeof(T) == 2) {
+        return (u32x4){df::pack_bf16x2(x[0], x[1]), df::pack_bf16x2(x[2], x[3]), df::pack_bf16x2(x[4], x[5]),
+                       df::pack_bf16x2(x[6], x[7])};
+    } else {
+        return (u32x4){__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    }
+}
 
 __device__ __forceinline__ int keys_of(const int32_t* nkeys, int b, int add, int S_max) {
     int n = nkeys[b] + add;
@@ -88,6 +139,10 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     if (blockIdx.x == 0 && threadIdx.x < 64) {   // for the combine pass
         if (lane < p.B) p.seq_tab[lane] = my_off;
         if (lane == 0) p.seq_tab[p.B] = KT;
+        if (p.qkv && p.status) {   // a new key outside the cache is not written
+            const int pos = lane < p.B ? p.nkeys[lane] : 0;
+            if (__ballot(pos < 0 || pos >= p.S_max) != 0 && lane == 0) p.status[0] |= 1;
+        }
     }
 
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -106,15 +161,43 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
         const int end = (int)(min(k_end, pair_lo + n) - pair_lo);
         const int slot = w + b * p.H + h;
         key = pair_lo + end;
-        float q1[EPL], q2[EPL];
+        // the new key (fused finish only): position n - 1 = nkeys[b], the
+        // last key of the pair, lies in this segment
+        const bool fused = p.qkv != nullptr;
+        const bool has_new = fused && end == n && p.nkeys[b] == n - 1;
+        const size_t n3 = (size_t)3 * p.H * DH;
+        const float* qkv_row = fused ? p.qkv + (size_t)(dual ? 2 * b : b) * n3 + h * DH + sub * EPL : nullptr;
+        const size_t qkv_stride = (size_t)p.qkv_M * n3;
+        float q1[EPL], q2[EPL], kn[EPL], vn[EPL];   // kn, vn: the new key's K and V (has_new)
         {
             const float* qp = p.q + ((size_t)(b * 2) * p.H + h) * DH + sub * EPL;
-            #pragma unroll
-            for (int e = 0; e < EPL; ++e) q1[e] = qp[e];
+            if (fused) {
+                // one round of loads: q1, q2raw and, in the segment that
+                // holds the new key, its K and V rows
+                const float* q2r = dual ? qkv_row + n3 : qkv_row;
+                if (has_new) {
+                    const float* rp[4] = {qkv_row, q2r, qkv_row + (size_t)p.H * DH, qkv_row + (size_t)2 * p.H * DH};
+                    float y[4][EPL];
+                    slice_sum<EPL, 4>(rp, qkv_stride, p.qkv_S, y);
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) { q1[e] = y[0][e]; q2[e] = y[1][e]; kn[e] = y[2][e]; vn[e] = y[3][e]; }
+                } else {
+                    const float* rp[2] = {qkv_row, q2r};
+                    float y[2][EPL];
+                    slice_sum<EPL, 2>(rp, qkv_stride, p.qkv_S, y);
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) { q1[e] = y[0][e]; q2[e] = y[1][e]; }
+                }
+            } else {
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) q1[e] = qp[e];
+            }
             if (dual) {
                 const float* q2p = qp + (size_t)p.H * DH;
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e) q2[e] = q2p[e];
+                if (!fused) {
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) q2[e] = q2p[e];
+                }
                 if (p.a) {
                     const float* ap = p.a + h * DH + sub * EPL;
                     #pragma unroll
@@ -136,18 +219,44 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
         #pragma unroll
         for (int e = 0; e < EPL; ++e) { o1[e] = 0.f; o2[e] = 0.f; }
 
-        for (int j0 = start; j0 < end; j0 += PPW * U) {
+        int kend = end;   // keys read from the cache: [start, kend)
+        if (has_new) {
+            // K and V of the primary row (slice sums), rounded to the cache
+            // type, written to the cache at the new position by lane group 0,
+            // then attended first (lane group 0 starts its state with it)
+            const u32x4 kw = pack_row<T, EPL>(kn), vw = pack_row<T, EPL>(vn);
+            if (g == 0) {
+                *reinterpret_cast<u32x4*>(const_cast<T*>(kp) + (size_t)(n - 1) * DH) = kw;
+                *reinterpret_cast<u32x4*>(const_cast<T*>(vp) + (size_t)(n - 1) * DH) = vw;
+            }
+            unpack<T, EPL>(kw, kn);
+            unpack<T, EPL>(vw, vn);
+            float a1 = 0.f, a2 = 0.f;
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) { a1 = fmaf(q1[e], kn[e], a1); a2 = fmaf(q2[e], kn[e], a2); }
+            a1 = df::group_sum<LPP>(a1);
+            if (dual) a2 = df::group_sum<LPP>(a2);
+            if (g == 0) {
+                m1 = a1; l1 = 1.f;
+                if (dual) { m2 = a2; l2 = 1.f; }
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) { o1[e] = vn[e]; o2[e] = dual ? vn[e] : 0.f; }
+            }
+            kend = end - 1;
+        }
+
+        for (int j0 = start; j0 < kend; j0 += PPW * U) {
             u32x4 kr[U], vr[U];
             #pragma unroll
             for (int u = 0; u < U; ++u) {
                 int j = j0 + u * PPW + g;
-                j = j < end ? j : end - 1;
+                j = j < kend ? j : kend - 1;
                 kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)j * DH));
             }
             #pragma unroll
             for (int u = 0; u < U; ++u) {
                 int j = j0 + u * PPW + g;
-                j = j < end ? j : end - 1;
+                j = j < kend ? j : kend - 1;
                 vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)j * DH));
             }
             float s1[U], s2[U];
@@ -160,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
                 for (int e = 0; e < EPL; ++e) { a1 = fmaf(q1[e], kk[e], a1); a2 = fmaf(q2[e], kk[e], a2); }
                 a1 = df::group_sum<LPP>(a1);
                 if (dual) a2 = df::group_sum<LPP>(a2);
-                const bool valid = (j0 + u * PPW + g) < end;
+                const bool valid = (j0 + u * PPW + g) < kend;
                 s1[u] = valid ? a1 : -INFINITY;
                 s2[u] = valid ? a2 : -INFINITY;
             }
@@ -336,6 +445,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     p.B = a.B; p.H = a.H; p.S_max = a.S_max; p.nkeys_add = a.nkeys_add; p.nflows = a.nflows;
     p.waves = waves;
     p.scale_log2 = df::kLog2e / sqrtf((float)DH);
+    p.qkv = a.qkv_part; p.qkv_S = a.qkv_S; p.qkv_M = a.nflows == 2 ? 2 * a.B : a.B; p.status = a.status;
+    if (p.qkv && (a.nkeys_add != 1 || a.qkv_S < 1)) return hipErrorInvalidValue;
     void* args[] = {&p};
     hipError_t e = launch_timed(reinterpret_cast<const void*>(&attn_partial<T, DH, U>), dim3(waves / 4), dim3(256),
                                 args, 0, s, a.ev_start, a.ev_stop);

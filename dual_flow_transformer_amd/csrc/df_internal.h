@@ -38,6 +38,16 @@ struct AttnArgs {
     float* o_rows;            // [2B][H*Dh] fp32 output rows (projection input), or nullptr
     hipEvent_t ev_start;      // optional events: start and stop timestamps of the partial pass
     hipEvent_t ev_stop;
+    // Fused finish of the Q/K/V projection (qkv_part != nullptr; then q is unused and
+    // nkeys_add must be 1): q1, q2raw and the primary K/V of the new position
+    // nkeys[b] are the slice sums of the projection's EPI_PART partials
+    // [qkv_S][M][3*H*Dh] (M = 2B rows with both flows, else B), the same sums in the
+    // same order as its reduce; the new K/V row is rounded to the cache type,
+    // written at position nkeys[b] (when 0 <= nkeys[b] < S_max; else bit 0 of
+    // status[0] is set) and attended from registers.
+    const float* qkv_part;
+    int qkv_S;
+    int32_t* status;
 };
 size_t attention_part_floats(int B, int H, int S_max, int Dh);
 hipError_t attention(const AttnArgs& a, hipStream_t s);
@@ -90,6 +100,8 @@ enum EpiKind {
     EPI_QKV = 1,       // Q rows (+ a coupling) to q_out, primary K/V appended to the cache
     EPI_GELU_B = 2,    // g = GELU(y), g2 += b*g1, g to x_out
     EPI_RESID = 3,     // (optional c coupling) h[m][n] += y; per-segment statistics of h to stats_out
+    EPI_PART = 4,      // bf16 only: the k-slice partial sums to part[s][m][n] (every S), no finish;
+                       // the consumer sums the slices in slice order (attention with AttnArgs::qkv_part)
 };
 
 struct GemvArgs {

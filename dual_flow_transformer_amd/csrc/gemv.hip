@@ -13,7 +13,7 @@
 // the B operand from LDS; split over k-slices, persistent over row tiles;
 // partial sums are finished by a reduce kernel with one of the epilogues:
 // plain store, Q coupling + K/V append, GELU + b coupling, or c coupling +
-// residual add (then LayerNorm). fp32 path (fp32 storage, row-major): one
+// residual add (then LayerNorm), or left for the next kernel (EPI_PART). fp32 path (fp32 storage, row-major): one
 // wave per weight row, lanes split K, wave reduction, same epilogues.
 #include <algorithm>
 
@@ -145,7 +145,9 @@ __device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&ac
 // iteration past the end reads a fixed hot address) so the compiler's wait
 // counts stay exact. With S > 1 each tile's partial sums go to
 // part[s][m][n] and a reduce kernel finishes in slice order; with S == 1
-// the epilogue runs from the registers.
+// the epilogue runs from the registers. EPI_PART always leaves the partial
+// sums for the consumer to finish (the Q/K/V projection, which the
+// attention pass finishes).
 template <int MT, int RT, int KU, int NW, int KS, int NBUF>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     extern __shared__ bf16_t xs[];
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
             #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const int nb = tile * TR + rt * 16;
-                if (S > 1 || p.epi == EPI_RESID) {
+                if (S > 1 || p.epi == EPI_RESID || p.epi == EPI_PART) {
                     #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const int m = mt * 16 + li, n0 = nb + 4 * lg;
@@ -507,7 +509,7 @@ hipError_t finish(GParams& p, int S, hipStream_t s) {
         hipLaunchKernelGGL(gemv_reduce_resid, dim3(stat_segs(p.N), p.B), dim3(kStatSeg), 0, s, p, S);
         return hipGetLastError();
     }
-    if (S > 1) {
+    if (S > 1 && p.epi != EPI_PART) {
         const long total = (long)p.B * p.N;
         hipLaunchKernelGGL(gemv_reduce_epi, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p, S);
         return hipGetLastError();
@@ -559,7 +561,7 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     p.kc = a.kc; p.vc = a.vc; p.len = a.len; p.H = a.H; p.Dh = a.Dh; p.S_max = a.S_max; p.status = a.status;
     p.part = a.part; p.eps = a.eps;
     if (a.dtype == DF_F32) {
-        if (p.M > 16) return hipErrorInvalidValue;
+        if (p.M > 16 || a.epi == EPI_PART) return hipErrorInvalidValue;
         if (a.x_stats) return hipErrorInvalidValue;   // fp32 rows are normalised by ln_apply
         if (a.epi == EPI_RESID && (!a.part || a.N > 4096)) return hipErrorInvalidValue;
         (void)hipGetLastError();
@@ -571,7 +573,7 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M);
     if (pl.MT == 0) return hipErrorInvalidValue;
     p.S = pl.S;
-    if ((pl.S > 1 || a.epi == EPI_RESID) && !a.part) return hipErrorInvalidValue;
+    if ((pl.S > 1 || a.epi == EPI_RESID || a.epi == EPI_PART) && !a.part) return hipErrorInvalidValue;
     if (a.epi == EPI_RESID && a.N > 4096) return hipErrorInvalidValue;
     if (a.x_stats && (!a.x_gain || a.K > kMaxSeg * kStatSeg)) return hipErrorInvalidValue;
     hipError_t e;
