@@ -35,10 +35,10 @@ TIMING_STRIDE = 7
 # write). Reported only while the kernel sources are the ones they were measured on.
 COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "aaf8f1603eba27bb2207f89439dae5682a41cae1351166434c9e750def3f8eba",
-    "attention_traffic_bytes_per_launch": 2.1502e9,
-    "library_sources_sha256": "c75d512e5bea15cec6e70f20e9cb81cc42a922113e2fbb0946d5d784aca1da1d",
-    "step_traffic_bytes": {"dual": 84.713e9, "primary_only": 83.322e9},
+    "attention_source_sha256": "972630f32691967517176f529076b5d2378ac871d919a3ba753c6bd50b155f59",
+    "attention_traffic_bytes_per_launch": 2.1545e9,
+    "library_sources_sha256": "224acbc71a2e62ddf1996d6f76e824c3ef1f7f6cc27c01df01d87d137ab37da3",
+    "step_traffic_bytes": {"dual": 84.621e9, "primary_only": 83.305e9},
 }
 
 
