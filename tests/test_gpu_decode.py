@@ -134,6 +134,32 @@ def test_tiny_fp32_end_to_end():
         assert max_abs(gm.v[l, :, :, :n].cpu().numpy(), V[:, :, :n]) < 1e-4
 
 
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_F32], ids=lambda c: c.name)
+def test_cache_edge_positions(cfg):
+    """New key in the last cache slot, a full cache and a short sequence in one
+    step: the last slot is written, the full sequence's cache is untouched and
+    flagged in the status word (bit 0), the short one writes at its length."""
+    say(f"cache edges {cfg.name}")
+    gm = DecodeModel(cfg, fill="device")
+    S = gm.S
+    lens = [S - 1, S, 5] + [7] * (cfg.B - 3)
+    lens = lens[:cfg.B]
+    gm.len.copy_(torch.tensor(lens, dtype=torch.int32))
+    k0, v0 = gm.k.clone(), gm.v.clone()
+    gm.decode_step(gm.tokens(Inputs(cfg).step_tokens(0)))
+    torch.cuda.synchronize()
+    assert gm.status() & 1
+    assert torch.isfinite(gm.logits).all() and torch.isfinite(gm.p_mix).all()
+    for name, t, t0 in (("k", gm.k, k0), ("v", gm.v, v0)):
+        changed = (t != t0).any(dim=-1).cpu().numpy()          # [L, B, H, S]
+        want = np.zeros_like(changed)
+        for b, n in enumerate(lens):
+            if 0 <= n < S:
+                want[:, b, :, n] = True
+        assert np.array_equal(changed, want), f"{name}: cache rows written {np.argwhere(changed != want)[:4]}"
+    assert gm.status() == 0          # reading the status word clears it
+
+
 @pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_MOE], ids=lambda c: c.name)
 def test_primary_independent_of_aux(cfg):
     """Primary logits and every cache byte are bitwise the same with the aux
