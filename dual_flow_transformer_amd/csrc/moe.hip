@@ -319,6 +319,45 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows,
         s_g[1][tid] = dual ? gates[((size_t)b * 2 + 1) * kr + tid] : 0.f;
     }
     __syncthreads();
+    // gate-weighted sums: the expert outputs of four ranks at a time (every
+    // column of the thread, both flows) are loaded together; each sum still
+    // adds its ranks in rank order
+    float y1[kCombCols], y2[kCombCols];
+    #pragma unroll
+    for (int c = 0; c < kCombCols; ++c) y1[c] = y2[c] = 0.f;
+    const int nj = dual ? max(k, ka) : k;
+    for (int j0 = 0; j0 < nj; j0 += 4) {
+        float t1[4][kCombCols], t2[4][kCombCols];
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const size_t r = (size_t)s_slot[min(j0 + u, nj - 1)] * 2 * d;
+            #pragma unroll
+            for (int c = 0; c < kCombCols; ++c) {
+                const int n = min(tid + kCombThreads * c, d - 1);
+                t1[u][c] = y_rows[r + n];
+                t2[u][c] = dual ? y_rows[r + d + n] : 0.f;
+            }
+        }
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u;
+            #pragma unroll
+            for (int c = 0; c < kCombCols; ++c) {
+                if (j < k) y1[c] = fmaf(s_g[0][j], t1[u][c], y1[c]);
+                if (dual && j < ka) y2[c] = fmaf(s_g[1][j], t2[u][c], y2[c]);
+            }
+        }
+    }
+    // residual rows, coupling and gains of every column, loaded together
+    float h1v[kCombCols], h2v[kCombCols], cv[kCombCols], gv[kCombCols];
+    #pragma unroll
+    for (int c = 0; c < kCombCols; ++c) {
+        const int n = min(tid + kCombThreads * c, d - 1);
+        h1v[c] = h[(size_t)(2 * b) * d + n];
+        h2v[c] = dual ? h[(size_t)(2 * b + 1) * d + n] : 0.f;
+        cv[c] = (dual && cpl_c) ? cpl_c[n] : 0.f;
+        gv[c] = x_next ? g_next[n] : 0.f;
+    }
     float v1[kCombCols], v2[kCombCols];
     float s1 = 0.f, s2 = 0.f;
     #pragma unroll
@@ -326,19 +365,15 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows,
         const int n = tid + kCombThreads * c;
         v1[c] = v2[c] = 0.f;
         if (n >= d) continue;
-        float y1 = 0.f, y2 = 0.f;
-        for (int j = 0; j < k; ++j) y1 = fmaf(s_g[0][j], y_rows[((size_t)s_slot[j] * 2) * d + n], y1);
-        if (dual)
-            for (int j = 0; j < ka; ++j) y2 = fmaf(s_g[1][j], y_rows[((size_t)s_slot[j] * 2 + 1) * d + n], y2);
         float* h1 = h + (size_t)(2 * b) * d + n;
-        v1[c] = *h1 + y1;
+        v1[c] = h1v[c] + y1[c];
         *h1 = v1[c];
         s1 += v1[c];
         if (dual) {
-            if (cpl_c) y2 = fmaf(cpl_c[n], y1, y2);   // output coupling c_l
-            float* h2 = h1 + d;
-            v2[c] = *h2 + y2;
-            *h2 = v2[c];
+            float yy2 = y2[c];
+            if (cpl_c) yy2 = fmaf(cv[c], y1[c], yy2);   // output coupling c_l
+            v2[c] = h2v[c] + yy2;
+            h1[d] = v2[c];
             s2 += v2[c];
         }
     }
@@ -358,8 +393,8 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows,
     for (int c = 0; c < kCombCols; ++c) {
         const int n = tid + kCombThreads * c;
         if (n >= d) continue;
-        x_next[(size_t)(2 * b) * d + n] = (v1[c] - mean1) * rstd1 * g_next[n];
-        if (dual) x_next[(size_t)(2 * b + 1) * d + n] = (v2[c] - mean2) * rstd2 * g_next[n];
+        x_next[(size_t)(2 * b) * d + n] = (v1[c] - mean1) * rstd1 * gv[c];
+        if (dual) x_next[(size_t)(2 * b + 1) * d + n] = (v2[c] - mean2) * rstd2 * gv[c];
     }
 }
 

@@ -11,10 +11,11 @@ namespace {
 constexpr int kRowThreads = 256;
 constexpr int kMaxPerThread = 16;   // d <= 4096
 
-// LayerNorm of one row held in registers (x[e] is element tid + e*256);
-// the normalised row is written in fp32 (projection inputs are not rounded).
-__device__ void ln_store(const float (&x)[kMaxPerThread], int d, const float* g, float eps, float* out,
-                         float* red) {
+// LayerNorm of one row held in registers (x[e] is element tid + e*256, g[e]
+// its gain); the normalised row is written in fp32 (projection inputs are not
+// rounded).
+__device__ void ln_store(const float (&x)[kMaxPerThread], const float (&g)[kMaxPerThread], int d, float eps,
+                         float* out, float* red) {
     const int tid = threadIdx.x;
     float s = 0.f;
     #pragma unroll
@@ -34,7 +35,7 @@ __device__ void ln_store(const float (&x)[kMaxPerThread], int d, const float* g,
     #pragma unroll
     for (int e = 0; e < kMaxPerThread; ++e) {
         const int i = tid + e * kRowThreads;
-        if (i < d) out[i] = (x[e] - mean) * rstd * g[i];
+        if (i < d) out[i] = (x[e] - mean) * rstd * g[e];
     }
 }
 
@@ -56,17 +57,24 @@ __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
         const T* e = (f == 0 ? emb0 : emb1) + (size_t)t * d;
         const T* pe = pos_emb + (size_t)pos * d;
         const size_t row = (size_t)(2 * b + f) * d;
+        // all loads first, unconditional (a column past d reads column d - 1
+        // and is masked), so they are in flight together
+        float xe[kMaxPerThread], xp[kMaxPerThread], gv[kMaxPerThread];
+        #pragma unroll
+        for (int k = 0; k < kMaxPerThread; ++k) {
+            const int i = min((int)threadIdx.x + k * kRowThreads, d - 1);
+            xe[k] = df::St<T>::ld(e, i);
+            xp[k] = df::St<T>::ld(pe, i);
+            gv[k] = g[i];
+        }
         float xv[kMaxPerThread];
         #pragma unroll
         for (int k = 0; k < kMaxPerThread; ++k) {
             const int i = threadIdx.x + k * kRowThreads;
-            xv[k] = 0.f;
-            if (i < d) {
-                xv[k] = df::St<T>::ld(e, i) + df::St<T>::ld(pe, i);
-                h[row + i] = xv[k];
-            }
+            xv[k] = i < d ? xe[k] + xp[k] : 0.f;
+            if (i < d) h[row + i] = xv[k];
         }
-        ln_store(xv, d, g, eps, x + row, red);
+        ln_store(xv, gv, d, eps, x + row, red);
     }
 }
 
