@@ -84,16 +84,46 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
             w[u] = *reinterpret_cast<const u32x4*>(wp + (size_t)min(kb0 + u, kbs - 1) * 512);
     };
     load(it, 0);
-    for (int f = 0; f < p.nflows; ++f) {
-        const int row = 2 * b + f;
-        const float2 mr = df::row_norm_from_segments(reinterpret_cast<const float2*>(p.stats) + (size_t)row * nseg,
-                                                     nseg, kStatSeg, d, p.eps);
-        for (int k = tid * 4; k < d; k += kGateThreads * 4) {
-            const float4 hv = *reinterpret_cast<const float4*>(p.h + (size_t)row * d + k);
-            const float4 gv = *reinterpret_cast<const float4*>(p.g + k);
-            const float4 v = make_float4((hv.x - mr.x) * mr.y * gv.x, (hv.y - mr.x) * mr.y * gv.y,
-                                         (hv.z - mr.x) * mr.y * gv.z, (hv.w - mr.x) * mr.y * gv.w);
-            *reinterpret_cast<float4*>(p.x + (size_t)row * d + k) = v;
+    {
+        // residual values of both rows (one float4 per thread and row:
+        // d <= 4 * kGateThreads) and the gains, in flight while wave 0 forms
+        // the row norms: lane 16 f + i loads segment i of row f, and the
+        // segments are added in order through shuffles (the arithmetic of
+        // row_norm_from_segments, without its chain of dependent loads)
+        __shared__ float2 s_mr[2];
+        const int k = min(tid * 4, d - 4);
+        float4 hv[2];
+        #pragma unroll
+        for (int f = 0; f < 2; ++f)
+            hv[f] = *reinterpret_cast<const float4*>(p.h + (size_t)(2 * b + (dual ? f : 0)) * d + k);
+        const float4 gv = *reinterpret_cast<const float4*>(p.g + k);
+        if (wv == 0) {
+            const int f = (lane >> 4) & 1, i = lane & 15;
+            const float2 sv = reinterpret_cast<const float2*>(p.stats)[(size_t)(2 * b + (dual ? f : 0)) * nseg +
+                                                                        min(i, nseg - 1)];
+            #pragma unroll
+            for (int ff = 0; ff < 2; ++ff) {
+                float mean = 0.f;
+                for (int j = 0; j < nseg; ++j)
+                    mean += (float)min(kStatSeg, d - j * kStatSeg) * __shfl(sv.x, 16 * ff + j, 64);
+                mean /= (float)d;
+                float m2 = 0.f;
+                for (int j = 0; j < nseg; ++j) {
+                    const float dm = __shfl(sv.x, 16 * ff + j, 64) - mean;
+                    m2 += __shfl(sv.y, 16 * ff + j, 64) + (float)min(kStatSeg, d - j * kStatSeg) * dm * dm;
+                }
+                if (lane == 0) s_mr[ff] = make_float2(mean, 1.0f / sqrtf(m2 / (float)d + p.eps));
+            }
+        }
+        __syncthreads();
+        #pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            if (f >= p.nflows || tid * 4 >= d) break;
+            const float2 mr = s_mr[f];
+            const float4 h4 = hv[f];
+            const float4 v = make_float4((h4.x - mr.x) * mr.y * gv.x, (h4.y - mr.x) * mr.y * gv.y,
+                                         (h4.z - mr.x) * mr.y * gv.z, (h4.w - mr.x) * mr.y * gv.w);
+            *reinterpret_cast<float4*>(p.x + (size_t)(2 * b + f) * d + k) = v;
             *reinterpret_cast<float4*>(s_x + f * d + k) = v;
         }
     }
