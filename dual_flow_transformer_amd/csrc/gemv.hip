@@ -69,11 +69,12 @@ __device__ __forceinline__ void epilogue(const GParams& p, int n, int b, float y
             if (dual) p.out_f32[r2] = y2;
             break;
         case EPI_GELU_B: {
+            const float cb = (dual && p.cpl) ? p.cpl[n] : 0.f;   // loaded before any store
             const float g1 = gelu(y1);
             p.x_out[r1] = g1;
             if (dual) {
                 float g2 = gelu(y2);
-                if (p.cpl) g2 = fmaf(p.cpl[n], g1, g2);          // MLP-intermediate coupling (b_l)
+                if (p.cpl) g2 = fmaf(cb, g1, g2);                 // MLP-intermediate coupling (b_l)
                 p.x_out[r2] = g2;
             }
             break;
@@ -82,8 +83,9 @@ __device__ __forceinline__ void epilogue(const GParams& p, int n, int b, float y
             const int d = p.H * p.Dh;
             if (n < d) {
                 const size_t q1 = (size_t)(2 * b) * d + n;
+                const float ca = (dual && p.cpl) ? p.cpl[n] : 0.f;   // loaded before the first store
                 p.q_out[q1] = y1;
-                if (dual) p.q_out[q1 + d] = p.cpl ? fmaf(p.cpl[n], y1, y2) : y2;   // Q2 = Q2raw + a*Q1
+                if (dual) p.q_out[q1 + d] = p.cpl ? fmaf(ca, y1, y2) : y2;   // Q2 = Q2raw + a*Q1
             } else {
                 // primary K/V only; the aux row's K/V part is discarded
                 const int kvsel = (n - d) / d;
@@ -382,15 +384,20 @@ __global__ __launch_bounds__(kStatSeg) void gemv_reduce_resid(GParams p, int S) 
     const bool dual = p.nflows == 2;
     float v1 = 0.f, v2 = 0.f;
     if (ok) {
+        // every load (residual rows, coupling) before the first store, so
+        // they are in flight with the partial sums
+        float* h1 = p.h + (size_t)(2 * b) * p.N + n;
+        float* h2 = p.h + (size_t)(2 * b + 1) * p.N + n;
+        const float h1v = *h1;
+        const float h2v = dual ? *h2 : 0.f;
+        const float cc = (dual && p.cpl) ? p.cpl[n] : 0.f;
         float y1, y2;
         sum_slices(p, S, dual ? 2 * b : b, dual ? 2 * b + 1 : -1, n, y1, y2);
-        float* h1 = p.h + (size_t)(2 * b) * p.N + n;
-        v1 = *h1 + y1;
+        v1 = h1v + y1;
         *h1 = v1;
         if (dual) {
-            if (p.cpl) y2 = fmaf(p.cpl[n], y1, y2);   // MLP-output coupling (c_l)
-            float* h2 = p.h + (size_t)(2 * b + 1) * p.N + n;
-            v2 = *h2 + y2;
+            if (p.cpl) y2 = fmaf(cc, y1, y2);   // MLP-output coupling (c_l)
+            v2 = h2v + y2;
             *h2 = v2;
         }
     }

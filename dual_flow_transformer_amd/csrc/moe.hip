@@ -311,12 +311,14 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
             const float y2 = p.nflows == 2 ? tile::lds_sum<MT>(red, NW, nl, ml + 1) : 0.f;
             const int t = s_pairs[mbase / p.nflows + q];
             if (p.up) {
+                const bool cpl = p.cpl_b && p.nflows == 2 && t % p.kk < p.kp;
+                const float cb = cpl ? p.cpl_b[n] : 0.f;   // loaded before the first store
                 const float g1 = 0.5f * y1 * (1.0f + erff(y1 * 0.70710678118654752f));
                 p.g_out[((size_t)t * 2) * p.N + n] = g1;
                 if (p.nflows == 2) {
                     float g2 = 0.5f * y2 * (1.0f + erff(y2 * 0.70710678118654752f));
                     // intermediate coupling b_l, per expert the primary also ran (rank < kp)
-                    if (p.cpl_b && t % p.kk < p.kp) g2 = fmaf(p.cpl_b[n], g1, g2);
+                    if (cpl) g2 = fmaf(cb, g1, g2);
                     p.g_out[((size_t)t * 2 + 1) * p.N + n] = g2;
                 }
             } else {
