@@ -42,10 +42,9 @@ __device__ void ln_store(const float (&x)[kMaxPerThread], const float (&g)[kMaxP
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void embed_ln_kernel(
     const T* emb0, const T* emb1, const T* pos_emb, const int32_t* tok, int tok_stride,
-    const int32_t* len, int d, int S_max, int V, int nflows, const float* g, float eps, float* h, float* x,
-    int32_t* status) {
+    const int32_t* len, int d, int S_max, int V, const float* g, float eps, float* h, float* x, int32_t* status) {
     __shared__ float red[16];
-    const int b = blockIdx.x, f = blockIdx.y;   // one workgroup per stacked row
+    const int b = blockIdx.x, f = blockIdx.y;   // one workgroup per stacked row (grid y: the flows)
     int pos = len[b];
     pos = pos < 0 ? 0 : (pos >= S_max ? S_max - 1 : pos);
     int t = tok[(size_t)b * tok_stride];
@@ -285,12 +284,12 @@ hipError_t embed_ln(int dtype, const void* emb0, const void* emb1, const void* p
     (void)hipGetLastError();
     if (dtype == DF_BF16)
         hipLaunchKernelGGL(embed_ln_kernel<bf16_t>, dim3(B, nflows), dim3(kRowThreads), 0, s, (const bf16_t*)emb0,
-                           (const bf16_t*)emb1, (const bf16_t*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
-                           g, eps, h, (float*)x, status);
+                           (const bf16_t*)emb1, (const bf16_t*)pos_emb, tok, tok_stride, len, d, S_max, V, g,
+                           eps, h, (float*)x, status);
     else
         hipLaunchKernelGGL(embed_ln_kernel<float>, dim3(B, nflows), dim3(kRowThreads), 0, s, (const float*)emb0,
-                           (const float*)emb1, (const float*)pos_emb, tok, tok_stride, len, d, S_max, V, nflows,
-                           g, eps, h, (float*)x, status);
+                           (const float*)emb1, (const float*)pos_emb, tok, tok_stride, len, d, S_max, V, g,
+                           eps, h, (float*)x, status);
     return hipGetLastError();
 }
 
