@@ -37,8 +37,8 @@ COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
     "attention_source_sha256": "972630f32691967517176f529076b5d2378ac871d919a3ba753c6bd50b155f59",
     "attention_traffic_bytes_per_launch": 2.1545e9,
-    "library_sources_sha256": "202694a4628804d0e598469c8d9c04653363ee298bb9882246ca41aff0de6fe6",
-    "step_traffic_bytes": {"dual": 84.620e9, "primary_only": 83.305e9},
+    "library_sources_sha256": "b5f7e1296ab07552ea01130e375e7f0295e1362c3b576e7a7d41c15279811c23",
+    "step_traffic_bytes": {"dual": 84.620e9, "primary_only": 83.303e9},
 }
 
 
