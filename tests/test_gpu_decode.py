@@ -20,6 +20,10 @@ pytestmark = pytest.mark.gpu
 
 SMALL_BF16 = Config("gpu_small_bf16", L=2, d=256, H=2, Dh=128, F=1024, V=512, B=3, ctx=300, S_max=320,
                     dtype="bf16", seed=21, sigma_w=0.05, sigma_ln=0.1)
+# d 768: the Q/K/V projection splits K into 3 slices, a count the attention
+# pass's slice sums take in a ragged batch
+SMALL_BF16_S3 = Config("gpu_small_bf16_s3", L=2, d=768, H=6, Dh=128, F=1536, V=512, B=3, ctx=200, S_max=224,
+                       dtype="bf16", seed=24, sigma_w=0.05, sigma_ln=0.1)
 SMALL_F32 = Config("gpu_small_f32", L=2, d=128, H=2, Dh=64, F=256, V=300, B=2, ctx=40, S_max=64,
                    dtype="f32", seed=22, sigma_w=0.05, sigma_ln=0.1)
 SMALL_MOE = Config("gpu_small_moe", L=2, d=256, H=2, Dh=128, F=0, V=512, B=8, ctx=40, S_max=64, dtype="bf16",
@@ -69,7 +73,7 @@ def _check_writes(gm, cfg, lens0, cache: odf.Cache, sentinel):
                 assert np.all(np.abs(got - ref) <= ulp * np.abs(ref) + KV_ABS), f"{name} values l={l} b={b}"
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_F32], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_BF16_S3, SMALL_F32], ids=lambda c: c.name)
 def test_small_dense_steps(cfg):
     say(f"decode case {cfg.name}")
     gm = DecodeModel(cfg, fill="host")
