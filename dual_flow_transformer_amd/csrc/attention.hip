@@ -65,21 +65,24 @@ __device__ __forceinline__ void unpack(const u32x4& r, float (&x)[EPL]) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sums over the S k-slices (stride floats apart) of EPL consecutive floats at
-// each of the R row pointers, each from 0 in slice order: the order of the
-// projection's own reduce, so the results are the same bits. Loads of four
-// slices of all R rows are in flight together.
-template <int EPL, int R>
-__device__ __forceinline__ void slice_sum(const float* const (&rp)[R], size_t stride, int S, float (&y)[R][EPL]) {
-    constexpr int SB = 4, C = EPL / 4;
+// each of the R row pointers. The PPW lane groups of a wave hold the same
+// elements, so group g loads slices g, g + PPW, ... (adding them in that
+// order; all of them in one round while S <= 2 PPW), and the group sums are
+// then added across the groups by xor-shuffles; an addition is commutative,
+// so every lane ends with the same bits.
+template <int EPL, int R, int PPW>
+__device__ __forceinline__ void slice_sum(const float* const (&rp)[R], size_t stride, int S, int g,
+                                          float (&y)[R][EPL]) {
+    constexpr int SB = 2, C = EPL / 4, LPP = 64 / PPW;
     #pragma unroll
     for (int r = 0; r < R; ++r)
         #pragma unroll
         for (int e = 0; e < EPL; ++e) y[r][e] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += SB) {
+    for (int s0 = g; s0 < S; s0 += SB * PPW) {
         float4 t[SB][R][C];
         #pragma unroll
         for (int u = 0; u < SB; ++u) {
-            const size_t o = (size_t)min(s0 + u, S - 1) * stride;
+            const size_t o = (size_t)min(s0 + u * PPW, S - 1) * stride;
             #pragma unroll
             for (int r = 0; r < R; ++r)
                 #pragma unroll
@@ -87,7 +90,7 @@ __device__ __forceinline__ void slice_sum(const float* const (&rp)[R], size_t st
         }
         #pragma unroll
         for (int u = 0; u < SB; ++u) {
-            if (s0 + u >= S) break;
+            if (s0 + u * PPW >= S) break;
             #pragma unroll
             for (int r = 0; r < R; ++r)
                 #pragma unroll
@@ -97,6 +100,12 @@ __device__ __forceinline__ void slice_sum(const float* const (&rp)[R], size_t st
                 }
         }
     }
+    #pragma unroll
+    for (int o = LPP; o < 64; o <<= 1)
+        #pragma unroll
+        for (int r = 0; r < R; ++r)
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) y[r][e] += __shfl_xor(y[r][e], o, 64);
 }
 
 // EPL values rounded to the cache type, as one 16-byte word.
@@ -178,13 +187,13 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
                 if (has_new) {
                     const float* rp[4] = {qkv_row, q2r, qkv_row + (size_t)p.H * DH, qkv_row + (size_t)2 * p.H * DH};
                     float y[4][EPL];
-                    slice_sum<EPL, 4>(rp, qkv_stride, p.qkv_S, y);
+                    slice_sum<EPL, 4, PPW>(rp, qkv_stride, p.qkv_S, g, y);
                     #pragma unroll
                     for (int e = 0; e < EPL; ++e) { q1[e] = y[0][e]; q2[e] = y[1][e]; kn[e] = y[2][e]; vn[e] = y[3][e]; }
                 } else {
                     const float* rp[2] = {qkv_row, q2r};
                     float y[2][EPL];
-                    slice_sum<EPL, 2>(rp, qkv_stride, p.qkv_S, y);
+                    slice_sum<EPL, 2, PPW>(rp, qkv_stride, p.qkv_S, g, y);
                     #pragma unroll
                     for (int e = 0; e < EPL; ++e) { q1[e] = y[0][e]; q2[e] = y[1][e]; }
                 }

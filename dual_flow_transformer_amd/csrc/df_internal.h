@@ -41,8 +41,8 @@ struct AttnArgs {
     // Fused finish of the Q/K/V projection (qkv_part != nullptr; then q is unused and
     // nkeys_add must be 1): q1, q2raw and the primary K/V of the new position
     // nkeys[b] are the slice sums of the projection's EPI_PART partials
-    // [qkv_S][M][3*H*Dh] (M = 2B rows with both flows, else B), the same sums in the
-    // same order as its reduce; the new K/V row is rounded to the cache type,
+    // [qkv_S][M][3*H*Dh] (M = 2B rows with both flows, else B), added in a fixed order
+    // (deterministic, the same for both flows); the new K/V row is rounded to the cache type,
     // written at position nkeys[b] (when 0 <= nkeys[b] < S_max; else bit 0 of
     // status[0] is set) and attended from registers.
     const float* qkv_part;
