@@ -70,6 +70,25 @@ def pin_round_bf16():
         assert odf.round_to(np.array([x]), "bf16")[0] == r, (x, r)
 
 
+def pin_decode_bf16():
+    """decode_bf16 against torch's bf16 -> float64 conversion over all 65536
+    bit patterns: every finite value exactly (with the sign of zero and the
+    subnormals), both infinities, and NaN patterns decoding to NaN."""
+    u16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(u16.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):          # signalling-NaN patterns
+        got = odf.decode_bf16(u16)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "NaN patterns differ"
+    assert np.array_equal(got[~nan], want[~nan]), "finite / infinite values differ"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), "sign of zero differs"
+    # hand-worked patterns: 1.0, -2.0, the smallest subnormal, the largest finite value
+    hand = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,
+            0x7F80: np.inf, 0xFF80: -np.inf}
+    for bits, val in hand.items():
+        assert odf.decode_bf16(np.array([bits], dtype=np.uint16))[0] == val, hex(bits)
+
+
 def pin_layer_norm():
     """LayerNorm against torch.nn.functional.layer_norm (float64, gain only)."""
     r = _rng(2)
@@ -671,12 +690,95 @@ def pin_forward_causal(cfg):
     assert np.min(np.max(np.abs(a.logits[:, -1] - b.logits[:, -1]), axis=-1)) > 1e-6
 
 
-ALL_BASIC = [pin_round_bf16, pin_layer_norm, pin_gelu, pin_attention_sdpa, pin_attention_closed_forms,
-             pin_attention_dual, pin_mix_properties, pin_mix_golden, pin_topk, pin_mix_aux_mode,
-             pin_mix_half_mode]
+
+def pin_run_tiny_schedule(cfg):
+    """The end-to-end run's schedule ([ES] Arquitectura Central: the aux flow
+    is skipped in prefill and active from the last prompt position on): the
+    primary prefill covers positions 0..T-2, step 0 consumes the last prompt
+    token at position T-1 with the aux flow on, step s > 0 consumes the token
+    step s-1 chose, and len ends at T-1+n with exactly positions 0..T-2+n
+    written. Checked against the full-sequence forward over the consumed
+    tokens: its position T-1+s holds both flows' logits, since the aux state
+    at a position depends on earlier positions only through the primary K/V."""
+    n = 3
+    c = cfg.replace(ctx=0, n_steps=n)
+    src = Inputs(c)
+    prompt = src.prompt()
+    T = prompt.shape[1]
+    cache, res = odf.run_tiny(odf.Model(src))
+    assert len(res) == n
+    assert np.array_equal(cache.lens, np.full(c.B, T - 1 + n))
+    for l in range(c.L):
+        for b in range(c.B):
+            written = sorted(pos for (ll, bb, pos) in cache.appended if ll == l and bb == b)
+            assert written == list(range(T - 1 + n)), (l, b, written)
+    seq = np.concatenate([prompt] + [r.next_tok[:, None] for r in res[:-1]], axis=1)
+    mf, cf = _fresh(c, src)
+    fw = odf.forward_dual(mf, cf, seq)
+    for s_, r in enumerate(res):
+        t = T - 1 + s_
+        assert np.max(np.abs(r.logits[:, 1])) > 0, "aux flow not active"
+        assert np.max(np.abs(fw.logits[:, t] - r.logits)) < 1e-9, f"step {s_} is not position {t}"
+        assert np.max(np.abs(fw.p_mix[:, t] - r.p_mix)) < 1e-12
+        assert np.array_equal(fw.next_tok[:, t], r.next_tok)
+
+
+# ----------------------------------------------------------------------------
+# Where rounding may sit: appended K/V entries only (no rounded projection inputs)
+# ----------------------------------------------------------------------------
+
+# The 24-layer, d 2048 dense model of the 1.3B workload, one sequence, a short
+# prefilled context; and a small 8-layer model for the quick check.
+R16_FULL_DEPTH = Config("r16_dense_1p3b", L=24, d=2048, H=16, Dh=128, F=8192, V=32000, B=1, ctx=16, S_max=32,
+                        dtype="bf16", seed=4)
+R16_SMALL = Config("r16_small", L=8, d=512, H=4, Dh=128, F=2048, V=4096, B=2, ctx=16, S_max=32,
+                   dtype="bf16", seed=4)
+R16_NOISE = 2.0 ** -20      # relative, about the fp32 rounding-order difference of a K = 2048 sum
+
+
+def step_logits_under_noise(cfg, round_inputs: bool, noise: float, seed: int = 1):
+    """Logits of one dual step when every projection input is multiplied by
+    (1 +- noise) (seeded signs) and, with round_inputs, then rounded to bf16
+    (the reading that rounds every projection input). The noise stands for a
+    different but equally correct fp32 summation order."""
+    orig = odf._matvec
+    rng = np.random.default_rng(seed)
+
+    def mv(W, x):
+        x = np.asarray(x, dtype=np.float64)
+        if noise:
+            x = x * (1.0 + noise * rng.choice([-1.0, 1.0], size=x.shape))
+        if round_inputs:
+            x = odf.round_to(x, "bf16")
+        return orig(W, x)
+
+    odf._matvec = mv
+    try:
+        src = Inputs(cfg)
+        m, cache = _fresh(cfg, src)
+        return odf.decode_step(m, cache, src.step_tokens(0), aux_on=True).logits
+    finally:
+        odf._matvec = orig
+
+
+def pin_unrounded_inputs_are_stable(cfg=R16_SMALL):
+    """With activations unrounded (only the appended K/V rounded), noise of
+    2^-20 relative on every projection input moves the logits by less than
+    1e-3, twenty times below the 2e-2 logits bar."""
+    a = step_logits_under_noise(cfg, False, 0.0)
+    b = step_logits_under_noise(cfg, False, R16_NOISE)
+    move = float(np.max(np.abs(a - b)))
+    assert move < 1e-3, f"unrounded oracle moved {move:.3e}"
+    return move
+
+
+ALL_BASIC = [pin_round_bf16, pin_decode_bf16, pin_layer_norm, pin_gelu, pin_attention_sdpa,
+             pin_attention_closed_forms, pin_attention_dual, pin_mix_properties, pin_mix_golden, pin_topk,
+             pin_mix_aux_mode, pin_mix_half_mode, pin_unrounded_inputs_are_stable]
 MODEL_PINS = [pin_aux_onoff, pin_tied_zero_coupling, pin_kv_sentinel, pin_prefill_equals_decode,
               pin_causality, pin_query_coupling, pin_mid_coupling, pin_out_coupling, pin_step_outputs]
 MOE_PINS = [pin_moe_single_expert_is_dense, pin_moe_all_experts_is_full_mixture, pin_moe_replay,
             pin_fanout_replay_and_primary, pin_fanout_closed_forms]
 VARIANT_PINS = [pin_no_coupling_tied, pin_variant_mix_in_step]
-FORWARD_PINS = [pin_forward_equals_steps, pin_forward_primary_is_prefill, pin_forward_causal]
+FORWARD_PINS = [pin_forward_equals_steps, pin_forward_primary_is_prefill, pin_forward_causal,
+                pin_run_tiny_schedule]

@@ -150,6 +150,23 @@ def _attend_excl_new(q, K, V, pos):
     return o
 
 
+def _decode_shift15(u16, out=None):
+    u = np.ascontiguousarray(u16, dtype=np.uint16)
+    return (u.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+
+
+def _decode_byteswap(u16, out=None):
+    u = np.ascontiguousarray(u16, dtype=np.uint16).byteswap()
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+_orig_matvec = odf._matvec
+
+
+def _matvec_rounds_inputs(W, x):
+    return _orig_matvec(W, odf.round_to(np.asarray(x, dtype=np.float64), "bf16"))
+
+
 MUTATIONS = [
     ("gelu_tanh_approx", "gelu", _gelu_tanh, [pins.pin_gelu]),
     ("attention_no_scale", "attention_one", _attn_noscale, [pins.pin_attention_sdpa]),
@@ -161,6 +178,9 @@ MUTATIONS = [
     ("topk_ties_to_upper", "topk_ids", _topk_upper_ties, [pins.pin_topk]),
     ("bf16_double_rounding", "round_to", _round_via_f32, [pins.pin_round_bf16]),
     ("bf16_truncation", "round_to", _round_truncate, [pins.pin_round_bf16]),
+    ("bf16_decode_wrong_shift", "decode_bf16", _decode_shift15, [pins.pin_decode_bf16]),
+    ("bf16_decode_byte_order", "decode_bf16", _decode_byteswap, [pins.pin_decode_bf16]),
+    ("projection_inputs_rounded", "_matvec", _matvec_rounds_inputs, [pins.pin_unrounded_inputs_are_stable]),
     ("query_coupling_sign", "couple_query", lambda q2, a, q1: q2 - a * q1,
      [lambda: pins.pin_query_coupling(pins.TINY_BF16)]),
     ("query_coupling_wrong_operand", "couple_query", lambda q2, a, q1: q2 + a * q2,
@@ -248,3 +268,29 @@ def test_forward_mutation_is_caught(monkeypatch, name, old, new):
     monkeypatch.setattr(odf, "forward_dual", _mutated_forward(old, new))
     with pytest.raises(AssertionError):
         pins.pin_forward_equals_steps(pins.TINY_BF16)
+
+
+def _mutated(fn, old, new):
+    """An oracle function with one line of its source replaced."""
+    import inspect
+    src = inspect.getsource(fn)
+    assert old in src, old
+    ns = dict(vars(odf))
+    exec(compile(src.replace(old, new), "<planted mistake>", "exec"), ns)
+    return ns[fn.__name__]
+
+
+RUN_TINY_MUTATIONS = [
+    ("prefill_takes_last_prompt_token", "prefill_primary(model, cache, prompt[:, :-1])",
+     "prefill_primary(model, cache, prompt)"),
+    ("first_step_wrong_token", "tok = prompt[:, -1]", "tok = prompt[:, -2]"),
+    ("aux_activated_one_position_late", "aux_on=True", "aux_on=(s > 0)"),
+    ("chosen_token_not_fed_back", "tok = r.next_tok", "tok = tok"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", RUN_TINY_MUTATIONS, ids=[m[0] for m in RUN_TINY_MUTATIONS])
+def test_run_tiny_mutation_is_caught(monkeypatch, name, old, new):
+    monkeypatch.setattr(odf, "run_tiny", _mutated(odf.run_tiny, old, new))
+    with pytest.raises(AssertionError):
+        pins.pin_run_tiny_schedule(pins.TINY_F32)
