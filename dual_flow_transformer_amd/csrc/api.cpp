@@ -37,7 +37,7 @@ void gemv_scratch(const df_config& c, size_t* part_floats, size_t* blocks) {
     for (int M : {2 * c.batch, c.batch}) {
         for (auto& sh : shapes) {
             if (sh[0] <= 0 || sh[1] <= 0) continue;
-            const dfk::GemvPlan pl = dfk::plan_gemv(c.dtype, sh[0], sh[1], M);
+            const dfk::GemvPlan pl = dfk::plan_gemv(c.dtype, sh[0], sh[1], M, 2 * c.batch);
             const size_t need = pl.part_floats > 0 ? pl.part_floats : (size_t)M * sh[0];
             if (need > *part_floats) *part_floats = need;
             if ((size_t)pl.nblocks > *blocks) *blocks = pl.nblocks;
@@ -276,7 +276,10 @@ struct Step {
         const bool couple = (c.variant & DF_VARIANT_NO_COUPLING) == 0;   // a, b, c applied
         const int kr = std::max(c.top_k, c.top_k_aux);                   // MoE ranking length
         float* stats = at<float>(L.stats);
-        const int qkv_slices = dfk::plan_gemv(c.dtype, 3 * d, d, nflows == 2 ? 2 * B : B).S;
+        // every projection is k-sliced as for the 2B stacked rows of a dual
+        // step, also in a primary-only step: the primary outputs are then
+        // summed over the same slices in the same order either way
+        const int qkv_slices = dfk::plan_gemv(c.dtype, 3 * d, d, nflows == 2 ? 2 * B : B, 2 * B).S;
         bool pending = false;   // h has fresh statistics whose norm has not been applied
         auto set_x = [&](dfk::GemvArgs& g, const float* gain) {
             if (pending && fused) { g.x = h; g.x_stats = stats; g.x_gain = gain; }
@@ -295,7 +298,7 @@ struct Step {
             const float* g_next = (l + 1 < L_) ? w.ln1 + (size_t)(l + 1) * d : w.lnf;
             dfk::GemvArgs g{};
             g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.H = c.n_heads; g.Dh = c.head_dim; g.S_max = c.max_seq;
-            g.part = at<float>(L.gpart); g.eps = c.ln_eps;
+            g.part = at<float>(L.gpart); g.eps = c.ln_eps; g.slice_rows = 2 * B;
             // Q/K/V projection of LN1(h). bf16: its k-slice partial sums go
             // straight to the attention pass, which sums them, applies the Q
             // coupling and appends the primary K/V; fp32: the projection's
@@ -363,7 +366,7 @@ struct Step {
             dfk::GemvArgs g{};
             g.dtype = c.dtype; g.B = B; g.nflows = nflows; g.w = w.w_out; g.N = c.vocab; g.K = d;
             g.epi = dfk::EPI_STORE; g.out_f32 = lg; g.eps = c.ln_eps;
-            g.part = at<float>(L.gpart);
+            g.part = at<float>(L.gpart); g.slice_rows = 2 * B;
             set_x(g, w.lnf);   // final norm
             if (dfk::gemv(g, s) != hipSuccess) return DF_ERR_HIP;
             const int mode = mix_mode_of(c, nflows);

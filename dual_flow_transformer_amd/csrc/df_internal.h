@@ -128,6 +128,8 @@ struct GemvArgs {
     int32_t* status;      // EPI_QKV: flag when a position is out of range
     float* part;          // split-K partial sums (plan_gemv(...).part_floats floats)
     float eps;            // LayerNorm epsilon (x_stats)
+    int slice_rows;       // bf16: stacked rows the k-slicing is planned for (0: the rows in use);
+                          // calls with the same slice_rows sum every output over the same slices
 };
 struct GemvPlan {
     int MT;               // 16-row activation tiles (0: shape not supported)
@@ -136,7 +138,9 @@ struct GemvPlan {
     int grid, nblocks;    // workgroups; row groups per slice
     size_t lds, part_floats;   // dynamic LDS bytes; partial-sum floats
 };
-GemvPlan plan_gemv(int dtype, int N, int K, int M);
+// M: stacked rows in use; M_slices (>= M, else taken as M): the row count whose
+// plan fixes the k-slice width.
+GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices = 0);
 hipError_t gemv(const GemvArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------

@@ -526,21 +526,52 @@ hipError_t finish(GParams& p, int S, hipStream_t s) {
 
 }  // namespace
 
-GemvPlan plan_gemv(int dtype, int N, int K, int M) {
-    GemvPlan pl{};
-    if (dtype != DF_BF16 || M < 1 || M > 128 || N < 16 || N % 16 || K < 256 || K % 256) return pl;
-    const int mt = (M + 15) / 16;
-    pl.MT = mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
-    // shapes from a plan sweep on the box (weights rotated past the MALL):
-    // 32-row tiles up to 16M weights or below 8192 rows, 256-wide k slices for
-    // the smallest matrices
+namespace {
+
+// k-slice widths the kernel shapes are instantiated for (launch_mt).
+bool ks_supported(int variant, int MT, int ks) {
+    if (variant == VAR_B) return MT <= 2 && (ks == 512 || ks == 256);
+    if (ks == 1024) return MT <= 2;
+    if (ks == 512) return MT <= 4;
+    return ks == 256;
+}
+
+// Widest supported k-slice for a shape (from a plan sweep on the box, weights
+// rotated past the MALL): 256 for the smallest matrices in the 32-row-tile
+// shape, else the widest the activation tile leaves LDS for.
+int ks_for(int variant, int MT, int N, int K) {
     const long nk = (long)N * K;
-    pl.variant = (pl.MT <= 2 && (N < 8192 || nk <= (16L << 20))) ? VAR_B : VAR_A;
-    const int ks_max = pl.variant == VAR_B ? (nk <= (4L << 20) ? 256 : 512)
-                                           : (pl.MT <= 2 ? 1024 : pl.MT == 4 ? 512 : 256);
-    int ks = 256;
+    const int ks_max = variant == VAR_B ? (nk <= (4L << 20) ? 256 : 512) : (MT <= 2 ? 1024 : MT == 4 ? 512 : 256);
     for (int c = ks_max; c >= 256; c /= 2)
-        if (K % c == 0) { ks = c; break; }
+        if (K % c == 0) return c;
+    return 256;
+}
+
+int variant_for(int MT, int N, int K) {
+    // 32-row tiles up to 16M weights or below 8192 rows
+    return (MT <= 2 && (N < 8192 || (long)N * K <= (16L << 20))) ? VAR_B : VAR_A;
+}
+
+int mt_for(int M) {
+    const int mt = (M + 15) / 16;
+    return mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
+}
+
+}  // namespace
+
+GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
+    GemvPlan pl{};
+    if (M_slices < M) M_slices = M;
+    if (dtype != DF_BF16 || M < 1 || M_slices > 128 || N < 16 || N % 16 || K < 256 || K % 256) return pl;
+    pl.MT = mt_for(M);
+    pl.variant = variant_for(pl.MT, N, K);
+    // The k-slice width is the one the M_slices-row plan takes, so that every
+    // output is summed over the same k-slices (in the same order) whichever
+    // row count runs: a primary-only step then gives bitwise the primary
+    // results of a dual step.
+    const int mt_s = mt_for(M_slices);
+    const int ks = ks_for(variant_for(mt_s, N, K), mt_s, N, K);
+    if (!ks_supported(pl.variant, pl.MT, ks)) return GemvPlan{};
     pl.ks = ks;
     pl.S = K / ks;
     pl.lds = (size_t)2 * 16 * pl.MT * (ks + 8) * 2;
@@ -577,7 +608,7 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         return finish(p, 1, s);
     }
-    const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M);
+    const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M, a.slice_rows);
     if (pl.MT == 0) return hipErrorInvalidValue;
     p.S = pl.S;
     if ((pl.S > 1 || a.epi == EPI_RESID || a.epi == EPI_PART) && !a.part) return hipErrorInvalidValue;

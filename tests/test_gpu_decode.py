@@ -24,6 +24,11 @@ SMALL_BF16 = Config("gpu_small_bf16", L=2, d=256, H=2, Dh=128, F=1024, V=512, B=
 # pass's slice sums take in a ragged batch
 SMALL_BF16_S3 = Config("gpu_small_bf16_s3", L=2, d=768, H=6, Dh=128, F=1536, V=512, B=3, ctx=200, S_max=224,
                        dtype="bf16", seed=24, sigma_w=0.05, sigma_ln=0.1)
+# d 2304 with 36 sequences (72 stacked rows): the Q/K/V projection splits K
+# into 9 slices of 256, more than the attention pass's slice sums take in
+# one round of loads (8), so they take a second round
+BF16_S9 = Config("gpu_bf16_s9_b36", L=1, d=2304, H=18, Dh=128, F=9216, V=512, B=36, ctx=40, S_max=64,
+                 dtype="bf16", seed=25, sigma_w=0.02, sigma_ln=0.1)
 SMALL_F32 = Config("gpu_small_f32", L=2, d=128, H=2, Dh=64, F=256, V=300, B=2, ctx=40, S_max=64,
                    dtype="f32", seed=22, sigma_w=0.05, sigma_ln=0.1)
 SMALL_MOE = Config("gpu_small_moe", L=2, d=256, H=2, Dh=128, F=0, V=512, B=8, ctx=40, S_max=64, dtype="bf16",
@@ -73,7 +78,7 @@ def _check_writes(gm, cfg, lens0, cache: odf.Cache, sentinel):
                 assert np.all(np.abs(got - ref) <= ulp * np.abs(ref) + KV_ABS), f"{name} values l={l} b={b}"
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_BF16_S3, SMALL_F32], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_BF16_S3, BF16_S9, SMALL_F32], ids=lambda c: c.name)
 def test_small_dense_steps(cfg):
     say(f"decode case {cfg.name}")
     gm = DecodeModel(cfg, fill="host")
@@ -164,7 +169,20 @@ def test_cache_edge_positions(cfg):
     assert gm.status() == 0          # reading the status word clears it
 
 
-@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_MOE], ids=lambda c: c.name)
+# Batch sizes whose dual step stacks more rows than a primary-only step
+# would plan alone (24 and 64 sequences: 48 / 128 stacked rows against 24 /
+# 64), at the d 2048 shapes of the dense 1.3B and MoE workloads, two layers.
+DENSE_B24 = Config("gpu_dense_d2048_b24", L=2, d=2048, H=16, Dh=128, F=8192, V=512, B=24, ctx=64, S_max=80,
+                   dtype="bf16", seed=26, sigma_w=0.02, sigma_ln=0.1)
+DENSE_B64 = DENSE_B24.replace(name="gpu_dense_d2048_b64", B=64)
+MOE_B24 = Config("gpu_moe_d2048_e64_b24", L=2, d=2048, H=16, Dh=128, F=0, V=512, B=24, ctx=64, S_max=80,
+                 dtype="bf16", moe=True, E=64, top_k=4, Fe=1024, router_override=True, seed=27, sigma_w=0.02,
+                 sigma_ln=0.1)
+MOE_B64 = MOE_B24.replace(name="gpu_moe_d2048_e64_b64", B=64)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_MOE, DENSE_B24, DENSE_B64, MOE_B24, MOE_B64],
+                         ids=lambda c: c.name)
 def test_primary_independent_of_aux(cfg):
     """Primary logits and every cache byte are bitwise the same with the aux
     flow on or off (the aux flow never feeds back and never writes K/V)."""
@@ -273,10 +291,12 @@ def test_moe_aux_fanout(ka, variant):
         _compare_step(cfg, gm, r)
 
 
-def test_moe_aux_fanout_leaves_primary_bitwise():
+@pytest.mark.parametrize("base", [SMALL_MOE, MOE_B24, MOE_B64], ids=lambda c: c.name)
+def test_moe_aux_fanout_leaves_primary_bitwise(base):
     """Whatever the aux fan-out, the primary logits and the cache are bitwise
     those of a primary-only step."""
-    cfg = SMALL_MOE.replace(top_k_aux=12)
+    cfg = base.replace(top_k_aux=12)
+    say(f"moe fan-out 12 on/off {cfg.name}")
     src = Inputs(cfg)
     a = DecodeModel(cfg, fill="device")
     b = DecodeModel(cfg, fill="device")
