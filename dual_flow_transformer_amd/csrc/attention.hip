@@ -364,6 +364,16 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     // the waves that covered this pair, and so its consecutive slots
     const long long KT = p.seq_tab[p.B];
     const int n = keys_of(p.nkeys, b, p.nkeys_add, p.S_max);
+    if (n == 0) {   // no keys: zero output, LSE -inf (no slot belongs to this pair)
+        if (f < p.nflows && cg == 0) {
+            const size_t row = (size_t)(2 * b + f) * p.H * DH + (size_t)h * DH + 4 * d4;
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p.o_f32) *reinterpret_cast<float4*>(p.o_f32 + row) = z;
+            if (p.o_rows) *reinterpret_cast<float4*>(p.o_rows + row) = z;
+            if (p.lse && d4 == 0) p.lse[(size_t)(2 * b + f) * p.H + h] = -INFINITY;
+        }
+        return;
+    }
     const long long lo = p.seq_tab[b] + (long long)h * n;
     const int w0 = (int)(lo / KT), w1 = (int)((lo + n - 1) / KT);
     const size_t first = (size_t)w0 + (size_t)b * p.H + h;

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
         for (int j = 0; j < NPT; ++j) {
             const int v = min((int)threadIdx.x + 1024 * j, V - 1);
             x1[j] = l1[v];
-            x2[j] = l2[v];
+            x2[j] = aux_on ? l2[v] : 0.f;   // the aux row is not read in DF_MIX_PRIMARY
         }
     }
     // logit v of flow f: from the registers or from memory

@@ -148,7 +148,11 @@ size_t df_workspace_bytes(const df_config* cfg);
  * sections "Arquitectura Central" and "Mecanismos Clave").
  *  d_tokens [batch]: token of each sequence at position len[b].
  *  aux_on: 1 = dual step; 0 = primary-only step (p_mix = p_primary,
- *    alpha = 1; the primary numerics are bitwise those of a dual step).
+ *    alpha = 1). The primary numerics (logits, cache, expert ids) are bitwise
+ *    those of a dual step at every batch size: both modes split every
+ *    projection's k range into the same slices (the plan for the 2 * batch
+ *    stacked rows) and add them in the same order, and no other reduction
+ *    depends on the row count.
  *  d_router_logits [L][batch][n_experts] or NULL: MoE only, primary router
  *    logits supplied by the caller (replacing the primary router output);
  *    NULL computes them from w_router.
@@ -226,12 +230,20 @@ int df_forward_dual(const df_config* cfg, const df_weights* w, const df_kv* kv,
                     float* d_alpha, int32_t* d_next_tok, void* d_ws, size_t ws_bytes,
                     void* stream);
 
-/* Write K/V entries of one layer at explicit positions: for each sequence b
- * and head h, k[layer][b][h][d_pos[b]][:] = round(d_k[b][h][:]) (same for v),
- * d_k, d_v fp32 [batch][n_heads][head_dim], rounded to the storage dtype.
- * The decode step fuses this write into its QKV projection. Positions
- * outside [0, max_seq) are skipped and flagged in d_status (int32, may be
- * NULL). */
+/* Append primary K/V entries to the one persistent cache
+ * (gist.science/es/paper/2608.12385, "Arquitectura Central": only the
+ * primary flow writes K/V; the aux flow reads the primary's entries and
+ * never writes): for each sequence b and head h of one layer,
+ * k[layer][b][h][d_pos[b]][:] = round(d_k[b][h][:]) (same for v).
+ *  d_k, d_v: fp32 [batch][n_heads][head_dim], rounded to the storage dtype
+ *    (nearest-even for bf16).
+ *  d_pos: int32 [batch] device positions; entries outside [0, max_seq) are
+ *    skipped and set bit 0 of *d_status (int32 device word, may be NULL).
+ * The decode step does not call this: with bf16 storage its attention pass
+ * forms, rounds and writes the new entry itself (and attends it from
+ * registers), with fp32 storage the Q/K/V projection's epilogue writes it.
+ * Asynchronous on `stream`; returns DF_ERR_* for bad arguments before any
+ * launch. */
 int df_kv_append(const df_config* cfg, const df_kv* kv, int32_t layer, const int32_t* d_pos,
                  const float* d_k, const float* d_v, int32_t* d_status, void* stream);
 
@@ -254,7 +266,8 @@ int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t mod
  *  d_a: [n_heads*head_dim] or NULL: if given Q2 = Q2raw + a * Q1.
  *  d_o: [batch][2][n_heads][head_dim] fp32 outputs; d_lse: [batch][2][n_heads]
  *  natural-log sum of exp of the scaled scores. Scores are q.k/sqrt(head_dim).
- *  d_len[b] must lie in [1, max_seq]; batch <= 64.
+ *  d_len[b] is clamped to [0, max_seq]; a sequence with no keys
+ *  (d_len[b] = 0) gets zero outputs and lse = -inf. batch <= 64.
  *  d_ws: df_attention_workspace_bytes bytes (the call's chunk table and
  *  per-chunk partial results; no initial contents needed). */
 int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch,

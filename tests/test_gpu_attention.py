@@ -140,3 +140,35 @@ def test_sampled_launch_timing():
     call()
     rc, ms, n = _abi.df_timing_read()
     assert rc == 0 and n == 0 and ms == 0.0
+
+
+@pytest.mark.parametrize("lens", [[0, 5, 0, 300, 0], [0, 0]], ids=["mixed", "all_empty"])
+def test_sequences_without_keys(lens):
+    """A sequence with no keys gets zero outputs and LSE -inf; the others
+    match the oracle as usual."""
+    B, H, S, Dh = len(lens), 2, 400, 128
+    say(f"empty-sequence case lens={lens}")
+    K = synth.normal((B, H, S, Dh), 43, synth.stream_id("t_k"), 1.0, "bf16")
+    V = synth.normal((B, H, S, Dh), 43, synth.stream_id("t_v"), 1.0, "bf16")
+    q = synth.normal((B, 2, H, Dh), 43, synth.stream_id("t_q"), 1.0, "f32")
+    dK, dV, dq = dev_bf16(K), dev_bf16(V), torch.from_numpy(q).cuda()
+    dl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = torch.full((B, 2, H, Dh), float("nan"), device="cuda")
+    lse = torch.full((B, 2, H), float("nan"), device="cuda")
+    wsb = _abi.df_attention_workspace_bytes(B, H, S, Dh)
+    ws = torch.full((wsb,), 0xA5, dtype=torch.uint8, device="cuda")
+    rc = _abi.df_attention_dual(_abi.DF_BF16, dK.data_ptr(), dV.data_ptr(), B, H, S, Dh, dl.data_ptr(),
+                                dq.data_ptr(), None, o.data_ptr(), lse.data_ptr(), ws.data_ptr(), wsb,
+                                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, _abi.df_status_str(rc)
+    torch.cuda.synchronize()
+    go, gl = o.cpu().numpy(), lse.cpu().numpy()
+    Kf, Vf = odf.to_f64(K), odf.to_f64(V)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(go[b] == 0.0) and np.all(gl[b] == -np.inf), f"sequence {b}"
+            continue
+        for h in range(H):
+            for f in range(2):
+                ro, rl = odf.attention_one(q[b, f, h].astype(np.float64), Kf[b, h, :n], Vf[b, h, :n])
+                assert max_abs(go[b, f, h], ro) < TOL and abs(gl[b, f, h] - rl) < TOL
