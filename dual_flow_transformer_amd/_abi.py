@@ -33,7 +33,8 @@ EXPORTS = ["df_workspace_bytes", "df_prefill_workspace_bytes", "df_forward_works
            "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
            "df_attention_dual", "df_attention_workspace_bytes", "df_device_status", "df_status_str",
            "df_timing_enable", "df_timing_read", "df_stacked_gemv", "df_stacked_gemv_workspace_bytes",
-           "df_pack_weights"]
+           "df_pack_weights", "df_attention_dual_noalloc"]
+DF_ATTENTION_NOALLOC_SCRATCH_BYTES = 17040384
 
 
 class df_config(ctypes.Structure):
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.df_mix_head.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.df_attention_dual.restype = ctypes.c_int
         L.df_attention_dual.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.df_attention_dual_noalloc.restype = ctypes.c_int
+        L.df_attention_dual_noalloc.argtypes = [i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.df_attention_workspace_bytes.restype = sz
         L.df_attention_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.df_device_status.restype = ctypes.c_int
@@ -163,6 +166,12 @@ def df_attention_dual(dtype, d_k, d_v, batch, n_heads, max_seq, head_dim, d_len,
                       ws_bytes, stream=0) -> int:
     return lib().df_attention_dual(int(dtype), d_k, d_v, int(batch), int(n_heads), int(max_seq), int(head_dim),
                                    d_len, d_q, d_a, d_o, d_lse, d_ws, ws_bytes, stream)
+
+
+def df_attention_dual_noalloc(dtype, d_k, d_v, batch, n_heads, max_seq, head_dim, d_len, d_q, d_a, d_o, d_lse,
+                              stream=0) -> int:
+    return lib().df_attention_dual_noalloc(int(dtype), d_k, d_v, int(batch), int(n_heads), int(max_seq),
+                                           int(head_dim), d_len, d_q, d_a, d_o, d_lse, stream)
 
 
 def df_attention_workspace_bytes(batch, n_heads, max_seq, head_dim) -> int:

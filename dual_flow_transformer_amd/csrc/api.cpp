@@ -642,20 +642,8 @@ size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_
 int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch, int32_t n_heads,
                       int32_t max_seq, int32_t head_dim, const int32_t* d_len, const float* d_q, const float* d_a,
                       float* d_o, float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
-    if (dtype != DF_F32 && dtype != DF_BF16) return DF_ERR_DTYPE;
-    if (!d_k || !d_v || !d_len || !d_q || !d_o || !d_lse || !d_ws) return DF_ERR_NULL;
-    if (batch < 1 || n_heads < 1 || max_seq < 1 || (head_dim != 32 && head_dim != 64 && head_dim != 128))
-        return DF_ERR_SHAPE;
-    if (!aligned16(d_k) || !aligned16(d_v) || !aligned16(d_q) || (d_a && !aligned16(d_a)) ||
-        (uintptr_t)d_ws % kAlign)
-        return DF_ERR_ALIGN;
-    if (ws_bytes < df_attention_workspace_bytes(batch, n_heads, max_seq, head_dim)) return DF_ERR_WORKSPACE;
-    dfk::AttnArgs a{};
-    a.dtype = dtype; a.k = d_k; a.v = d_v; a.B = batch; a.H = n_heads; a.S_max = max_seq; a.Dh = head_dim;
-    a.q = d_q; a.a = d_a; a.nkeys = d_len; a.nkeys_add = 0; a.nflows = 2; a.part = reinterpret_cast<float*>(d_ws);
-    a.o_f32 = d_o; a.lse = d_lse; a.o_rows = nullptr;
-    timing_events(0, &a.ev_start, &a.ev_stop);
-    return dfk::attention(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
+    return dfk::attention_dual_entry(dtype, d_k, d_v, batch, n_heads, max_seq, head_dim, d_len, d_q, d_a, d_o,
+                                     d_lse, d_ws, ws_bytes, stream, true);
 }
 
 size_t df_stacked_gemv_workspace_bytes(int32_t dtype, int32_t rows, int32_t N, int32_t K) {
@@ -767,3 +755,27 @@ int df_timing_read(double* total_ms, int64_t* launches) {
 }
 
 }  // extern "C"
+
+namespace dfk {
+
+int attention_dual_entry(int dtype, const void* d_k, const void* d_v, int batch, int n_heads, int max_seq,
+                         int head_dim, const int32_t* d_len, const float* d_q, const float* d_a, float* d_o,
+                         float* d_lse, void* d_ws, size_t ws_bytes, void* stream, bool timed) {
+    if (dtype != DF_F32 && dtype != DF_BF16) return DF_ERR_DTYPE;
+    if (!d_k || !d_v || !d_len || !d_q || !d_o || !d_lse || !d_ws) return DF_ERR_NULL;
+    if (batch < 1 || n_heads < 1 || max_seq < 1 || (head_dim != 32 && head_dim != 64 && head_dim != 128))
+        return DF_ERR_SHAPE;
+    if (!attention_fits(batch, n_heads)) return DF_ERR_SHAPE;
+    if (!aligned16(d_k) || !aligned16(d_v) || !aligned16(d_q) || (d_a && !aligned16(d_a)) ||
+        (uintptr_t)d_ws % kAlign)
+        return DF_ERR_ALIGN;
+    if (ws_bytes < df_attention_workspace_bytes(batch, n_heads, max_seq, head_dim)) return DF_ERR_WORKSPACE;
+    AttnArgs a{};
+    a.dtype = dtype; a.k = d_k; a.v = d_v; a.B = batch; a.H = n_heads; a.S_max = max_seq; a.Dh = head_dim;
+    a.q = d_q; a.a = d_a; a.nkeys = d_len; a.nkeys_add = 0; a.nflows = 2; a.part = reinterpret_cast<float*>(d_ws);
+    a.o_f32 = d_o; a.lse = d_lse; a.o_rows = nullptr;
+    if (timed) timing_events(0, &a.ev_start, &a.ev_stop);
+    return attention(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? DF_OK : DF_ERR_HIP;
+}
+
+}  // namespace dfk

@@ -429,8 +429,9 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     if (p.lse && d4 == 0) p.lse[(size_t)(2 * b + f) * p.H + h] = (m + __log2f(l)) * df::kLn2;
 }
 
-constexpr int kMaxSlots = 16384;    // partial results per launch at most (workspace bound)
-constexpr int kTabFloats = 256;     // sequence table [65] 64-bit, padded
+constexpr int kMaxSlots = kAttnMaxSlots;   // partial results per launch at most (workspace bound)
+constexpr int kTabFloats = 256;            // sequence table [65] 64-bit, padded
+static_assert(kTabFloats + (size_t)kMaxSlots * (4 + 2 * 128) == kAttnPartFloatsMax, "workspace bound");
 
 // Waves of an attn_partial launch on the current device (cached): one
 // 4-wave workgroup per compute unit. Measured against two and three per CU
@@ -479,6 +480,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool attention_fits(int B, int H) { return B >= 1 && B <= 64 && H >= 1 && launch_waves() + B * H <= kMaxSlots; }
 
 size_t attention_part_floats(int B, int H, int S_max, int Dh) {
     (void)S_max;

@@ -50,7 +50,18 @@ struct AttnArgs {
     int32_t* status;
 };
 size_t attention_part_floats(int B, int H, int S_max, int Dh);
+// Partial-result slots of one launch at most, and the largest
+// attention_part_floats (head_dim 128).
+constexpr int kAttnMaxSlots = 16384;
+constexpr size_t kAttnPartFloatsMax = 256 + (size_t)kAttnMaxSlots * (4 + 2 * 128);
+// Whether B sequences x H heads fit the slot bound on the current device.
+bool attention_fits(int B, int H);
 hipError_t attention(const AttnArgs& a, hipStream_t s);
+// df_attention_dual after its argument checks; with timed, the launch takes
+// the kernel-timing events when timing is enabled (df_timing_enable).
+int attention_dual_entry(int dtype, const void* d_k, const void* d_v, int batch, int n_heads, int max_seq,
+                         int head_dim, const int32_t* d_len, const float* d_q, const float* d_a, float* d_o,
+                         float* d_lse, void* d_ws, size_t ws_bytes, void* stream, bool timed);
 
 // ---------------------------------------------------------------------------
 // Row operations

@@ -267,13 +267,34 @@ int df_mix_head(const float* d_logits, int32_t batch, int32_t vocab, int32_t mod
  *  d_o: [batch][2][n_heads][head_dim] fp32 outputs; d_lse: [batch][2][n_heads]
  *  natural-log sum of exp of the scaled scores. Scores are q.k/sqrt(head_dim).
  *  d_len[b] is clamped to [0, max_seq]; a sequence with no keys
- *  (d_len[b] = 0) gets zero outputs and lse = -inf. batch <= 64.
+ *  (d_len[b] = 0) gets zero outputs and lse = -inf. batch <= 64 and
+ *  batch * n_heads <= 16384 - 4 x (compute units), 15360 on the MI355X
+ *  (else DF_ERR_SHAPE).
  *  d_ws: df_attention_workspace_bytes bytes (the call's chunk table and
  *  per-chunk partial results; no initial contents needed). */
 int df_attention_dual(int32_t dtype, const void* d_k, const void* d_v, int32_t batch,
                       int32_t n_heads, int32_t max_seq, int32_t head_dim, const int32_t* d_len,
                       const float* d_q, const float* d_a, float* d_o, float* d_lse,
                       void* d_ws, size_t ws_bytes, void* stream);
+
+/* df_attention_dual without a workspace argument and without allocating
+ * anything, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, results and errors as df_attention_dual; the chunk table and
+ * partial results go to a static device array of the library,
+ * DF_ATTENTION_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, kept
+ * until the process ends. Its address is looked up once per device (on the
+ * first call with that device current). Every call on a GPU shares that
+ * GPU's array, so calls that overlap on one GPU (different streams, or
+ * several host threads) race: order them on one stream. Sizes whose
+ * workspace would exceed the array return DF_ERR_WORKSPACE (no supported
+ * size does); more than 16384 - 4 x (compute units) sequence-head pairs
+ * return DF_ERR_SHAPE, as in df_attention_dual. Never calls hipMalloc or
+ * hipFree; no kernel timing. */
+#define DF_ATTENTION_NOALLOC_SCRATCH_BYTES 17040384
+int df_attention_dual_noalloc(int32_t dtype, const void* d_k, const void* d_v, int32_t batch,
+                              int32_t n_heads, int32_t max_seq, int32_t head_dim, const int32_t* d_len,
+                              const float* d_q, const float* d_a, float* d_o, float* d_lse, void* stream);
 
 /* Workspace bytes df_attention_dual needs for these sizes. */
 size_t df_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t max_seq, int32_t head_dim);
