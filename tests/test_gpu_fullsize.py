@@ -63,3 +63,43 @@ def test_full_size_sampled(name, seqs, ka):
                 ref = cache.appended[(l, b, cfg.ctx)][which]
                 assert np.all(np.abs(got - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, b, which)
                 assert np.all(t[i, :, 1].numpy() == 0), "write beyond position len"
+
+
+def test_c3_three_steps_teacher_forced():
+    """Three consecutive dual steps of the dense 1.3B workload (the new keys
+    at positions 2048, 2049, 2050), teacher-forced on the workload's step
+    tokens, against the oracle on sequences 0, 7 and 15: each step's logits,
+    p_mix, alpha and argmax, and every layer's three appended K/V entries
+    (the aux flow is active at every generated position, [ES] Arquitectura
+    Central)."""
+    cfg = PRESETS["c3"]
+    seqs = [0, 7, 15]
+    say(f"full-size {cfg.name}: three steps, oracle on sequences {seqs}")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    m = odf.Model(src, keep_layers=False)
+    cache = odf.Cache(cfg, seqs, src, lazy=True)
+    for step in range(3):
+        tok = src.step_tokens(step)
+        gm.decode_step(gm.tokens(tok))
+        torch.cuda.synchronize()
+        assert gm.status() == 0
+        lg = gm.logits.cpu().numpy()[seqs]
+        pm = gm.p_mix.cpu().numpy()[seqs]
+        al = gm.alpha.cpu().numpy()[seqs]
+        nt = gm.next_tok.cpu().numpy()[seqs]
+        r = odf.decode_step(m, cache, tok[seqs], aux_on=True)
+        el, ep = max_abs(lg, r.logits), max_abs(pm, r.p_mix)
+        say(f"  step {step}: logits max|d|={el:.3e} p_mix max|d|={ep:.3e}")
+        assert el < 2e-2 and ep < 1e-3 and max_abs(al, r.alpha) < 1e-3
+        for i in range(len(seqs)):
+            assert argmax_agrees(pm[i], r.p_mix[i], nt[i], margin=2e-3)
+    assert np.array_equal(gm.len.cpu().numpy()[seqs], cache.lens)
+    for l in range(cfg.L):
+        for i, b in enumerate(seqs):
+            for t, which in ((gm.k, 0), (gm.v, 1)):
+                got = bits_to_f64(t[l, b, :, cfg.ctx:cfg.ctx + 4].cpu(), cfg.dtype)    # [H, 4, Dh]
+                for s_ in range(3):
+                    ref = cache.appended[(l, b, cfg.ctx + s_)][which]
+                    assert np.all(np.abs(got[:, s_] - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, b, s_, which)
+                assert np.all(got[:, 3] == 0), "write beyond position len"

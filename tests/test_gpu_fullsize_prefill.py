@@ -10,8 +10,18 @@ plus 3 D_1 in layer 1 (D_1 measured on the oracle with every layer-0 K/V
 value perturbed by a seeded relative +-2^-17 before its rounding). The dual
 forward's primary half is the prefill computed by the same kernels row by
 row, so its cache must equal the prefill's bit for bit (a property at any
-size); its p_mix rows must sum to 1 and alpha lie in [0.5, 1]."""
+size); its p_mix rows must sum to 1 and alpha lie in [0.5, 1].
+
+Deeper layers and the forward's outputs are held against the oracle's own
+results for sequence 0, stored by tests/golden/make_fullsize_prefill_forward.py
+(which calls only the oracle; the full-depth oracle takes tens of minutes):
+cache entries of layers 0, 1, 11, 12, 22, 23 at positions around the chunk
+edges, within one ulp + 5e-4 + 3 D_l (D_l stored beside them, measured the
+same way through every layer), and the forward's logits (2e-2) and p_mix
+(1e-3) at sampled vocabulary ids, alpha and the argmax at positions 0, 511,
+512, 1023, 1024, 1535, 1536 and 2047 (chunk edges of both passes)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -24,6 +34,7 @@ from synth.workloads import FORWARD_DENSE, PREFILL_DENSE, Inputs
 
 pytestmark = pytest.mark.gpu
 KV_ABS = 5e-4
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize_prefill_forward_seq0.npz")
 SEQS = [0, 15]
 POS = [0, 1, 511, 512, 1023, 1024, 2047]
 
@@ -74,6 +85,8 @@ def test_prefill_full_size_sampled():
     assert gm.status() == 0
     assert torch.all(gm.len == cfg.prompt_len)
     got = {(l, b): (gm.k[l, b].cpu(), gm.v[l, b].cpu()) for l in (0, 1) for b in SEQS}
+    gold = np.load(GOLDEN)
+    deep = {int(l): (gm.k[int(l), 0].cpu(), gm.v[int(l), 0].cpu()) for l in gold["kv_layers"]}
     del gm
     torch.cuda.empty_cache()
     for b in SEQS:
@@ -87,6 +100,20 @@ def test_prefill_full_size_sampled():
                 g = bits_to_f64(got[(l, b)][i][:, p], cfg.dtype)
                 err = _excess(g, want) - (KV_ABS + (3 * d1 if l else 0.0))
                 assert np.all(err <= 0), f"l={l} b={b} p={p} {'kv'[i]}: worst excess {err.max():.3e}"
+    # every depth, sequence 0, against the stored oracle cache
+    worst = {}
+    for li, l in enumerate(gold["kv_layers"]):
+        l = int(l)
+        bound = KV_ABS + 3 * max(float(gold["kv_bound"][l]), 0.0)
+        for pi, p in enumerate(gold["kv_pos"]):
+            for i, name in enumerate(("k", "v")):
+                want = odf.decode_bf16(gold[name][li, pi])              # [H, Dh]
+                have = bits_to_f64(deep[l][i][:, int(p)], cfg.dtype)   # [H, Dh]
+                ex = float(_excess(have, want).max())
+                worst[l] = max(worst.get(l, -1.0), ex)
+                assert ex <= bound, f"layer {l} position {int(p)} {name}: excess {ex:.3e} > {bound:.3e}"
+    say("  stored-oracle cache, worst excess over one ulp by layer: " +
+        ", ".join(f"{l}: {e:.2e} (D_l {float(gold['kv_bound'][l]):.2e})" for l, e in worst.items()))
 
 
 def test_forward_full_size_primary_is_prefill():
@@ -95,9 +122,27 @@ def test_forward_full_size_primary_is_prefill():
     toks = Inputs(cfg).prompt()
     a = DecodeModel(cfg, fill="device")
     a.len.zero_()
-    _, pm, al, nt = a.forward(a.tokens(toks).contiguous(), logits=False)
+    lg, pm, al, nt = a.forward(a.tokens(toks).contiguous(), logits=True)
     torch.cuda.synchronize()
     assert a.status() == 0
+    # sequence 0 against the oracle's forward at sampled positions
+    gold = np.load(GOLDEN)
+    for i, t in enumerate(gold["fw_pos"]):
+        t = int(t)
+        ids = torch.from_numpy(gold["fw_ids"][i]).to(lg.device)
+        gl = lg[0, t][:, ids].cpu().numpy()
+        gp = pm[0, t][ids].cpu().numpy()
+        el = float(np.max(np.abs(gl - gold["fw_logits"][i])))
+        ep = float(np.max(np.abs(gp - gold["fw_pmix"][i])))
+        ea = abs(float(al[0, t]) - float(gold["fw_alpha"][i]))
+        say(f"  position {t}: logits max|d|={el:.3e} p_mix max|d|={ep:.3e} alpha |d|={ea:.3e}")
+        assert el < 2e-2 and ep < 1e-3 and ea < 1e-3
+        # the stored ids start with the oracle's 32 largest p_mix entries: the GPU's argmax
+        # is the oracle's unless the top two are within 2e-3
+        top = gold["fw_pmix"][i][:32]
+        if top[0] - np.max(top[1:]) > 2e-3:
+            assert int(nt[0, t]) == int(gold["fw_next"][i])
+    del lg
     s = pm.sum(dim=-1)
     assert torch.all((s - 1).abs() < 1e-4), f"p_mix sums {s.min().item()}..{s.max().item()}"
     assert torch.all((al >= 0.5) & (al <= 1.0))

@@ -65,6 +65,8 @@ CASES = [
     # tiled GEMM (prefill rows): ragged row and column tiles, one and many k steps
     (129, 16, 32), (256, 256, 256), (1000, 1040, 512), (2048, 3072, 1024), (333, 4096, 2048),
     (4100, 2064, 2048),
+    # the prefill's down projection (K 8192: 256 k blocks) and up projection shapes
+    (300, 2048, 8192), (4096, 8192, 2048),
 ]
 
 
