@@ -13,8 +13,12 @@
 // the B operand from LDS; split over k-slices, persistent over row tiles;
 // partial sums are finished by a reduce kernel with one of the epilogues:
 // plain store, Q coupling + K/V append, GELU + b coupling, or c coupling +
-// residual add (then LayerNorm), or left for the next kernel (EPI_PART). fp32 path (fp32 storage, row-major): one
-// wave per weight row, lanes split K, wave reduction, same epilogues.
+// residual add (then LayerNorm), or left for the next kernel (EPI_PART). For
+// matrices of 32M weights or more and up to 32 stacked rows, the activation
+// fragments sit in registers instead (shape R: the waves of a workgroup split
+// its k-slice and add their products through LDS). fp32 path (fp32 storage,
+// row-major): one wave per weight row, lanes split K, wave reduction, same
+// epilogues.
 #include <algorithm>
 
 #include "df_device.h"
@@ -332,6 +336,202 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     }
 }
 
+// LayerNorm of the activation rows on the fly: the row mean and rstd come
+// from the per-segment (mean, M2) of the residual reduce by Chan's
+// combination, 16 lanes per row (lane j holds segment j), reduced by DPP
+// sums. Loading (into registers) and reducing are separate steps, so the
+// loads can be issued ahead of the weight stream and reduced after it.
+template <int SPT, int NT>
+struct RowStats {
+    float2 sv[SPT];
+    __device__ __forceinline__ void load(const GParams& p, int rows) {
+        const int nseg = stat_segs(p.K);
+        #pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int e = threadIdx.x + u * NT;
+            const int m = min(min(e >> 4, rows - 1), p.M - 1), j = min(e & 15, nseg - 1);
+            sv[u] = *reinterpret_cast<const float2*>(p.x_stats + ((size_t)(m * p.row_step) * nseg + j) * 2);
+        }
+    }
+    __device__ __forceinline__ void reduce(const GParams& p, int rows, float* s_mean, float* s_rstd) const {
+        const int nseg = stat_segs(p.K);
+        #pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int e = threadIdx.x + u * NT;
+            const int m = e >> 4, j = e & 15;
+            const bool valid = j < nseg;
+            const float cnt = valid ? (float)min(kStatSeg, p.K - j * kStatSeg) : 0.f;
+            const float mean = df::group_sum<16>(cnt * sv[u].x) / (float)p.K;
+            const float dm = sv[u].x - mean;
+            const float m2 = df::group_sum<16>(valid ? fmaf(cnt * dm, dm, sv[u].y) : 0.f);
+            if (j == 0 && m < rows) {
+                s_mean[m] = mean;
+                s_rstd[m] = 1.0f / sqrtf(m2 / (float)p.K + p.eps);
+            }
+        }
+    }
+};
+
+// Activation fragment (B operand) of one 32-column block for one row: the
+// lane's eight columns k0 .. k0 + 7 of row m, normalised when norm (gain g),
+// split into bf16 hi and lo parts.
+__device__ __forceinline__ void act_fragment(const float4& v0, const float4& v1, const float4& g0, const float4& g1,
+                                             bool norm, float mean, float rstd, bf16x8& hi, bf16x8& lo) {
+    float4 a = v0, b = v1;
+    if (norm) {
+        a = make_float4((a.x - mean) * rstd * g0.x, (a.y - mean) * rstd * g0.y, (a.z - mean) * rstd * g0.z,
+                        (a.w - mean) * rstd * g0.w);
+        b = make_float4((b.x - mean) * rstd * g1.x, (b.y - mean) * rstd * g1.y, (b.z - mean) * rstd * g1.z,
+                        (b.w - mean) * rstd * g1.w);
+    }
+    uint2 h0, l0, h1, l1;
+    df::split_hi_lo(a, h0, l0);
+    df::split_hi_lo(b, h1, l1);
+    hi = __builtin_bit_cast(bf16x8, (u32x4){h0.x, h0.y, h1.x, h1.y});
+    lo = __builtin_bit_cast(bf16x8, (u32x4){l0.x, l0.y, l1.x, l1.y});
+}
+
+// Finished products of weight rows n0 .. n0 + 3 (y) for logical row m: the
+// slice's partial sums, or with one slice the epilogue (the aux row 2b + 1
+// is the neighbouring lane of the primary row 2b). Every lane of the wave
+// calls it (the shuffle).
+__device__ __forceinline__ void tile_out(const GParams& p, int s, int m, int n0, bool valid, const f32x4& y) {
+    if (p.S > 1 || p.epi == EPI_RESID || p.epi == EPI_PART) {
+        if (valid && m < p.M) *reinterpret_cast<f32x4*>(p.part + ((size_t)s * p.M + m) * p.N + n0) = y;
+        return;
+    }
+    const bool dual = p.nflows == 2;
+    #pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float partner = __shfl_xor(y[r], 1, 64);
+        if (!valid || m >= p.M) continue;
+        if (dual) {
+            if ((m & 1) == 0) epilogue<bf16_t>(p, n0 + r, m >> 1, y[r], partner);
+        } else {
+            epilogue<bf16_t>(p, n0 + r, m, y[r], 0.f);
+        }
+    }
+}
+
+// Shape R (up to 32 stacked rows). The NW waves of a workgroup split its
+// k-slice (KS = NW * KWB * 32 columns) into sub-ranges of KWB 32-column
+// blocks; each wave holds the activation fragments of its sub-range in
+// registers (hi and lo parts, normalised on the fly for a residual input)
+// and streams the matching weight fragments of TB 16-row tiles per batch
+// straight from global memory (one contiguous KWB KiB piece per tile), two
+// batches in flight. The NW partial products of a batch are added in wave
+// order through LDS (double-buffered) and stored as the slice's partial sums
+// (or, with one slice, run through the epilogue). No activation fragment is
+// read from LDS, and every wave of a workgroup does the same work.
+template <int MT, int NW, int KWB, int TB>
+__global__ __launch_bounds__(NW * 64) void gemv_r(GParams p) {
+    constexpr int KS = NW * KWB * 32, NT = NW * 64, NP = TB * MT;
+    constexpr int SPT = (16 * MT * 16 + NT - 1) / NT;
+    extern __shared__ f32x4 red[];   // [2][NW][NP][64]
+    __shared__ float s_mean[16 * MT], s_rstd[16 * MT];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int S = p.S;
+    const int s = blockIdx.x % S, grp = blockIdx.x / S, ngrp = gridDim.x / S;
+    const int NT16 = p.N / 16, KB = p.K / 32;
+    const int t_lo = (int)((long)grp * NT16 / ngrp), t_hi = (int)((long)(grp + 1) * NT16 / ngrp);
+    const int nb = (t_hi - t_lo + TB - 1) / TB;
+    const int kb0 = s * (KS / 32) + wv * KWB;
+    const bf16_t* W = reinterpret_cast<const bf16_t*>(p.w);
+    const float* X = reinterpret_cast<const float*>(p.x);
+    const bool norm = p.x_stats != nullptr;
+
+    // loads first: row statistics, gains, activations, then two weight batches
+    RowStats<SPT, NT> st;
+    if (norm) st.load(p, 16 * MT);
+    float4 gv[KWB][2], xv[MT][KWB][2];
+    #pragma unroll
+    for (int kb = 0; kb < KWB; ++kb) {
+        const int k = (kb0 + kb) * 32 + lg * 8;
+        if (norm) {
+            gv[kb][0] = *reinterpret_cast<const float4*>(p.x_gain + k);
+            gv[kb][1] = *reinterpret_cast<const float4*>(p.x_gain + k + 4);
+        }
+        #pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = min(mt * 16 + li, p.M - 1);
+            const float* q = X + (size_t)(m * p.row_step) * p.K + k;
+            xv[mt][kb][0] = *reinterpret_cast<const float4*>(q);
+            xv[mt][kb][1] = *reinterpret_cast<const float4*>(q + 4);
+        }
+    }
+    const bf16_t* dummy = reinterpret_cast<const bf16_t*>(X);
+    auto load = [&](int j, u32x4 (&a)[TB][KWB]) {
+        #pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = t_lo + j * TB + tb;
+            const bool real = j < nb && t < t_hi;
+            const bf16_t* q = W + (((size_t)min(t, NT16 - 1) * KB + kb0) * 64 + lane) * 8;
+            q = real ? q : dummy;   // past the end: a fixed hot address, no branch
+            #pragma unroll
+            for (int kb = 0; kb < KWB; ++kb)
+                a[tb][kb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + (real ? 512 * kb : 0)));
+        }
+    };
+    u32x4 a0[TB][KWB], a1[TB][KWB];
+    load(0, a0);
+    load(1, a1);
+    if (norm) {
+        st.reduce(p, 16 * MT, s_mean, s_rstd);
+        __syncthreads();
+    }
+    bf16x8 xh[MT][KWB], xl[MT][KWB];
+    #pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + li;
+        const float mean = norm ? s_mean[m] : 0.f, rstd = norm ? s_rstd[m] : 0.f;
+        #pragma unroll
+        for (int kb = 0; kb < KWB; ++kb)
+            act_fragment(xv[mt][kb][0], xv[mt][kb][1], gv[kb][0], gv[kb][1], norm, mean, rstd, xh[mt][kb],
+                         xl[mt][kb]);
+    }
+
+    auto step = [&](int j, u32x4 (&cur)[TB][KWB]) {
+        f32x4 acc[TB][MT];
+        #pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+            #pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[tb][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int kb = 0; kb < KWB; ++kb)
+            #pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, cur[tb][kb]);
+                #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[tb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xh[mt][kb], acc[tb][mt], 0, 0, 0);
+                    acc[tb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, xl[mt][kb], acc[tb][mt], 0, 0, 0);
+                }
+            }
+        load(j + 2, cur);
+        f32x4* rb = red + (size_t)(j & 1) * NW * NP * 64;
+        #pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+            #pragma unroll
+            for (int mt = 0; mt < MT; ++mt) rb[((size_t)wv * NP + tb * MT + mt) * 64 + lane] = acc[tb][mt];
+        __syncthreads();
+        for (int pr = wv; pr < NP; pr += NW) {   // waves add the NW partial products in wave order
+            const int tb = pr / MT, mt = pr - (pr / MT) * MT;
+            f32x4 y = rb[(size_t)pr * 64 + lane];
+            #pragma unroll
+            for (int w = 1; w < NW; ++w) y += rb[((size_t)w * NP + pr) * 64 + lane];
+            const int t = t_lo + j * TB + tb;
+            tile_out(p, s, mt * 16 + li, t * 16 + 4 * lg, t < t_hi, y);
+        }
+    };
+    int j = 0;
+    for (; j + 1 < nb; j += 2) {
+        step(j, a0);
+        step(j + 1, a1);
+    }
+    if (j < nb) step(j, a0);
+}
+
 // Sums of the S k-slice partials of logical rows m1 and m2 (m2 < 0: none),
 // column n, in slice order; the loads of sixteen slices (32 values) are in
 // flight together.
@@ -478,7 +678,22 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
 // B = 32-row tiles, 4 waves, batches of 4 fragments per tile, one batch ahead
 // (up to 32 stacked rows, for matrices with fewer than 8192 rows or at most
 // 16 M weights; plan_gemv holds the choice).
-enum Variant { VAR_A = 0, VAR_B = 1 };
+// R: the register-resident shape above (gemv_r, up to 32 stacked rows).
+enum Variant { VAR_A = 0, VAR_B = 1, VAR_R = 2 };
+
+template <typename K>
+hipError_t launch_kernel(K* fn, GParams& p, const GemvPlan& pl, int threads, hipStream_t s) {
+    hipError_t e = tile::allow_lds(reinterpret_cast<const void*>(fn), pl.lds);
+    if (e != hipSuccess) return e;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fn, dim3(pl.grid), dim3(threads), pl.lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_r(GParams& p, const GemvPlan& pl, hipStream_t s) {
+    if (pl.MT == 1) return launch_kernel(&gemv_r<1, 8, 4, 2>, p, pl, 512, s);
+    return launch_kernel(&gemv_r<2, 8, 4, 2>, p, pl, 512, s);
+}
 
 template <int MT, int RT, int KU, int NW, int KS, int NBUF>
 hipError_t launch_one(GParams& p, const GemvPlan& pl, hipStream_t s) {
@@ -564,12 +779,28 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
     if (M_slices < M) M_slices = M;
     if (dtype != DF_BF16 || M < 1 || M_slices > 128 || N < 16 || N % 16 || K < 256 || K % 256) return pl;
     pl.MT = mt_for(M);
-    pl.variant = variant_for(pl.MT, N, K);
-    // The k-slice width is the one the M_slices-row plan takes, so that every
-    // output is summed over the same k-slices (in the same order) whichever
-    // row count runs: a primary-only step then gives bitwise the primary
-    // results of a dual step.
+    // The shape and the k-slice width follow from the planned row count only,
+    // so every output is summed over the same slices, in the same order,
+    // whichever row count runs (a primary-only step gives bitwise the primary
+    // results of a dual step). The register-resident shape where it measured
+    // faster inside the decode step (per-kernel traces): up to 32 rows and
+    // matrices of 32M weights or more (1024-wide slices).
     const int mt_s = mt_for(M_slices);
+    const int NT16 = N / 16;
+    if (mt_s <= 2 && (long)N * K >= (32L << 20) && K % 1024 == 0) {
+        pl.variant = VAR_R;
+        pl.ks = 1024;
+        pl.lds = (size_t)2 * 8 * 2 * pl.MT * 64 * 16;   // the waves' partial products, double-buffered
+        pl.S = K / pl.ks;
+        const int ngrp = std::min(std::max(1, kCUs / pl.S), NT16);
+        pl.grid = ngrp * pl.S;
+        pl.nblocks = ngrp;
+        pl.part_floats = (size_t)pl.S * M * N;
+        return pl;
+    }
+    pl.variant = variant_for(pl.MT, N, K);
+    // the k-slice width of the M_slices-row plan (the kernel shape may differ:
+    // the k order within a slice is the same in both)
     const int ks = ks_for(variant_for(mt_s, N, K), mt_s, N, K);
     if (!ks_supported(pl.variant, pl.MT, ks)) return GemvPlan{};
     pl.ks = ks;
@@ -615,6 +846,11 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     if (a.epi == EPI_RESID && a.N > 4096) return hipErrorInvalidValue;
     if (a.x_stats && (!a.x_gain || a.K > kMaxSeg * kStatSeg)) return hipErrorInvalidValue;
     hipError_t e;
+    if (pl.variant == VAR_R) {
+        e = launch_r(p, pl, s);
+        if (e != hipSuccess) return e;
+        return finish(p, pl.S, s);
+    }
     switch (pl.MT) {
         case 1: e = launch_mt<1>(p, pl, s); break;
         case 2: e = launch_mt<2>(p, pl, s); break;

@@ -62,6 +62,11 @@ def test_pack_matches_layout_definition():
 CASES = [
     (2, 16, 256), (6, 48, 768), (16, 1024, 512), (32, 8192, 1024), (32, 4096, 4096), (32, 12288, 4096),
     (32, 4096, 16384), (32, 32000, 4096), (64, 2048, 1536), (128, 6144, 2048), (128, 64, 2048), (30, 1040, 2304),
+    # the register-resident shape (32M weights or more, up to 32 rows): one slice (epilogue from
+    # registers) with 2 rows, ragged tiles per row group, 16 rows and two slices; and more shapes of
+    # the others (ragged row counts, 65..128 rows)
+    (2, 32768, 1024), (32, 8208, 4096), (16, 16384, 2048), (2, 16, 512), (32, 2048, 8192), (32, 4112, 2048),
+    (100, 640, 1024), (128, 32000, 2048), (66, 2064, 512),
     # tiled GEMM (prefill rows): ragged row and column tiles, one and many k steps
     (129, 16, 32), (256, 256, 256), (1000, 1040, 512), (2048, 3072, 1024), (333, 4096, 2048),
     (4100, 2064, 2048),
