@@ -30,15 +30,19 @@ PEAK_HBM_GBS = 8000.0
 # sample walks through every layer).
 TIMING_STRIDE = 7
 
-# HBM traffic measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on the dense 32-layer
-# workload (counters scaled by their reading for a plain 1 GiB copy: x2.0 fetch, x1.0
-# write). Reported only while the kernel sources are the ones they were measured on.
+# HBM traffic measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (one pass each, 1 warm-up + 2
+# timed steps, dual and primary-only), counters scaled by their reading for a plain 1 GiB copy
+# (x2.0 fetch, x1.0 write). Reported only while the kernel sources are the ones they were
+# measured on (attention pass: attention.hip; step traffic: every library source).
+COUNTER_SOURCES = {"attention_source_sha256": "fb17a30121580a82c8b87d8ee63a3b35e3cce693132291d3a29b1ad6fb41ac14",
+                   "library_sources_sha256": "eff0ae295203895258aff1f327ac08323c59f93636aef5482fd60f17f7ccb667"}
 COUNTERS = {
-    "workload": "dense_32l_d4096_b16_ctx8192",
-    "attention_source_sha256": "2894d8d06dbc8295c03d2a3660d3a4be589a4039e8e1c56e41294cabb0d881f7",
-    "attention_traffic_bytes_per_launch": 2.1545e9,
-    "library_sources_sha256": "4a4bbbcb255a8da57cce946d39032c104098f6dce46e8a6a9d24ba90521f7868",
-    "step_traffic_bytes": {"dual": 84.620e9, "primary_only": 83.303e9},
+    "dense_32l_d4096_b16_ctx8192": {"attention_traffic_bytes_per_launch": 2.15446e+09,
+                   "step_traffic_bytes": {"dual": 8.40717e+10, "primary_only": 8.30297e+10}},
+    "dense_1p3b_b16_ctx2048": {"attention_traffic_bytes_per_launch": 2.73376e+08,
+                   "step_traffic_bytes": {"dual": 9.89258e+09, "primary_only": 9.47028e+09}},
+    "moe_16l_e64_top4_b64_ctx1024": {"attention_traffic_bytes_per_launch": 5.55975e+08,
+                   "step_traffic_bytes": {"dual": 1.98301e+10, "primary_only": 1.88828e+10}},
 }
 
 
@@ -602,12 +606,12 @@ def main():
         log(f"[bench] oracle: {cpu['value']:.4f} tok/s ({cpu['seconds_per_token']:.2f} s/token)")
 
     att_sha, lib_sha = source_hashes()
-    same_work = cfg.name == COUNTERS["workload"] and cfg.variant == 0 and not cfg.top_k_aux
-    traffic = COUNTERS["attention_traffic_bytes_per_launch"] if (
-        same_work and att_sha == COUNTERS["attention_source_sha256"]) else None
+    measured = COUNTERS.get(cfg.name) if cfg.variant == 0 and not cfg.top_k_aux else None
+    traffic = measured["attention_traffic_bytes_per_launch"] if (
+        measured and att_sha == COUNTER_SOURCES["attention_source_sha256"]) else None
     counter_ratio = None
-    if same_work and lib_sha == COUNTERS["library_sources_sha256"]:
-        st = COUNTERS["step_traffic_bytes"]
+    if measured and lib_sha == COUNTER_SOURCES["library_sources_sha256"]:
+        st = measured["step_traffic_bytes"]
         counter_ratio = st["dual"] / st["primary_only"]
 
     out = {
