@@ -63,7 +63,7 @@ struct GemmParams {
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-__global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16(GemmParams p) {
     extern __shared__ u32x4 lds[];   // [stage][piece][lane]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int wn = wv & 1, wr = wv >> 1;           // 128 weight rows x 64 activation rows per wave
@@ -115,21 +115,36 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16(GemmParams p) {
         asm volatile("s_barrier" ::: "memory");
         issue(min(kb + 2, KB - 1), st == 0 ? 2 : st - 1);   // stage of block kb - 1 (clamped: always PPW loads)
         const u32x4* S = lds + (size_t)st * PIECES * 64;
-        bf16x8 bh[4], bl[4];
+        // every operand fragment of the block is read up front, in the order the
+        // matrix cores consume them (hi parts first), so each product waits only
+        // for its own operands and the lo parts land behind the 32 hi products
+        bf16x8 a[8], bh[4], bl[4];
+        bh[0] = __builtin_bit_cast(bf16x8, S[(TT16 + wr * 4) * 64 + lane]);
         #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            bh[mt] = __builtin_bit_cast(bf16x8, S[(TT16 + wr * 4 + mt) * 64 + lane]);
-            bl[mt] = __builtin_bit_cast(bf16x8, S[(2 * TT16 + wr * 4 + mt) * 64 + lane]);
-        }
+        for (int nt = 0; nt < 8; ++nt) a[nt] = __builtin_bit_cast(bf16x8, S[(wn * 8 + nt) * 64 + lane]);
         #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, S[(wn * 8 + nt) * 64 + lane]);
+        for (int mt = 1; mt < 4; ++mt) bh[mt] = __builtin_bit_cast(bf16x8, S[(TT16 + wr * 4 + mt) * 64 + lane]);
+        #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) bl[mt] = __builtin_bit_cast(bf16x8, S[(2 * TT16 + wr * 4 + mt) * 64 + lane]);
+        #pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
             #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[mt], acc[nt][mt], 0, 0, 0);
-                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[mt], acc[nt][mt], 0, 0, 0);
-            }
-        }
+            for (int nt = 0; nt < 8; ++nt)
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[nt], bh[mt], acc[nt][mt], 0, 0, 0);
+        #pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            #pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[nt], bl[mt], acc[nt][mt], 0, 0, 0);
+        // schedule: ten LDS reads (bh[0], a[], bh[1]), the first eight products,
+        // the six other reads, the other 56 products; fewer than 16 reads are
+        // ever outstanding, so each product waits only for its own operands
+        // (the compiler's own order reuses operand registers and waits for
+        // every read three times per block)
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 56, 0);
         st = st == 2 ? 0 : st + 1;
     }
     GEMM_WAIT_VM(0);             // no load still landing when the wave leaves
