@@ -587,6 +587,7 @@ def main():
         prim_ms = e0.elapsed_time(e1) / K
         log(f"[bench] primary-only: {prim_ms:.3f} ms/step")
 
+    read_ceiling = None
     if args.copy_calibration:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -594,7 +595,21 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log("[bench] calibration copy of 1 GiB done")
-        del a, b
+        # a plain read of the same 1 GiB by a library reduction (row sums of a [262144, 4096]
+        # fp32 view: the fastest torch read measured on the box), for the practical read rate
+        ai = a.view(torch.float32).view(-1, 4096)
+        ai.sum(dim=1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            ai.sum(dim=1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 5
+        read_ceiling = {"bytes": n, "us": us, "GBs": n / us / 1e3,
+                        "how": "torch row sums over a [262144, 4096] fp32 view of 1 GiB, 5 calls"}
+        log(f"[bench] plain 1 GiB read (torch row sums): {us:.1f} us, {n / us / 1e3:.0f} GB/s")
+        del a, b, ai
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -635,6 +650,8 @@ def main():
         "device_status": status,
         "cpu_baseline": cpu,
     }
+    if read_ceiling:
+        out["read_ceiling"] = read_ceiling
     print(json.dumps(out), flush=True)
 
 
