@@ -84,6 +84,52 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def stream_read_ceiling(buf, attn_bytes: float, attn_gbs: float, stream) -> dict:
+    """The practical read rate of the device in the attention pass's launch
+    shape: df_stream_read (one 4-wave workgroup per CU, contiguous share per
+    wave, 16-byte non-temporal loads) over the first bytes of `buf` (the K
+    cache), 10 back-to-back calls per size. Sizes 8 MiB .. 512 MiB give the
+    fixed cost per launch and the streaming rate (least squares of time =
+    fixed + bytes / rate); one size equals the attention pass's bytes per
+    launch, whose rate the attention's is compared with."""
+    import numpy as np
+    import torch
+
+    from dual_flow_transformer_amd import _abi
+
+    have = buf.numel() * buf.element_size()
+    out = torch.zeros(_abi.DF_STREAM_READ_OUT_WORDS, dtype=torch.int32, device="cuda")
+    att = int(attn_bytes) // 16 * 16
+    sizes = [n for n in (8 << 20, 32 << 20, 128 << 20, 512 << 20) if n <= have]
+    rows = []
+    for n in sizes + ([att] if att <= have else []):
+        call = lambda: _abi.check(_abi.df_stream_read(buf.data_ptr(), n, out.data_ptr(), stream.cuda_stream),
+                                  "df_stream_read")
+        call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rows.append((n, e0.elapsed_time(e1) * 1e3 / 10))
+    res = {"kernel": "df_stream_read", "calls_per_size": 10,
+           "bytes": [r[0] for r in rows], "us_per_call": [round(r[1], 2) for r in rows]}
+    if len(sizes) >= 2:
+        x = np.array([r[0] for r in rows[:len(sizes)]], dtype=np.float64)
+        y = np.array([r[1] for r in rows[:len(sizes)]], dtype=np.float64)
+        slope, fixed = np.polyfit(x, y, 1)
+        res["fit_fixed_us"] = float(fixed)
+        res["fit_streaming_GBs"] = float(1e-3 / slope)
+    if att <= have:
+        read_gbs = att / rows[-1][1] / 1e3
+        res["attention_bytes_GBs"] = read_gbs
+        res["attention_frac_of_read"] = attn_gbs / read_gbs
+        log(f"[bench] streaming read of the attention's {att / 1e9:.3f} GB: {rows[-1][1]:.1f} us "
+            f"({read_gbs:.0f} GB/s); attention pass at {attn_gbs / read_gbs:.3f} of it")
+    return res
+
+
 def cpu_baseline(cfg, n_layers: int, min_seconds: float = 10.0):
     """The CPU oracle as it stands, on a bounded sample: sequence 0 of the
     workload through its first n_layers layers plus the LM head and mixture
@@ -587,7 +633,6 @@ def main():
         prim_ms = e0.elapsed_time(e1) / K
         log(f"[bench] primary-only: {prim_ms:.3f} ms/step")
 
-    read_ceiling = None
     if args.copy_calibration:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -595,21 +640,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log("[bench] calibration copy of 1 GiB done")
-        # a plain read of the same 1 GiB by a library reduction (row sums of a [262144, 4096]
-        # fp32 view: the fastest torch read measured on the box), for the practical read rate
-        ai = a.view(torch.float32).view(-1, 4096)
-        ai.sum(dim=1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            ai.sum(dim=1)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / 5
-        read_ceiling = {"bytes": n, "us": us, "GBs": n / us / 1e3,
-                        "how": "torch row sums over a [262144, 4096] fp32 view of 1 GiB, 5 calls"}
-        log(f"[bench] plain 1 GiB read (torch row sums): {us:.1f} us, {n / us / 1e3:.0f} GB/s")
-        del a, b, ai
+        del a, b
+
+    read_ceiling = stream_read_ceiling(gm.k, attn_bytes_per_launch, attn_gbs, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -650,8 +683,7 @@ def main():
         "device_status": status,
         "cpu_baseline": cpu,
     }
-    if read_ceiling:
-        out["read_ceiling"] = read_ceiling
+    out["read_ceiling"] = read_ceiling
     print(json.dumps(out), flush=True)
 
 

@@ -33,8 +33,9 @@ EXPORTS = ["df_workspace_bytes", "df_prefill_workspace_bytes", "df_forward_works
            "df_decode_step", "df_prefill_primary", "df_kv_append", "df_mix_head",
            "df_attention_dual", "df_attention_workspace_bytes", "df_device_status", "df_status_str",
            "df_timing_enable", "df_timing_read", "df_stacked_gemv", "df_stacked_gemv_workspace_bytes",
-           "df_pack_weights", "df_attention_dual_noalloc"]
+           "df_pack_weights", "df_attention_dual_noalloc", "df_stream_read"]
 DF_ATTENTION_NOALLOC_SCRATCH_BYTES = 17040384
+DF_STREAM_READ_OUT_WORDS = 4096
 
 
 class df_config(ctypes.Structure):
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.df_stacked_gemv_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.df_pack_weights.restype = ctypes.c_int
         L.df_pack_weights.argtypes = [i32, vp, vp, ctypes.c_int64, i32, i32, vp]
+        L.df_stream_read.restype = ctypes.c_int
+        L.df_stream_read.argtypes = [vp, sz, vp, vp]
         L.df_timing_enable.restype = ctypes.c_int
         L.df_timing_enable.argtypes = [i32, i32]
         L.df_timing_read.restype = ctypes.c_int
@@ -198,6 +201,10 @@ def df_stacked_gemv_workspace_bytes(dtype, rows, N, K) -> int:
 
 def df_pack_weights(dtype, d_src, d_dst, n_mats, rows, cols, stream=0) -> int:
     return lib().df_pack_weights(int(dtype), d_src, d_dst, int(n_mats), int(rows), int(cols), stream)
+
+
+def df_stream_read(d_src, nbytes, d_out, stream=0) -> int:
+    return lib().df_stream_read(d_src, nbytes, d_out, stream)
 
 
 def df_timing_enable(kclass: int = 0, stride: int = 1) -> int:

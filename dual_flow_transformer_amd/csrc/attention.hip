@@ -124,7 +124,9 @@ __device__ __forceinline__ int keys_of(const int32_t* nkeys, int b, int add, int
     return n < 0 ? 0 : (n > S_max ? S_max : n);
 }
 
-template <typename T, int DH, int U>
+// FUSED: the queries (and the new key's K/V) come from the Q/K/V
+// projection's k-slice partial sums (p.qkv); otherwise from p.q.
+template <typename T, int DH, int U, bool FUSED>
 __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte load
     constexpr int LPP = DH / EPL;              // lanes per key row
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
 
     // Key offsets of the sequences (lane b holds sequence b): pair (b, h)
     // starts at key off_b + h * n_b of the flattened range.
+    const int my_raw = lane < p.B ? p.nkeys[lane] : 0;   // the position of the new key (fused finish)
     const int my_n = lane < p.B ? keys_of(p.nkeys, lane, p.nkeys_add, p.S_max) : 0;
     long long incl = (long long)p.H * my_n;      // inclusive prefix over lanes
     for (int o = 1; o < 64; o <<= 1) {
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     if (blockIdx.x == 0 && threadIdx.x < 64) {   // for the combine pass
         if (lane < p.B) p.seq_tab[lane] = my_off;
         if (lane == 0) p.seq_tab[p.B] = KT;
-        if (p.qkv && p.status) {   // a new key outside the cache is not written
+        if (FUSED && p.status) {   // a new key outside the cache is not written
             const int pos = lane < p.B ? p.nkeys[lane] : 0;
             if (__ballot(pos < 0 || pos >= p.S_max) != 0 && lane == 0) p.status[0] |= 1;
         }
@@ -158,10 +161,10 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     const long long k_end = min(total, (long long)(w + 1) * KT);
     long long key = (long long)w * KT;
     while (key < k_end) {
-        // sequence of this key: the last b whose offset <= key
-        int b = 0;
-        for (int bb = 1; bb < p.B; ++bb)
-            if (__shfl(my_off, bb, 64) <= key) b = bb;
+        // sequence of this key: the last b whose offset <= key (it has
+        // keys: a sequence without keys shares its offset with the next)
+        const unsigned long long below = __ballot(lane < p.B && my_off <= key);
+        const int b = 63 - __builtin_clzll(below);   // lane 0: offset 0 <= key
         const int n = __shfl(my_n, b, 64);
         const long long off_b = __shfl(my_off, b, 64);
         const int h = (int)((key - off_b) / n);
@@ -172,11 +175,38 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
         key = pair_lo + end;
         // the new key (fused finish only): position n - 1 = nkeys[b], the
         // last key of the pair, lies in this segment
-        const bool fused = p.qkv != nullptr;
-        const bool has_new = fused && end == n && p.nkeys[b] == n - 1;
+        constexpr bool fused = FUSED;
+        const bool has_new = fused && end == n && __shfl(my_raw, b, 64) == n - 1;
         const size_t n3 = (size_t)3 * p.H * DH;
         const float* qkv_row = fused ? p.qkv + (size_t)(dual ? 2 * b : b) * n3 + h * DH + sub * EPL : nullptr;
         const size_t qkv_stride = (size_t)p.qkv_M * n3;
+        const size_t off = (size_t)b * p.seq_stride + (size_t)h * p.S_max * DH + sub * EPL;
+        const T* kp = reinterpret_cast<const T*>(p.k) + off;
+        const T* vp = reinterpret_cast<const T*>(p.v) + off;
+        // keys read from the cache: [start, kend) (the new key, if in this
+        // segment, comes from the slice sums); the bounds are the same in
+        // every lane and kept as scalars
+        const int kend = __builtin_amdgcn_readfirstlane(has_new ? end - 1 : end);
+        const int j_start = __builtin_amdgcn_readfirstlane(start);
+        // U rows per lane group of K and of V; past kend the last key is
+        // read again and masked out of the scores
+        auto load_block = [&](int j0, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = min(j0 + u * PPW + g, kend - 1);
+                kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)j * DH));
+            }
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = min(j0 + u * PPW + g, kend - 1);
+                vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)j * DH));
+            }
+        };
+        // the segment's first block is requested before the queries, so the
+        // two round trips overlap
+        u32x4 kr[U], vr[U];
+        if (j_start < kend) load_block(j_start, kr, vr);
+
         float q1[EPL], q2[EPL], kn[EPL], vn[EPL];   // kn, vn: the new key's K and V (has_new)
         {
             const float* qp = p.q + ((size_t)(b * 2) * p.H + h) * DH + sub * EPL;
@@ -219,16 +249,11 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
             #pragma unroll
             for (int e = 0; e < EPL; ++e) { q1[e] *= p.scale_log2; q2[e] *= p.scale_log2; }
         }
-        const size_t off = (size_t)b * p.seq_stride + (size_t)h * p.S_max * DH + sub * EPL;
-        const T* kp = reinterpret_cast<const T*>(p.k) + off;
-        const T* vp = reinterpret_cast<const T*>(p.v) + off;
-
         float m1 = -1e30f, l1 = 0.f, m2 = -1e30f, l2 = 0.f;
         float o1[EPL], o2[EPL];
         #pragma unroll
         for (int e = 0; e < EPL; ++e) { o1[e] = 0.f; o2[e] = 0.f; }
 
-        int kend = end;   // keys read from the cache: [start, kend)
         if (has_new) {
             // K and V of the primary row (slice sums), rounded to the cache
             // type, written to the cache at the new position by lane group 0,
@@ -251,23 +276,9 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
                 #pragma unroll
                 for (int e = 0; e < EPL; ++e) { o1[e] = vn[e]; o2[e] = dual ? vn[e] : 0.f; }
             }
-            kend = end - 1;
         }
 
-        for (int j0 = start; j0 < kend; j0 += PPW * U) {
-            u32x4 kr[U], vr[U];
-            #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                int j = j0 + u * PPW + g;
-                j = j < kend ? j : kend - 1;
-                kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)j * DH));
-            }
-            #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                int j = j0 + u * PPW + g;
-                j = j < kend ? j : kend - 1;
-                vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)j * DH));
-            }
+        for (int j0 = j_start; j0 < kend;) {
             float s1[U], s2[U];
             #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -301,6 +312,9 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
                 #pragma unroll
                 for (int e = 0; e < EPL; ++e) { o1[e] = fmaf(p1, vv[e], o1[e]); o2[e] = fmaf(p2, vv[e], o2[e]); }
             }
+            j0 += PPW * U;
+            if (j0 >= kend) break;
+            load_block(j0, kr, vr);
         }
 
         // Merge the PPW lane groups (same dims, different key subsets).
@@ -468,8 +482,9 @@ hipError_t launch(const AttnArgs& a, hipStream_t s) {
     p.qkv = a.qkv_part; p.qkv_S = a.qkv_S; p.qkv_M = a.nflows == 2 ? 2 * a.B : a.B; p.status = a.status;
     if (p.qkv && (a.nkeys_add != 1 || a.qkv_S < 1)) return hipErrorInvalidValue;
     void* args[] = {&p};
-    hipError_t e = launch_timed(reinterpret_cast<const void*>(&attn_partial<T, DH, U>), dim3(waves / 4), dim3(256),
-                                args, 0, s, a.ev_start, a.ev_stop);
+    const void* fn = p.qkv ? reinterpret_cast<const void*>(&attn_partial<T, DH, U, true>)
+                           : reinterpret_cast<const void*>(&attn_partial<T, DH, U, false>);
+    hipError_t e = launch_timed(fn, dim3(waves / 4), dim3(256), args, 0, s, a.ev_start, a.ev_stop);
     if (e != hipSuccess) return e;
     CombParams c;
     c.part_o = p.part_o; c.part_ml = p.part_ml; c.seq_tab = p.seq_tab; c.nkeys = a.nkeys; c.o_f32 = a.o_f32;

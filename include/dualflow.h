@@ -339,6 +339,23 @@ int df_device_status(void* d_ws, void* stream, int32_t* status_out);
 /* Text of a DF_* return code. */
 const char* df_status_str(int code);
 
+/* A measurement instrument, not a step of the method: a plain streaming
+ * read of `bytes` bytes at d_src in the launch shape of the decode
+ * attention pass (one 4-wave workgroup per compute unit, each wave reading
+ * one contiguous share with 16-byte non-temporal loads). Its duration is the
+ * read rate that pass, which reads each K/V byte once, can at best reach on
+ * the device; small sizes give the fixed cost of one launch.
+ *  d_src: device memory, 16-byte aligned; bytes: a multiple of 16 (0 is
+ *  allowed). d_out: device uint32 [DF_STREAM_READ_OUT_WORDS]; wave w writes
+ *  the XOR of the 32-bit words it read to d_out[w] (w < 4 x compute units),
+ *  the other words are untouched: with d_out cleared first, the XOR of all
+ *  its words is the XOR of every word of the source.
+ * Asynchronous on `stream`. DF_ERR_NULL, DF_ERR_ALIGN (pointer or size),
+ * DF_ERR_SHAPE (device with more than DF_STREAM_READ_OUT_WORDS / 4 compute
+ * units), DF_ERR_HIP (launch failure). */
+#define DF_STREAM_READ_OUT_WORDS 4096
+int df_stream_read(const void* d_src, size_t bytes, uint32_t* d_out, void* stream);
+
 /* Kernel timing with HIP events on the launching stream. While enabled,
  * launches of the kernels of class `kclass` (0 = attention partial pass
  * of a decode step, 1 = tiled GEMM of the prefill projections, 2 = causal

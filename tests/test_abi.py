@@ -151,6 +151,12 @@ def test_other_entry_points_reject_bad_arguments():
     assert a(wsb=16) == _abi.DF_ERR_WORKSPACE
     assert _abi.df_timing_enable(5) == _abi.DF_ERR_ARG
     assert _abi.df_timing_enable(0, 0) == _abi.DF_ERR_ARG
+    # streaming read: pointer and size checks come before any device query
+    assert _abi.df_stream_read(None, 1024, 0x1000) == _abi.DF_ERR_NULL
+    assert _abi.df_stream_read(0x1000, 1024, None) == _abi.DF_ERR_NULL
+    assert _abi.df_stream_read(0x1008, 1024, 0x2000) == _abi.DF_ERR_ALIGN
+    assert _abi.df_stream_read(0x1000, 1000, 0x2000) == _abi.DF_ERR_ALIGN
+    assert _abi.df_stream_read(0x1000, 1024, 0x2002) == _abi.DF_ERR_ALIGN
 
 
 def test_status_strings():
