@@ -34,15 +34,15 @@ TIMING_STRIDE = 7
 # timed steps, dual and primary-only), counters scaled by their reading for a plain 1 GiB copy
 # (x2.0 fetch, x1.0 write). Reported only while the kernel sources are the ones they were
 # measured on (attention pass: attention.hip; step traffic: every library source).
-COUNTER_SOURCES = {"attention_source_sha256": "fb17a30121580a82c8b87d8ee63a3b35e3cce693132291d3a29b1ad6fb41ac14",
-                   "library_sources_sha256": "eff0ae295203895258aff1f327ac08323c59f93636aef5482fd60f17f7ccb667"}
+COUNTER_SOURCES = {"attention_source_sha256": "f92b9ef8bfee3b3aa837ace3c52fadd3416d1a81741a722506eb049e9aeb04e0",
+                   "library_sources_sha256": "e386da7d50bbb87deb679f8a3193fa3fc743a246fcc09830dfebc4fbf4e5b990"}
 COUNTERS = {
-    "dense_32l_d4096_b16_ctx8192": {"attention_traffic_bytes_per_launch": 2.15446e+09,
-                   "step_traffic_bytes": {"dual": 8.40717e+10, "primary_only": 8.30297e+10}},
-    "dense_1p3b_b16_ctx2048": {"attention_traffic_bytes_per_launch": 2.73376e+08,
-                   "step_traffic_bytes": {"dual": 9.89258e+09, "primary_only": 9.47028e+09}},
-    "moe_16l_e64_top4_b64_ctx1024": {"attention_traffic_bytes_per_launch": 5.55975e+08,
-                   "step_traffic_bytes": {"dual": 1.98301e+10, "primary_only": 1.88828e+10}},
+    "dense_32l_d4096_b16_ctx8192": {"attention_traffic_bytes_per_launch": 2.15450e+09,
+                   "step_traffic_bytes": {"dual": 8.40720e+10, "primary_only": 8.30300e+10}},
+    "dense_1p3b_b16_ctx2048": {"attention_traffic_bytes_per_launch": 2.73400e+08,
+                   "step_traffic_bytes": {"dual": 9.89400e+09, "primary_only": 9.47100e+09}},
+    "moe_16l_e64_top4_b64_ctx1024": {"attention_traffic_bytes_per_launch": 5.56000e+08,
+                   "step_traffic_bytes": {"dual": 1.98310e+10, "primary_only": 1.88830e+10}},
 }
 
 
