@@ -103,3 +103,125 @@ def test_c3_three_steps_teacher_forced():
                     ref = cache.appended[(l, b, cfg.ctx + s_)][which]
                     assert np.all(np.abs(got[:, s_] - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, b, s_, which)
                 assert np.all(got[:, 3] == 0), "write beyond position len"
+
+
+def test_c3_bench_loop_steady_state():
+    """The benchmark's own loop on the dense 1.3B workload: 23 dual steps
+    (3 warm-up + 20 timed), each fed the previous step's next_tok, new keys
+    at positions 2048 .. 2070. The oracle replays the same token stream for
+    sequences 0 and 9 (teacher-forced on the GPU's choices, which must be
+    the oracle's argmax at every step): each step's logits, p_mix, alpha and
+    argmax, and every layer's 23 appended K/V entries."""
+    base = PRESETS["c3"]
+    n = 23
+    cfg = base.replace(S_max=base.ctx + n + 8)
+    seqs = [0, 9]
+    say(f"full-size {cfg.name}: {n} steps fed from next_tok, oracle on sequences {seqs}")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    m = odf.Model(src, keep_layers=False)
+    cache = odf.Cache(cfg, seqs, src, lazy=True)
+    tok = src.step_tokens(0)[seqs]
+    for step in range(n):
+        gm.decode_step(gm.tokens(src.step_tokens(0)) if step == 0 else gm.next_tok)
+        torch.cuda.synchronize()
+        assert gm.status() == 0
+        lg = gm.logits.cpu().numpy()[seqs]
+        pm = gm.p_mix.cpu().numpy()[seqs]
+        al = gm.alpha.cpu().numpy()[seqs]
+        nt = gm.next_tok.cpu().numpy()[seqs]
+        r = odf.decode_step(m, cache, tok, aux_on=True)
+        el, ep = max_abs(lg, r.logits), max_abs(pm, r.p_mix)
+        if step % 5 == 0 or step == n - 1:
+            say(f"  step {step}: logits max|d|={el:.3e} p_mix max|d|={ep:.3e}")
+        assert el < 2e-2 and ep < 1e-3 and max_abs(al, r.alpha) < 1e-3, step
+        for i in range(len(seqs)):
+            assert argmax_agrees(pm[i], r.p_mix[i], nt[i], margin=2e-3), (step, i)
+        tok = nt.astype(np.int64)
+    assert np.array_equal(gm.len.cpu().numpy()[seqs], cache.lens)
+    for l in range(cfg.L):
+        for i, b in enumerate(seqs):
+            for t, which in ((gm.k, 0), (gm.v, 1)):
+                got = bits_to_f64(t[l, b, :, cfg.ctx:cfg.ctx + n + 1].cpu(), cfg.dtype)    # [H, n + 1, Dh]
+                for s_ in range(n):
+                    ref = cache.appended[(l, b, cfg.ctx + s_)][which]
+                    assert np.all(np.abs(got[:, s_] - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, b, s_, which)
+                assert np.all(got[:, n] == 0), "write beyond position len"
+
+
+def test_c4_three_steps_teacher_forced():
+    """Three consecutive dual steps of the MoE workload (batch 64, router
+    replay), each with its own primary router logits, teacher-forced on the
+    workload's step tokens, against the oracle on sequences 5 and 50: each
+    step's logits, p_mix, alpha, argmax and expert ids (bit-exact), and every
+    layer's three appended K/V entries."""
+    cfg = PRESETS["c4"]
+    seqs = [5, 50]
+    say(f"full-size {cfg.name}: three steps, oracle on sequences {seqs}")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    m = odf.Model(src, keep_layers=False)
+    cache = odf.Cache(cfg, seqs, src, lazy=True)
+    for step in range(3):
+        tok = src.step_tokens(step)
+        rl = gm.router_logits(step)
+        gm.decode_step(gm.tokens(tok), router_logits=rl)
+        torch.cuda.synchronize()
+        assert gm.status() == 0
+        lg = gm.logits.cpu().numpy()[seqs]
+        pm = gm.p_mix.cpu().numpy()[seqs]
+        al = gm.alpha.cpu().numpy()[seqs]
+        nt = gm.next_tok.cpu().numpy()[seqs]
+        ids = gm.expert_ids.cpu().numpy()[:, seqs]
+        r = odf.decode_step(m, cache, tok[seqs], aux_on=True, router_logits=rl.cpu().numpy()[:, seqs])
+        el, ep = max_abs(lg, r.logits), max_abs(pm, r.p_mix)
+        say(f"  step {step}: logits max|d|={el:.3e} p_mix max|d|={ep:.3e}")
+        assert el < 2e-2 and ep < 1e-3 and max_abs(al, r.alpha) < 1e-3
+        assert np.array_equal(ids, r.ids), ("expert ids differ", step)
+        for i in range(len(seqs)):
+            assert argmax_agrees(pm[i], r.p_mix[i], nt[i], margin=2e-3)
+    for l in range(cfg.L):
+        for i, b in enumerate(seqs):
+            for t, which in ((gm.k, 0), (gm.v, 1)):
+                got = bits_to_f64(t[l, b, :, cfg.ctx:cfg.ctx + 4].cpu(), cfg.dtype)
+                for s_ in range(3):
+                    ref = cache.appended[(l, b, cfg.ctx + s_)][which]
+                    assert np.all(np.abs(got[:, s_] - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, b, s_, which)
+                assert np.all(got[:, 3] == 0), "write beyond position len"
+
+
+def test_c5_three_steps_teacher_forced():
+    """Three consecutive dual steps of the dense large workload (32 layers,
+    d 4096, context 8192: the benchmark's default), teacher-forced on the
+    workload's step tokens, against the oracle on sequence 11: each step's
+    logits, p_mix, alpha and argmax, and every layer's three appended K/V
+    entries (keys at positions 8192, 8193, 8194)."""
+    cfg = PRESETS["c5"]
+    seqs = [11]
+    say(f"full-size {cfg.name}: three steps, oracle on sequence {seqs}")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    m = odf.Model(src, keep_layers=False)
+    cache = odf.Cache(cfg, seqs, src, lazy=True)
+    for step in range(3):
+        tok = src.step_tokens(step)
+        gm.decode_step(gm.tokens(tok))
+        torch.cuda.synchronize()
+        assert gm.status() == 0
+        lg = gm.logits.cpu().numpy()[seqs]
+        pm = gm.p_mix.cpu().numpy()[seqs]
+        al = gm.alpha.cpu().numpy()[seqs]
+        nt = gm.next_tok.cpu().numpy()[seqs]
+        r = odf.decode_step(m, cache, tok[seqs], aux_on=True)
+        el, ep = max_abs(lg, r.logits), max_abs(pm, r.p_mix)
+        say(f"  step {step}: logits max|d|={el:.3e} p_mix max|d|={ep:.3e}")
+        assert el < 2e-2 and ep < 1e-3 and max_abs(al, r.alpha) < 1e-3
+        assert argmax_agrees(pm[0], r.p_mix[0], nt[0], margin=2e-3)
+    for l in range(cfg.L):
+        b = seqs[0]
+        for t, which in ((gm.k, 0), (gm.v, 1)):
+            got = bits_to_f64(t[l, b, :, cfg.ctx:cfg.ctx + 4].cpu(), cfg.dtype)
+            for s_ in range(3):
+                ref = cache.appended[(l, b, cfg.ctx + s_)][which]
+                assert np.all(np.abs(got[:, s_] - ref) <= KV_REL * np.abs(ref) + KV_ABS), (l, s_, which)
+            assert np.all(got[:, 3] == 0), "write beyond position len"
