@@ -22,25 +22,23 @@ typedef char* bf16p;   // byte pointer into bf16 hi / lo planes
 
 // Workspace regions (byte offsets from the workspace base).
 struct WsLayout {
-    size_t status, h, xd, xo, xf, q, part, logits, ids, gates, grows, yrows, gpart, gcount,
+    size_t status, h, xd, xo, xf, q, part, logits, ids, gates, grows, yrows, gpart,
         stats, total;
 };
 
-// Largest split-K partial buffer and row-block count over the model's GEMVs.
-void gemv_scratch(const df_config& c, size_t* part_floats, size_t* blocks) {
+// Largest split-K partial buffer over the model's GEMVs.
+void gemv_scratch(const df_config& c, size_t* part_floats) {
     const bool moe = c.n_experts > 0;
     const int d = c.d_model;
     const int shapes[5][2] = {{3 * d, d}, {d, d}, {moe ? 0 : c.ffn, d}, {d, moe ? 0 : c.ffn},
                               {c.vocab, d}};
     *part_floats = 0;
-    *blocks = 0;
     for (int M : {2 * c.batch, c.batch}) {
         for (auto& sh : shapes) {
             if (sh[0] <= 0 || sh[1] <= 0) continue;
             const dfk::GemvPlan pl = dfk::plan_gemv(c.dtype, sh[0], sh[1], M, 2 * c.batch);
             const size_t need = pl.part_floats > 0 ? pl.part_floats : (size_t)M * sh[0];
             if (need > *part_floats) *part_floats = need;
-            if ((size_t)pl.nblocks > *blocks) *blocks = pl.nblocks;
         }
     }
 }
@@ -65,10 +63,9 @@ WsLayout layout(const df_config& c) {
     L.gates = take(P * 2 * 4);
     L.grows = take(P * 2 * (size_t)c.expert_ffn * 4);
     L.yrows = take(P * 2 * (size_t)c.d_model * 4);
-    size_t gp = 0, gb = 0;
-    gemv_scratch(c, &gp, &gb);
+    size_t gp = 0;
+    gemv_scratch(c, &gp);
     L.gpart = take(gp * 4);
-    L.gcount = take(gb * 4);
     L.stats = take(M * dfk::stat_segs(c.d_model) * 2 * 4);
     L.total = o;
     return L;

@@ -146,7 +146,7 @@ struct GemvPlan {
     int MT;               // 16-row activation tiles (0: shape not supported)
     int variant;          // kernel shape
     int ks, S;            // k-slice width and count
-    int grid, nblocks;    // workgroups; row groups per slice
+    int grid;             // workgroups
     size_t lds, part_floats;   // dynamic LDS bytes; partial-sum floats
 };
 // M: stacked rows in use; M_slices (>= M, else taken as M): the row count whose

@@ -794,7 +794,6 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
         pl.S = K / pl.ks;
         const int ngrp = std::min(std::max(1, kCUs / pl.S), NT16);
         pl.grid = ngrp * pl.S;
-        pl.nblocks = ngrp;
         pl.part_floats = (size_t)pl.S * M * N;
         return pl;
     }
@@ -815,7 +814,6 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
     int ngrp = std::max(1, kCUs * wg_per_cu / pl.S);
     ngrp = std::min(ngrp, n_tiles);
     pl.grid = ngrp * pl.S;
-    pl.nblocks = ngrp;
     pl.part_floats = (size_t)pl.S * M * N;   // used when S > 1 or before a residual + norm
     return pl;
 }
