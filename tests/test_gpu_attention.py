@@ -63,6 +63,14 @@ def test_no_coupling_vector():
     _run(_abi.DF_BF16, 2, 2, 128, 300, [300, 37], seed=32, with_a=False)
 
 
+def test_long_context():
+    """Contexts far beyond the workloads': 131,072 keys and a ragged 77,777, so
+    the flattened key offsets, each wave's key range (about 800 keys here,
+    in one or two segments) and the slot staircase run at large indices;
+    every (sequence, head) against the oracle."""
+    _run(_abi.DF_BF16, 2, 4, 128, 131072, [131072, 77777], seed=33)
+
+
 def test_full_attention_workload_sampled():
     c = C2_ATTN
     src = AttnInputs(c)

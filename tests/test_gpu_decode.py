@@ -29,6 +29,10 @@ SMALL_BF16_S3 = Config("gpu_small_bf16_s3", L=2, d=768, H=6, Dh=128, F=1536, V=5
 # one round of loads (8), so they take a second round
 BF16_S9 = Config("gpu_bf16_s9_b36", L=1, d=2304, H=18, Dh=128, F=9216, V=512, B=36, ctx=40, S_max=64,
                  dtype="bf16", seed=25, sigma_w=0.02, sigma_ln=0.1)
+# a context of 65,536 positions: the fused attention pass (Q/K/V slice sums,
+# the new key at the end of a long segment) at large key indices
+LONG_CTX = Config("gpu_long_ctx", L=2, d=256, H=2, Dh=128, F=1024, V=512, B=3, ctx=65536, S_max=65544,
+                  dtype="bf16", seed=26, sigma_w=0.05, sigma_ln=0.1)
 SMALL_F32 = Config("gpu_small_f32", L=2, d=128, H=2, Dh=64, F=256, V=300, B=2, ctx=40, S_max=64,
                    dtype="f32", seed=22, sigma_w=0.05, sigma_ln=0.1)
 SMALL_MOE = Config("gpu_small_moe", L=2, d=256, H=2, Dh=128, F=0, V=512, B=8, ctx=40, S_max=64, dtype="bf16",
@@ -85,6 +89,31 @@ def test_small_dense_steps(cfg):
     src = Inputs(cfg)
     m = odf.Model(src)
     cache = odf.Cache(cfg, list(range(cfg.B)), src)
+    s = _sentinel(gm, cfg)
+    for step in range(2):
+        lens0 = gm.len.cpu().numpy().copy()
+        tok = src.step_tokens(step)
+        gm.decode_step(gm.tokens(tok))
+        torch.cuda.synchronize()
+        r = odf.decode_step(m, cache, tok, aux_on=True)
+        say(f" step {step}")
+        _compare_step(cfg, gm, r)
+        if step == 0:
+            _check_writes(gm, cfg, lens0, cache, s)
+    assert np.array_equal(gm.len.cpu().numpy(), cache.lens)
+    assert gm.status() == 0
+
+
+def test_long_context_steps():
+    """Two dual steps of a small model at a 65,536-position context (the
+    prefilled cache from the device generator), against the oracle on every
+    sequence, with the appended K/V checked at position len."""
+    cfg = LONG_CTX
+    say(f"decode case {cfg.name}")
+    gm = DecodeModel(cfg, fill="device")
+    src = Inputs(cfg)
+    m = odf.Model(src)
+    cache = odf.Cache(cfg, list(range(cfg.B)), src, lazy=True)
     s = _sentinel(gm, cfg)
     for step in range(2):
         lens0 = gm.len.cpu().numpy().copy()
