@@ -147,6 +147,7 @@ struct GemvPlan {
     int variant;          // kernel shape
     int ks, S;            // k-slice width and count
     int grid;             // workgroups
+    int halves;           // 2: rows 0-63 and 64-127 in two workgroups per (row tiles, k-slice)
     size_t lds, part_floats;   // dynamic LDS bytes; partial-sum floats
 };
 // M: stacked rows in use; M_slices (>= M, else taken as M): the row count whose

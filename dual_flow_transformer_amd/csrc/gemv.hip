@@ -20,6 +20,7 @@
 // row-major): one wave per weight row, lanes split K, wave reduction, same
 // epilogues.
 #include <algorithm>
+#include <numeric>
 
 #include "df_device.h"
 #include "df_internal.h"
@@ -57,6 +58,7 @@ struct GParams {
     const float* x_stats; // activation rows normalised on the fly (see GemvArgs)
     const float* x_gain;
     float eps;
+    int halves;           // 2: the stacked rows are split over two workgroups of 64 (see gemv_bf16)
 };
 
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
@@ -115,7 +117,8 @@ typedef tile::bf16x8 bf16x8;
 // wave's 16 weight rows x 16 stacked rows (per m tile). With both flows, the
 // aux row 2b+1 sits in the neighbouring lane of the primary row 2b.
 template <int MT>
-__device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&acc)[MT], int n_base, int lane) {
+__device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&acc)[MT], int n_base, int lane,
+                                              int m0) {
     const int li = lane & 15, lg = lane >> 4;
     const bool dual = p.nflows == 2;
     #pragma unroll
@@ -125,7 +128,7 @@ __device__ __forceinline__ void epilogue_regs(const GParams& p, const f32x4 (&ac
             const float v = acc[mt][r];
             const float partner = __shfl_xor(v, 1, 64);
             const int n = n_base + 4 * lg + r;
-            const int m = mt * 16 + li;
+            const int m = m0 + mt * 16 + li;
             if (n >= p.N || m >= p.M) continue;
             if (dual) {
                 if ((m & 1) == 0) epilogue<bf16_t>(p, n, m >> 1, v, partner);
@@ -164,7 +167,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int S = p.S;
-    const int s = blockIdx.x % S, grp = blockIdx.x / S, ngrp = gridDim.x / S;
+    // With two row halves, workgroups b and b + 8 (dispatched together, on
+    // the same XCD) take rows 0-63 and 64-127 of the same row tiles and
+    // k-slice, so the second reads the weights from L2.
+    const int item = p.halves == 2 ? (int)(((blockIdx.x >> 4) << 3) | (blockIdx.x & 7)) : (int)blockIdx.x;
+    const int m0 = p.halves == 2 ? (int)((blockIdx.x >> 3) & 1) * 16 * MT : 0;
+    const int s = item % S, grp = item / S, ngrp = gridDim.x / p.halves / S;
     const int n_tiles = (p.N + TR - 1) / TR;
     const int t_lo = (int)((long)grp * n_tiles / ngrp), t_hi = (int)((long)(grp + 1) * n_tiles / ngrp);
     const int my_tiles = t_hi - t_lo > wv ? (t_hi - t_lo - wv + NW - 1) / NW : 0;
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
         #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int e = threadIdx.x + u * NW * 64;
-            const int m = min(e >> 4, p.M - 1), j = min(e & 15, nseg - 1);
+            const int m = min(m0 + (e >> 4), p.M - 1), j = min(e & 15, nseg - 1);
             sv[u] = *reinterpret_cast<const float2*>(p.x_stats + ((size_t)(m * p.row_step) * nseg + j) * 2);
         }
     }
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
     for (int u = 0; u < XB; ++u) {
         const int i = min((int)threadIdx.x + u * NW * 64, NI - 1);
         const int m = i / C4, c = i - m * C4;
-        xv[u] = *reinterpret_cast<const float4*>(X + (size_t)(min(m, p.M - 1) * p.row_step) * p.K + ks0 + c * 4);
+        xv[u] = *reinterpret_cast<const float4*>(X + (size_t)(min(m0 + m, p.M - 1) * p.row_step) * p.K + ks0 + c * 4);
     }
     static_assert(NBUF == 2 || NBUF == 3, "fragment buffers");
     u32x4 a0[RT][KU], a1[RT][KU], a2[NBUF == 3 ? RT : 1][NBUF == 3 ? KU : 1];
@@ -306,12 +314,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16(GParams p) {
                 if (S > 1 || p.epi == EPI_RESID || p.epi == EPI_PART) {
                     #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const int m = mt * 16 + li, n0 = nb + 4 * lg;
+                        const int m = m0 + mt * 16 + li, n0 = nb + 4 * lg;
                         if (n0 < p.N && m < p.M)
                             *reinterpret_cast<f32x4*>(p.part + ((size_t)s * p.M + m) * p.N + n0) = acc[rt][mt];
                     }
                 } else {
-                    epilogue_regs<MT>(p, acc[rt], nb, lane);
+                    epilogue_regs<MT>(p, acc[rt], nb, lane, m0);
                 }
                 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -776,6 +784,7 @@ int mt_for(int M) {
 
 GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
     GemvPlan pl{};
+    pl.halves = 1;
     if (M_slices < M) M_slices = M;
     if (dtype != DF_BF16 || M < 1 || M_slices > 128 || N < 16 || N % 16 || K < 256 || K % 256) return pl;
     pl.MT = mt_for(M);
@@ -797,10 +806,20 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
         pl.part_floats = (size_t)pl.S * M * N;
         return pl;
     }
-    pl.variant = variant_for(pl.MT, N, K);
     // the k-slice width of the M_slices-row plan (the kernel shape may differ:
     // the k order within a slice is the same in both)
-    const int ks = ks_for(variant_for(mt_s, N, K), mt_s, N, K);
+    int ks = ks_for(variant_for(mt_s, N, K), mt_s, N, K);
+    if (mt_s == 8 && K % 512 == 0) {
+        // 65-128 planned rows: 512-wide slices, the rows split into two
+        // workgroups of 64 (a 128-row tile would leave LDS for 256 columns
+        // only, and the split-K partials grow with the slice count)
+        ks = 512;
+        if (pl.MT == 8) {
+            pl.MT = 4;
+            pl.halves = 2;
+        }
+    }
+    pl.variant = variant_for(pl.MT, N, K);
     if (!ks_supported(pl.variant, pl.MT, ks)) return GemvPlan{};
     pl.ks = ks;
     pl.S = K / ks;
@@ -811,9 +830,15 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
     const int wg_per_cu = pl.variant == VAR_A && pl.lds + lds_static <= 80 * 1024 ? 2 : 1;
     const int rt = pl.variant == VAR_B ? 2 : 1;
     const int n_tiles = (N + 16 * rt - 1) / (16 * rt);
-    int ngrp = std::max(1, kCUs * wg_per_cu / pl.S);
+    int ngrp = std::max(1, kCUs * wg_per_cu / (pl.S * pl.halves));
     ngrp = std::min(ngrp, n_tiles);
-    pl.grid = ngrp * pl.S;
+    if (pl.halves == 2) {
+        // the pairing of workgroups b and b + 8 needs ngrp * S % 8 == 0
+        // (groups past the last row tile have no tiles and exit)
+        const int g = 8 / std::gcd(pl.S, 8);
+        ngrp = std::max(g, ngrp / g * g);
+    }
+    pl.grid = ngrp * pl.S * pl.halves;
     pl.part_floats = (size_t)pl.S * M * N;   // used when S > 1 or before a residual + norm
     return pl;
 }
@@ -840,6 +865,7 @@ hipError_t gemv(const GemvArgs& a, hipStream_t s) {
     const GemvPlan pl = plan_gemv(a.dtype, a.N, a.K, p.M, a.slice_rows);
     if (pl.MT == 0) return hipErrorInvalidValue;
     p.S = pl.S;
+    p.halves = pl.halves;
     if ((pl.S > 1 || a.epi == EPI_RESID || a.epi == EPI_PART) && !a.part) return hipErrorInvalidValue;
     if (a.epi == EPI_RESID && a.N > 4096) return hipErrorInvalidValue;
     if (a.x_stats && (!a.x_gain || a.K > kMaxSeg * kStatSeg)) return hipErrorInvalidValue;
