@@ -681,8 +681,9 @@ __global__ __launch_bounds__(256) void gemv_f32(GParams p) {
     }
 }
 
-// Kernel shapes: A = 16-row tiles, 8 waves, batches of 8 fragments (4 with 64
-// stacked rows, 2 with 128), two batches ahead (one with 128 rows);
+// Kernel shapes: A = 16-row tiles, 8 waves (12 with 64 stacked rows), batches
+// of 8 fragments (4 with 64 stacked rows, 2 with 128), two batches ahead (one
+// with 128 rows);
 // B = 32-row tiles, 4 waves, batches of 4 fragments per tile, one batch ahead
 // (up to 32 stacked rows, for matrices with fewer than 8192 rows or at most
 // 16 M weights; plan_gemv holds the choice).
@@ -726,9 +727,13 @@ hipError_t launch_mt(GParams& p, const GemvPlan& pl, hipStream_t s) {
     constexpr int NB = MT >= 8 ? 2 : 3;
     if constexpr (MT <= 2) {
         if (pl.ks == 1024) return launch_one<MT, 1, KU, 8, 1024, NB>(p, pl, s);
-    }
-    if constexpr (MT <= 4) {
         if (pl.ks == 512) return launch_one<MT, 1, KU, 8, 512, NB>(p, pl, s);
+    }
+    if constexpr (MT == 4) {
+        // 12 waves (three per SIMD; 163 VGPRs): the MoE step's Q/K/V gives
+        // each workgroup 12 row tiles, one per wave instead of two on half
+        // of eight waves
+        if (pl.ks == 512) return launch_one<MT, 1, KU, 12, 512, NB>(p, pl, s);
     }
     if (pl.ks == 256) return launch_one<MT, 1, KU, 8, 256, NB>(p, pl, s);
     return hipErrorInvalidValue;

@@ -334,38 +334,74 @@ __global__ __launch_bounds__(1024) void moe_expert(ExpParams p) {
 // One workgroup per sequence: both flows' gate-weighted sums over their
 // ranks (rank order), the c coupling, the residual add; then, with g_next,
 // the LayerNorm of the updated rows into x_next (the next projection's
-// input), the rows being at hand.
-constexpr int kCombThreads = 1024;
-constexpr int kCombCols = 4;   // d <= kCombThreads * kCombCols
-__global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows, const float* gates, const float* cpl_c, int d, int k, int ka, int kr, int kk,
-                                                            int nflows, float* h, const float* g_next, float eps,
-                                                            float* x_next) {
-    __shared__ int s_slot[kMaxK];
-    __shared__ float s_g[2][kMaxK];
-    __shared__ float red[16];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const bool dual = nflows == 2;
-    if (tid < kk) s_slot[tid] = b * kk + tid;
-    if (tid < kr) {
-        s_g[0][tid] = gates[((size_t)b * 2) * kr + tid];
-        s_g[1][tid] = dual ? gates[((size_t)b * 2 + 1) * kr + tid] : 0.f;
-    }
+// input), the rows being at hand. Every global load of a thread (the gates
+// in lanes 0..kr-1 of each wave, the expert outputs of four ranks, the
+// residual rows, coupling and gains) is issued before the first use, so the
+// kernel waits on one memory round trip, not a chain of them.
+constexpr int kCombMaxThreads = 1024;
+constexpr int kCombCols = 4;   // d <= kCombMaxThreads * kCombCols
+
+// Threads of the combine for width d: kCombCols columns each, whole waves.
+inline int comb_threads(int d) {
+    const int t = (d + kCombCols - 1) / kCombCols;
+    return std::min(kCombMaxThreads, std::max(64, (t + 63) / 64 * 64));
+}
+
+// Block-wide sums of two values with one pair of barriers (each as
+// df::block_sum adds it: the wave's lanes, then the waves in order).
+__device__ __forceinline__ float2 block_sum2(float a, float c, float2* red /* >= 16 */) {
+    a = df::wave_sum(a);
+    c = df::wave_sum(c);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
     __syncthreads();
-    // gate-weighted sums: the expert outputs of four ranks at a time (every
-    // column of the thread, both flows) are loaded together; each sum still
-    // adds its ranks in rank order
+    if ((threadIdx.x & 63) == 0) red[w] = make_float2(a, c);
+    __syncthreads();
+    float2 t = make_float2(0.f, 0.f);
+    for (int i = 0; i < nw; ++i) {
+        t.x += red[i].x;
+        t.y += red[i].y;
+    }
+    return t;
+}
+
+__device__ __forceinline__ float lane_value(float v, int j) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
+__global__ __launch_bounds__(kCombMaxThreads) void moe_combine(const float* y_rows, const float* gates, const float* cpl_c, int d, int k, int ka, int kr, int kk,
+                                                               int nflows, float* h, const float* g_next, float eps,
+                                                               float* x_next) {
+    __shared__ float2 red[16];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, nt = blockDim.x;
+    const bool dual = nflows == 2;
+    const int nj = dual ? max(k, ka) : k;
+    // gates of rank `lane` of both flows
+    const float gl1 = lane < kr ? gates[((size_t)b * 2) * kr + lane] : 0.f;
+    const float gl2 = (dual && lane < kr) ? gates[((size_t)b * 2 + 1) * kr + lane] : 0.f;
+    // residual rows, coupling and gains of every column
+    float h1v[kCombCols], h2v[kCombCols], cv[kCombCols], gv[kCombCols];
+    #pragma unroll
+    for (int c = 0; c < kCombCols; ++c) {
+        const int n = min(tid + nt * c, d - 1);
+        h1v[c] = h[(size_t)(2 * b) * d + n];
+        h2v[c] = dual ? h[(size_t)(2 * b + 1) * d + n] : 0.f;
+        cv[c] = (dual && cpl_c) ? cpl_c[n] : 0.f;
+        gv[c] = x_next ? g_next[n] : 0.f;
+    }
+    // gate-weighted sums, the expert outputs of four ranks at a time (every
+    // column of the thread, both flows; pair t = b kk + j holds rows 2 t + f);
+    // each sum adds its ranks in rank order
     float y1[kCombCols], y2[kCombCols];
     #pragma unroll
     for (int c = 0; c < kCombCols; ++c) y1[c] = y2[c] = 0.f;
-    const int nj = dual ? max(k, ka) : k;
     for (int j0 = 0; j0 < nj; j0 += 4) {
         float t1[4][kCombCols], t2[4][kCombCols];
         #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const size_t r = (size_t)s_slot[min(j0 + u, nj - 1)] * 2 * d;
+            const size_t r = ((size_t)b * kk + min(j0 + u, nj - 1)) * 2 * d;
             #pragma unroll
             for (int c = 0; c < kCombCols; ++c) {
-                const int n = min(tid + kCombThreads * c, d - 1);
+                const int n = min(tid + nt * c, d - 1);
                 t1[u][c] = y_rows[r + n];
                 t2[u][c] = dual ? y_rows[r + d + n] : 0.f;
             }
@@ -373,28 +409,19 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows,
         #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = j0 + u;
+            const float g1 = lane_value(gl1, min(j, 63)), g2 = lane_value(gl2, min(j, 63));
             #pragma unroll
             for (int c = 0; c < kCombCols; ++c) {
-                if (j < k) y1[c] = fmaf(s_g[0][j], t1[u][c], y1[c]);
-                if (dual && j < ka) y2[c] = fmaf(s_g[1][j], t2[u][c], y2[c]);
+                if (j < k) y1[c] = fmaf(g1, t1[u][c], y1[c]);
+                if (dual && j < ka) y2[c] = fmaf(g2, t2[u][c], y2[c]);
             }
         }
-    }
-    // residual rows, coupling and gains of every column, loaded together
-    float h1v[kCombCols], h2v[kCombCols], cv[kCombCols], gv[kCombCols];
-    #pragma unroll
-    for (int c = 0; c < kCombCols; ++c) {
-        const int n = min(tid + kCombThreads * c, d - 1);
-        h1v[c] = h[(size_t)(2 * b) * d + n];
-        h2v[c] = dual ? h[(size_t)(2 * b + 1) * d + n] : 0.f;
-        cv[c] = (dual && cpl_c) ? cpl_c[n] : 0.f;
-        gv[c] = x_next ? g_next[n] : 0.f;
     }
     float v1[kCombCols], v2[kCombCols];
     float s1 = 0.f, s2 = 0.f;
     #pragma unroll
     for (int c = 0; c < kCombCols; ++c) {
-        const int n = tid + kCombThreads * c;
+        const int n = tid + nt * c;
         v1[c] = v2[c] = 0.f;
         if (n >= d) continue;
         float* h1 = h + (size_t)(2 * b) * d + n;
@@ -410,20 +437,22 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine(const float* y_rows,
         }
     }
     if (!x_next) return;
-    const float mean1 = df::block_sum(s1, red) / (float)d;
-    const float mean2 = dual ? df::block_sum(s2, red) / (float)d : 0.f;
+    const float2 sm = block_sum2(s1, s2, red);
+    const float mean1 = sm.x / (float)d;
+    const float mean2 = dual ? sm.y / (float)d : 0.f;
     float q1 = 0.f, q2 = 0.f;
     #pragma unroll
     for (int c = 0; c < kCombCols; ++c) {
-        if (tid + kCombThreads * c >= d) continue;
+        if (tid + nt * c >= d) continue;
         q1 = fmaf(v1[c] - mean1, v1[c] - mean1, q1);
         q2 = fmaf(v2[c] - mean2, v2[c] - mean2, q2);
     }
-    const float rstd1 = 1.0f / sqrtf(df::block_sum(q1, red) / (float)d + eps);
-    const float rstd2 = dual ? 1.0f / sqrtf(df::block_sum(q2, red) / (float)d + eps) : 0.f;
+    const float2 sq = block_sum2(q1, q2, red);
+    const float rstd1 = 1.0f / sqrtf(sq.x / (float)d + eps);
+    const float rstd2 = dual ? 1.0f / sqrtf(sq.y / (float)d + eps) : 0.f;
     #pragma unroll
     for (int c = 0; c < kCombCols; ++c) {
-        const int n = tid + kCombThreads * c;
+        const int n = tid + nt * c;
         if (n >= d) continue;
         x_next[(size_t)(2 * b) * d + n] = (v1[c] - mean1) * rstd1 * gv[c];
         if (dual) x_next[(size_t)(2 * b + 1) * d + n] = (v2[c] - mean2) * rstd2 * gv[c];
@@ -449,7 +478,7 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     const int ka = a.ka > 0 ? a.ka : a.k;
     const int kr = std::max(a.k, ka), kk = a.nflows == 2 ? kr : a.k;
     if (kr > kMaxK || a.k < 1 || a.B < 1 || a.B > kMaxPairs || a.E < 16 || a.E % 16 || a.E > 64 * kPerLane ||
-        a.d < 32 || a.d % 32 || a.d > kMaxSeg * kStatSeg || a.d > kCombThreads * kCombCols || a.dtype != DF_BF16 ||
+        a.d < 32 || a.d % 32 || a.d > kMaxSeg * kStatSeg || a.d > kCombMaxThreads * kCombCols || a.dtype != DF_BF16 ||
         (a.nflows != 1 && a.nflows != 2))
         return hipErrorInvalidValue;
     GateParams gp;
@@ -479,7 +508,7 @@ hipError_t moe(const MoeArgs& a, hipStream_t s) {
     dn.N = a.d; dn.K = a.Fe; dn.g_out = nullptr; dn.y_out = a.y_rows; dn.up = false;
     e = launch_expert<2>(dn, a.E, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(kCombThreads), 0, s, a.y_rows, a.gates, a.cpl_c, a.d, a.k,
+    hipLaunchKernelGGL(moe_combine, dim3(a.B), dim3(comb_threads(a.d)), 0, s, a.y_rows, a.gates, a.cpl_c, a.d, a.k,
                        ka, kr, kk, a.nflows, a.h, a.g_next, a.eps, a.x_next);
     return hipGetLastError();
 }
