@@ -64,6 +64,41 @@ constexpr int kGateThreads = 1024;
 constexpr int kGateWaves = kGateThreads / 64;
 constexpr int kGateFrags = 16;   // weight fragments per lane in flight
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+// (v, i) := the better of (v, i) and (ov, oi): larger value, then lower index.
+__device__ __forceinline__ void take_best(float& v, int& i, float ov, int oi) {
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Wave-wide best (largest value, then lowest index); every lane ends with
+// it. A total order, so the reduction tree does not change the result:
+// quad, half-row and row exchanges by DPP, then two cross-row shuffles.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+    take_best(v, i, df::dpp<df::kQuadSwap1>(v), dpp_i<df::kQuadSwap1>(i));
+    take_best(v, i, df::dpp<df::kQuadSwap2>(v), dpp_i<df::kQuadSwap2>(i));
+    take_best(v, i, df::dpp<df::kRowHalfMirror>(v), dpp_i<df::kRowHalfMirror>(i));
+    take_best(v, i, df::dpp<df::kRowMirror>(v), dpp_i<df::kRowMirror>(i));
+    take_best(v, i, __shfl_xor(v, 16, 64), __shfl_xor(i, 16, 64));
+    take_best(v, i, __shfl_xor(v, 32, 64), __shfl_xor(i, 32, 64));
+}
+
+// Wave-wide maximum, every lane ending with it.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = fmaxf(x, df::dpp<df::kQuadSwap1>(x));
+    x = fmaxf(x, df::dpp<df::kQuadSwap2>(x));
+    x = fmaxf(x, df::dpp<df::kRowHalfMirror>(x));
+    x = fmaxf(x, df::dpp<df::kRowMirror>(x));
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
 template <int NPL>   // logits per lane: E <= 64 NPL
 __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
     extern __shared__ float s_x[];   // [2][d] normalised rows, then [2][E / 16][ns][16] logit parts
@@ -87,9 +122,9 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
     {
         // residual values of both rows (one float4 per thread and row:
         // d <= 4 * kGateThreads) and the gains, in flight while wave 0 forms
-        // the row norms: lane 16 f + i loads segment i of row f, and the
-        // segments are added in order through shuffles (the arithmetic of
-        // row_norm_from_segments, without its chain of dependent loads)
+        // the row norms: lane 16 f + i loads segment i of row f, and each
+        // 16-lane group combines its segments' (mean, M2) (Chan), as the
+        // projections' on-the-fly LayerNorm does
         __shared__ float2 s_mr[2];
         const int k = min(tid * 4, d - 4);
         float4 hv[2];
@@ -101,19 +136,12 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
             const int f = (lane >> 4) & 1, i = lane & 15;
             const float2 sv = reinterpret_cast<const float2*>(p.stats)[(size_t)(2 * b + (dual ? f : 0)) * nseg +
                                                                         min(i, nseg - 1)];
-            #pragma unroll
-            for (int ff = 0; ff < 2; ++ff) {
-                float mean = 0.f;
-                for (int j = 0; j < nseg; ++j)
-                    mean += (float)min(kStatSeg, d - j * kStatSeg) * __shfl(sv.x, 16 * ff + j, 64);
-                mean /= (float)d;
-                float m2 = 0.f;
-                for (int j = 0; j < nseg; ++j) {
-                    const float dm = __shfl(sv.x, 16 * ff + j, 64) - mean;
-                    m2 += __shfl(sv.y, 16 * ff + j, 64) + (float)min(kStatSeg, d - j * kStatSeg) * dm * dm;
-                }
-                if (lane == 0) s_mr[ff] = make_float2(mean, 1.0f / sqrtf(m2 / (float)d + p.eps));
-            }
+            const bool valid = i < nseg;
+            const float cnt = valid ? (float)min(kStatSeg, d - i * kStatSeg) : 0.f;
+            const float mean = df::group_sum<16>(cnt * sv.x) / (float)d;
+            const float dm = sv.x - mean;
+            const float m2 = df::group_sum<16>(valid ? fmaf(cnt * dm, dm, sv.y) : 0.f);
+            if (lane < 32 && i == 0) s_mr[f] = make_float2(mean, 1.0f / sqrtf(m2 / (float)d + p.eps));
         }
         __syncthreads();
         #pragma unroll
@@ -198,18 +226,14 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
                 bi = e;
             }
         }
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
+        wave_best(bv, bi);
         if (lane == j) { my_val = bv; my_sel = bi; }
         if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     }
     // gates: softmax over each flow's ranks (lanes = ranks), zero beyond its fan-out
     const float top = __shfl(my_val, 0, 64);   // rank 0 holds the largest logit
     const float e1 = lane < p.k ? expf(my_val - top) : 0.f;
-    const float s1 = df::wave_sum(e1);
+    const float s1 = df::group_sum<64>(e1);
     if (lane < p.kr) {
         p.gates[((size_t)b * 2) * p.kr + lane] = lane < p.k ? e1 / s1 : 0.f;
         p.ids[(size_t)b * p.kr + lane] = my_sel;
@@ -218,9 +242,9 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
     if (dual) {
         // the aux router's logit of rank `lane`'s expert
         const float l2 = lane < p.ka ? s_r[E + my_sel] : -INFINITY;
-        const float m2 = df::wave_max(l2);
+        const float m2 = wave_max_dpp(l2);
         const float e2 = lane < p.ka ? expf(l2 - m2) : 0.f;
-        const float s2 = df::wave_sum(e2);
+        const float s2 = df::group_sum<64>(e2);
         if (lane < p.kr) p.gates[((size_t)b * 2 + 1) * p.kr + lane] = lane < p.ka ? e2 / s2 : 0.f;
     }
 }
