@@ -72,13 +72,16 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
+// Wave-wide sum and maximum, every lane ending with the same value: exchanges
+// within rows of 16 lanes by DPP, then two cross-row shuffles.
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 __device__ __forceinline__ float wave_max(float x) {
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+    x = fmaxf(x, dpp<kQuadSwap1>(x));
+    x = fmaxf(x, dpp<kQuadSwap2>(x));
+    x = fmaxf(x, dpp<kRowHalfMirror>(x));
+    x = fmaxf(x, dpp<kRowMirror>(x));
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
 }
 
 // Block-wide sum (blockDim.x a multiple of 64, <= 1024); result to all threads.

@@ -89,16 +89,6 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
     take_best(v, i, __shfl_xor(v, 32, 64), __shfl_xor(i, 32, 64));
 }
 
-// Wave-wide maximum, every lane ending with it.
-__device__ __forceinline__ float wave_max_dpp(float x) {
-    x = fmaxf(x, df::dpp<df::kQuadSwap1>(x));
-    x = fmaxf(x, df::dpp<df::kQuadSwap2>(x));
-    x = fmaxf(x, df::dpp<df::kRowHalfMirror>(x));
-    x = fmaxf(x, df::dpp<df::kRowMirror>(x));
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    return fmaxf(x, __shfl_xor(x, 32, 64));
-}
-
 template <int NPL>   // logits per lane: E <= 64 NPL
 __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
     extern __shared__ float s_x[];   // [2][d] normalised rows, then [2][E / 16][ns][16] logit parts
@@ -233,7 +223,7 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
     // gates: softmax over each flow's ranks (lanes = ranks), zero beyond its fan-out
     const float top = __shfl(my_val, 0, 64);   // rank 0 holds the largest logit
     const float e1 = lane < p.k ? expf(my_val - top) : 0.f;
-    const float s1 = df::group_sum<64>(e1);
+    const float s1 = df::wave_sum(e1);
     if (lane < p.kr) {
         p.gates[((size_t)b * 2) * p.kr + lane] = lane < p.k ? e1 / s1 : 0.f;
         p.ids[(size_t)b * p.kr + lane] = my_sel;
@@ -242,9 +232,9 @@ __global__ __launch_bounds__(kGateThreads) void moe_gate(GateParams p) {
     if (dual) {
         // the aux router's logit of rank `lane`'s expert
         const float l2 = lane < p.ka ? s_r[E + my_sel] : -INFINITY;
-        const float m2 = wave_max_dpp(l2);
+        const float m2 = df::wave_max(l2);
         const float e2 = lane < p.ka ? expf(l2 - m2) : 0.f;
-        const float s2 = df::group_sum<64>(e2);
+        const float s2 = df::wave_sum(e2);
         if (lane < p.kr) p.gates[((size_t)b * 2 + 1) * p.kr + lane] = lane < p.ka ? e2 / s2 : 0.f;
     }
 }
