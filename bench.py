@@ -35,14 +35,14 @@ TIMING_STRIDE = 7
 # (x2.0 fetch, x1.0 write). Reported only while the kernel sources are the ones they were
 # measured on (attention pass: attention.hip; step traffic: every library source).
 COUNTER_SOURCES = {"attention_source_sha256": "f92b9ef8bfee3b3aa837ace3c52fadd3416d1a81741a722506eb049e9aeb04e0",
-                   "library_sources_sha256": "a3ad83b0ff79bc51faaa651b5ed0676069fdf59caf8143d890a77eea5fcaaa43"}
+                   "library_sources_sha256": "f157883b12fd28ed633de4ff900aa4f54a339569aceea22857ba94b3109d3ade"}
 COUNTERS = {
     "dense_32l_d4096_b16_ctx8192": {"attention_traffic_bytes_per_launch": 2.15450e+09,
-                   "step_traffic_bytes": {"dual": 8.40720e+10, "primary_only": 8.30310e+10}},
+                   "step_traffic_bytes": {"dual": 8.40720e+10, "primary_only": 8.30300e+10}},
     "dense_1p3b_b16_ctx2048": {"attention_traffic_bytes_per_launch": 2.73400e+08,
-                   "step_traffic_bytes": {"dual": 9.89300e+09, "primary_only": 9.47100e+09}},
+                   "step_traffic_bytes": {"dual": 9.89300e+09, "primary_only": 9.47000e+09}},
     "moe_16l_e64_top4_b64_ctx1024": {"attention_traffic_bytes_per_launch": 5.47600e+08,
-                   "step_traffic_bytes": {"dual": 1.92890e+10, "primary_only": 1.85690e+10}},
+                   "step_traffic_bytes": {"dual": 1.92990e+10, "primary_only": 1.85680e+10}},
 }
 
 
