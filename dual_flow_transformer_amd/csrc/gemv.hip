@@ -437,6 +437,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_r(GParams p) {
     constexpr int SPT = (16 * MT * 16 + NT - 1) / NT;
     extern __shared__ f32x4 red[];   // [2][NW][NP][64]
     __shared__ float s_mean[16 * MT], s_rstd[16 * MT];
+    __shared__ float4 s_gain[NW][KWB * 8];   // each wave's gains, loaded once
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int S = p.S;
@@ -449,17 +450,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_r(GParams p) {
     const float* X = reinterpret_cast<const float*>(p.x);
     const bool norm = p.x_stats != nullptr;
 
-    // loads first: row statistics, gains, activations, then two weight batches
+    // loads first: row statistics, the wave's gains (one float4 per lane
+    // for the first KWB * 8 lanes; every lane group needs them, so they go
+    // through LDS rather than being loaded 16 times), activations, then two
+    // weight batches
     RowStats<SPT, NT> st;
     if (norm) st.load(p, 16 * MT);
+    float4 g_own = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (norm && lane < KWB * 8) g_own = *reinterpret_cast<const float4*>(p.x_gain + kb0 * 32 + 4 * lane);
     float4 gv[KWB][2], xv[MT][KWB][2];
     #pragma unroll
     for (int kb = 0; kb < KWB; ++kb) {
         const int k = (kb0 + kb) * 32 + lg * 8;
-        if (norm) {
-            gv[kb][0] = *reinterpret_cast<const float4*>(p.x_gain + k);
-            gv[kb][1] = *reinterpret_cast<const float4*>(p.x_gain + k + 4);
-        }
         #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = min(mt * 16 + li, p.M - 1);
@@ -485,8 +487,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_r(GParams p) {
     load(0, a0);
     load(1, a1);
     if (norm) {
+        if (lane < KWB * 8) s_gain[wv][lane] = g_own;
         st.reduce(p, 16 * MT, s_mean, s_rstd);
         __syncthreads();
+        #pragma unroll
+        for (int kb = 0; kb < KWB; ++kb) {
+            gv[kb][0] = s_gain[wv][kb * 8 + lg * 2];
+            gv[kb][1] = s_gain[wv][kb * 8 + lg * 2 + 1];
+        }
     }
     bf16x8 xh[MT][KWB], xl[MT][KWB];
     #pragma unroll
