@@ -549,10 +549,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_r(GParams p) {
 }
 
 // Sums of the S k-slice partials of logical rows m1 and m2 (m2 < 0: none),
-// column n, in slice order; the loads of sixteen slices (32 values) are in
+// column n, in slice order; the loads of SB slices (2 SB values) are in
 // flight together.
-__device__ __forceinline__ void sum_slices(const GParams& p, int S, int m1, int m2, int n, float& y1, float& y2) {
-    constexpr int SB = 16;
+template <int SB>
+__device__ __forceinline__ void sum_slices_sb(const GParams& p, int S, int m1, int m2, int n, float& y1, float& y2) {
     const float* q1 = p.part + (size_t)m1 * p.N + n;
     const float* q2 = p.part + (size_t)(m2 < 0 ? m1 : m2) * p.N + n;
     const size_t stride = (size_t)p.M * p.N;
@@ -574,6 +574,14 @@ __device__ __forceinline__ void sum_slices(const GParams& p, int S, int m1, int 
     }
     y1 = v1;
     y2 = m2 < 0 ? 0.f : v2;
+}
+
+// The batch is sized to S (uniform branch), so no load is spent on a clamped
+// slice when S <= 4 or 8; the sums are the same either way.
+__device__ __forceinline__ void sum_slices(const GParams& p, int S, int m1, int m2, int n, float& y1, float& y2) {
+    if (S <= 4) sum_slices_sb<4>(p, S, m1, m2, n, y1, y2);
+    else if (S <= 8) sum_slices_sb<8>(p, S, m1, m2, n, y1, y2);
+    else sum_slices_sb<16>(p, S, m1, m2, n, y1, y2);
 }
 
 // Split-K finish for the elementwise epilogues: thread per (sequence, column).
