@@ -181,15 +181,24 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
     }
     mx1 = df::block_max(mx1, red);
     if (aux_on) mx2 = df::block_max(mx2, red);
+    // exponentials, kept in place of the register-resident logits for the
+    // output pass (the memory path computes them again there)
+    auto E1 = [&](int j, int v) { return __builtin_amdgcn_exp2f((L1(j, v) - mx1) * df::kLog2e); };
+    auto E2 = [&](int j, int v) { return __builtin_amdgcn_exp2f((L2(j, v) - mx2) * df::kLog2e); };
     float s1 = 0.f, c1 = 0.f, s2 = 0.f;
     #pragma unroll
     for (int j = 0; j < nj; ++j) {
         const int v = threadIdx.x + 1024 * j;
         if (v >= V) break;
-        const float e1 = __builtin_amdgcn_exp2f((L1(j, v) - mx1) * df::kLog2e);
+        const float e1 = E1(j, v);
         s1 += e1;
         c1 = fmaf(e1, e1, c1);
-        if (aux_on) s2 += __builtin_amdgcn_exp2f((L2(j, v) - mx2) * df::kLog2e);
+        const float e2 = aux_on ? E2(j, v) : 0.f;
+        s2 += e2;
+        if constexpr (NPT > 0) {
+            x1[j] = e1;
+            x2[j] = e2;
+        }
     }
     s1 = df::block_sum(s1, red);
     c1 = df::block_sum(c1, red);
@@ -207,8 +216,14 @@ __global__ __launch_bounds__(1024) void mix_head_kernel(MixRows m, int V, int mo
     for (int j = 0; j < nj; ++j) {
         const int v = threadIdx.x + 1024 * j;
         if (v >= V) break;
-        float p = __builtin_amdgcn_exp2f((L1(j, v) - mx1) * df::kLog2e) * w1;
-        if (aux_on) p = fmaf(__builtin_amdgcn_exp2f((L2(j, v) - mx2) * df::kLog2e), w2, p);
+        float p;
+        if constexpr (NPT > 0) {
+            p = x1[j] * w1;
+            if (aux_on) p = fmaf(x2[j], w2, p);
+        } else {
+            p = E1(j, v) * w1;
+            if (aux_on) p = fmaf(E2(j, v), w2, p);
+        }
         out[v] = p;
         if (p > best) { best = p; besti = v; }
     }
