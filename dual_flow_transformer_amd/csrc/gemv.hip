@@ -14,7 +14,8 @@
 // partial sums are finished by a reduce kernel with one of the epilogues:
 // plain store, Q coupling + K/V append, GELU + b coupling, or c coupling +
 // residual add (then LayerNorm), or left for the next kernel (EPI_PART). For
-// matrices of 32M weights or more and up to 32 stacked rows, the activation
+// matrices of 32M weights or more (16M with 4096 rows and columns or more)
+// and up to 32 stacked rows, the activation
 // fragments sit in registers instead (shape R: the waves of a workgroup split
 // its k-slice and add their products through LDS). fp32 path (fp32 storage,
 // row-major): one wave per weight row, lanes split K, wave reduction, same
@@ -814,10 +815,13 @@ GemvPlan plan_gemv(int dtype, int N, int K, int M, int M_slices) {
     // whichever row count runs (a primary-only step gives bitwise the primary
     // results of a dual step). The register-resident shape where it measured
     // faster inside the decode step (per-kernel traces): up to 32 rows and
-    // matrices of 32M weights or more (1024-wide slices).
+    // matrices of 32M weights or more, or of 16M with at least 4096 rows and
+    // columns (1024-wide slices; the 1.3B model's 2048-row down projection
+    // measured slower in it).
     const int mt_s = mt_for(M_slices);
     const int NT16 = N / 16;
-    if (mt_s <= 2 && (long)N * K >= (32L << 20) && K % 1024 == 0) {
+    const long nk = (long)N * K;
+    if (mt_s <= 2 && (nk >= (32L << 20) || (nk >= (16L << 20) && N >= 4096 && K >= 4096)) && K % 1024 == 0) {
         pl.variant = VAR_R;
         pl.ks = 1024;
         pl.lds = (size_t)2 * 8 * 2 * pl.MT * 64 * 16;   // the waves' partial products, double-buffered
