@@ -6,10 +6,16 @@
 // Split-K flash decode with an even split of all keys over the waves of the
 // launch (one 4-wave workgroup per compute unit). The keys of the
 // (sequence, head) pairs are laid end to end (pair p = b*H + h holds n_b
-// keys); wave w of G takes the key range
-// [w*KT, (w+1)*KT), KT = ceil(total / G), which covers one segment of each
-// pair it overlaps, so every wave streams the same number of bytes whatever
-// the mix of context lengths. The partial result of (wave w, pair p) goes to
+// keys); wave w of G takes a contiguous key range of KE keys (waves of even
+// workgroups) or KO keys (odd workgroups), laid out in wave order, which
+// covers one segment of each pair it overlaps, so every wave streams the
+// same number of bytes whatever the mix of context lengths. KE = KO =
+// ceil(total / G) unless the waves average 2048 keys or more: workgroups are
+// dispatched round-robin over the eight XCDs, and in such long launches the
+// waves on the odd XCDs were measured (per-wave completion timestamps) to
+// finish ~6 % later than those on the even ones, so even-workgroup waves
+// take 3 % more keys and odd ones 3 % fewer. The split depends only on the
+// key counts, never on timing. The partial result of (wave w, pair p) goes to
 // slot w + p (unique: the overlaps form a staircase in (w, p)), and the
 // slots of a pair are consecutive. Each 16-byte load of a key row is shared
 // by both queries; LPP lanes hold one key row (Dh/LPP elements each), so a
@@ -35,7 +41,7 @@ struct PartParams {
     const int32_t* nkeys;
     float* part_o;     // [slots][2][Dh]
     float* part_ml;    // [slots][4]
-    long long* seq_tab; // [B + 1]: key offset of sequence b's first pair; [B]: keys per wave
+    long long* seq_tab; // [B + 2]: key offset of sequence b's first pair; [B], [B + 1]: KE, KO
     size_t seq_stride; // elements between sequences in the cache
     int B, H, S_max, nkeys_add, nflows;
     int waves;         // G: waves of the launch
@@ -124,6 +130,31 @@ __device__ __forceinline__ int keys_of(const int32_t* nkeys, int b, int add, int
     return n < 0 ? 0 : (n > S_max ? S_max : n);
 }
 
+// Keys per wave for a launch of G waves over `total` keys: KE for the four
+// waves of an even workgroup, KO for those of an odd one (equal below 2048
+// keys per wave). Both are rounded up, so the G ranges cover every key.
+constexpr int kLongWaveKeys = 2048;
+constexpr int kXcdSkewMilli = 30;
+__device__ __forceinline__ void wave_keys(long long total, int G, long long& KE, long long& KO) {
+    const long long g = (long long)G * 1000;
+    const int skew = total >= (long long)kLongWaveKeys * G ? kXcdSkewMilli : 0;
+    KE = max(1LL, (total * (1000 + skew) + g - 1) / g);
+    KO = max(1LL, (total * (1000 - skew) + g - 1) / g);
+}
+
+// First key of wave w: the waves of workgroup pairs (2i, 2i + 1) cover
+// 4 (KE + KO) keys in wave order.
+__device__ __forceinline__ long long wave_first_key(int w, long long KE, long long KO) {
+    const int r = w & 7;
+    return (long long)(w >> 3) * 4 * (KE + KO) + (r < 4 ? r * KE : 4 * KE + (r - 4) * KO);
+}
+
+// The wave whose key range holds `key`.
+__device__ __forceinline__ int wave_of_key(long long key, long long KE, long long KO) {
+    const long long P = 4 * (KE + KO), q = key / P, r = key - q * P;
+    return (int)(8 * q + (r < 4 * KE ? r / KE : 4 + (r - 4 * KE) / KO));
+}
+
 // FUSED: the queries (and the new key's K/V) come from the Q/K/V
 // projection's k-slice partial sums (p.qkv); otherwise from p.q.
 template <typename T, int DH, int U, bool FUSED>
@@ -147,10 +178,11 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     const long long my_off = incl - (long long)p.H * my_n;
     const long long total = __shfl(incl, 63, 64);
     const int G = p.waves;
-    const long long KT = total > G ? (total + G - 1) / G : 1;   // keys per wave
+    long long KE, KO;   // keys per wave of an even and of an odd workgroup
+    wave_keys(total, G, KE, KO);
     if (blockIdx.x == 0 && threadIdx.x < 64) {   // for the combine pass
         if (lane < p.B) p.seq_tab[lane] = my_off;
-        if (lane == 0) p.seq_tab[p.B] = KT;
+        if (lane == 0) { p.seq_tab[p.B] = KE; p.seq_tab[p.B + 1] = KO; }
         if (FUSED && p.status) {   // a new key outside the cache is not written
             const int pos = lane < p.B ? p.nkeys[lane] : 0;
             if (__ballot(pos < 0 || pos >= p.S_max) != 0 && lane == 0) p.status[0] |= 1;
@@ -158,8 +190,9 @@ __global__ __launch_bounds__(256) void attn_partial(PartParams p) {
     }
 
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const long long k_end = min(total, (long long)(w + 1) * KT);
-    long long key = (long long)w * KT;
+    const long long k_begin = wave_first_key(w, KE, KO);
+    const long long k_end = min(total, k_begin + ((w & 4) ? KO : KE));
+    long long key = k_begin;
     while (key < k_end) {
         // sequence of this key: the last b whose offset <= key (it has
         // keys: a sequence without keys shares its offset with the next)
@@ -376,7 +409,7 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
     const int cg = threadIdx.x / PER, r = threadIdx.x - cg * PER;
     const int f = r / D4, d4 = r - f * D4;
     // the waves that covered this pair, and so its consecutive slots
-    const long long KT = p.seq_tab[p.B];
+    const long long KE = p.seq_tab[p.B], KO = p.seq_tab[p.B + 1];
     const int n = keys_of(p.nkeys, b, p.nkeys_add, p.S_max);
     if (n == 0) {   // no keys: zero output, LSE -inf (no slot belongs to this pair)
         if (f < p.nflows && cg == 0) {
@@ -389,7 +422,7 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
         return;
     }
     const long long lo = p.seq_tab[b] + (long long)h * n;
-    const int w0 = (int)(lo / KT), w1 = (int)((lo + n - 1) / KT);
+    const int w0 = wave_of_key(lo, KE, KO), w1 = wave_of_key(lo + n - 1, KE, KO);
     const size_t first = (size_t)w0 + (size_t)b * p.H + h;
     const int C = w1 - w0 + 1;
     float m = -1e30f, l = 0.f;
@@ -444,7 +477,7 @@ __global__ __launch_bounds__(256) void attn_combine(CombParams p) {
 }
 
 constexpr int kMaxSlots = kAttnMaxSlots;   // partial results per launch at most (workspace bound)
-constexpr int kTabFloats = 256;            // sequence table [65] 64-bit, padded
+constexpr int kTabFloats = 256;            // sequence table [66] 64-bit, padded
 static_assert(kTabFloats + (size_t)kMaxSlots * (4 + 2 * 128) == kAttnPartFloatsMax, "workspace bound");
 
 // Waves of an attn_partial launch on the current device (cached): one

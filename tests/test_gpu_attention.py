@@ -71,6 +71,14 @@ def test_long_context():
     _run(_abi.DF_BF16, 2, 4, 128, 131072, [131072, 77777], seed=33)
 
 
+def test_long_waves_skewed_split():
+    """Enough keys that the waves average 2048 or more (2,127,174 keys over
+    1,024 waves), so even-workgroup waves take 3 % more keys than odd ones:
+    every (sequence, head) against the oracle, across the uneven wave ranges
+    and the combine's slot lookup for them."""
+    _run(_abi.DF_BF16, 3, 6, 64, 131072, [131072, 100000, 123457], seed=34)
+
+
 def test_full_attention_workload_sampled():
     c = C2_ATTN
     src = AttnInputs(c)
