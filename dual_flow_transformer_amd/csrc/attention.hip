@@ -145,12 +145,14 @@ __device__ __forceinline__ void wave_keys(long long total, int G, long long& KE,
 // First key of wave w: the waves of workgroup pairs (2i, 2i + 1) cover
 // 4 (KE + KO) keys in wave order.
 __device__ __forceinline__ long long wave_first_key(int w, long long KE, long long KO) {
+    if (KE == KO) return (long long)w * KE;
     const int r = w & 7;
     return (long long)(w >> 3) * 4 * (KE + KO) + (r < 4 ? r * KE : 4 * KE + (r - 4) * KO);
 }
 
 // The wave whose key range holds `key`.
 __device__ __forceinline__ int wave_of_key(long long key, long long KE, long long KO) {
+    if (KE == KO) return (int)(key / KE);   // unskewed: one division
     const long long P = 4 * (KE + KO), q = key / P, r = key - q * P;
     return (int)(8 * q + (r < 4 * KE ? r / KE : 4 + (r - 4 * KE) / KO));
 }
