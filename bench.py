@@ -34,15 +34,15 @@ TIMING_STRIDE = 7
 # timed steps, dual and primary-only), counters scaled by their reading for a plain 1 GiB copy
 # (x2.0 fetch, x1.0 write). Reported only while the kernel sources are the ones they were
 # measured on (attention pass: attention.hip; step traffic: every library source).
-COUNTER_SOURCES = {"attention_source_sha256": "f92b9ef8bfee3b3aa837ace3c52fadd3416d1a81741a722506eb049e9aeb04e0",
-                   "library_sources_sha256": "f157883b12fd28ed633de4ff900aa4f54a339569aceea22857ba94b3109d3ade"}
+COUNTER_SOURCES = {"attention_source_sha256": "b5eb70e54b8ee2d865fa1c741f1b650fdb21be0a0a533d09e4075cd9f5bf56e9",
+                   "library_sources_sha256": "5d2586b0f473afd81e105517cdd486b3ab82bd3295804fe83514d7c94db9e556"}
 COUNTERS = {
-    "dense_32l_d4096_b16_ctx8192": {"attention_traffic_bytes_per_launch": 2.15450e+09,
-                   "step_traffic_bytes": {"dual": 8.40720e+10, "primary_only": 8.30300e+10}},
+    "dense_32l_d4096_b16_ctx8192": {"attention_traffic_bytes_per_launch": 2.15500e+09,
+                   "step_traffic_bytes": {"dual": 8.39800e+10, "primary_only": 8.29850e+10}},
     "dense_1p3b_b16_ctx2048": {"attention_traffic_bytes_per_launch": 2.73400e+08,
-                   "step_traffic_bytes": {"dual": 9.89300e+09, "primary_only": 9.47000e+09}},
+                   "step_traffic_bytes": {"dual": 9.89500e+09, "primary_only": 9.47300e+09}},
     "moe_16l_e64_top4_b64_ctx1024": {"attention_traffic_bytes_per_launch": 5.47600e+08,
-                   "step_traffic_bytes": {"dual": 1.92990e+10, "primary_only": 1.85680e+10}},
+                   "step_traffic_bytes": {"dual": 1.93000e+10, "primary_only": 1.85690e+10}},
 }
 
 
