@@ -42,10 +42,16 @@ def _run(dtype, B, H, Dh, S, lens, seed, with_a=True):
                                 wsb, torch.cuda.current_stream().cuda_stream)
     assert rc == 0, _abi.df_status_str(rc)
     torch.cuda.synchronize()
-    Kf = odf.to_f64(K)
-    Vf = odf.to_f64(V)
-    ro, rl = odf.attention_dual(Kf, Vf, q[:, 0], q[:, 1], lens, a if with_a else None)
     go, gl = o.cpu().numpy(), lse.cpu().numpy()
+    # a sequence with no keys: zero outputs and LSE -inf; the oracle runs on the others
+    nz = [b for b, n in enumerate(lens) if n > 0]
+    for b in range(B):
+        if b not in nz:
+            assert np.all(go[b] == 0.0) and np.all(gl[b] == -np.inf), f"sequence {b}"
+    Kf = odf.to_f64(K[nz])
+    Vf = odf.to_f64(V[nz])
+    ro, rl = odf.attention_dual(Kf, Vf, q[nz, 0], q[nz, 1], [lens[b] for b in nz], a if with_a else None)
+    go, gl = go[nz], gl[nz]
     eo, el = max_abs(go, ro), max_abs(gl, rl)
     say(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
@@ -71,12 +77,15 @@ def test_long_context():
     _run(_abi.DF_BF16, 2, 4, 128, 131072, [131072, 77777], seed=33)
 
 
-def test_long_waves_skewed_split():
-    """Enough keys that the waves average 2048 or more (2,127,174 keys over
-    1,024 waves), so even-workgroup waves take 3 % more keys than odd ones:
-    every (sequence, head) against the oracle, across the uneven wave ranges
-    and the combine's slot lookup for them."""
-    _run(_abi.DF_BF16, 3, 6, 64, 131072, [131072, 100000, 123457], seed=34)
+@pytest.mark.parametrize("B,H,lens", [(3, 6, [131072, 100000, 123457]),
+                                      (4, 9, [131072, 0, 1, 120000])])
+def test_long_waves_skewed_split(B, H, lens):
+    """Enough keys that the waves average 2048 or more (2,127,174 and
+    2,259,657 keys over 1,024 waves), so even-workgroup waves take 3 % more
+    keys than odd ones: every (sequence, head) against the oracle, across the
+    uneven wave ranges and the combine's slot lookup for them, with a
+    sequence that has no keys and one with a single key in the same launch."""
+    _run(_abi.DF_BF16, B, H, 64, 131072, lens, seed=34)
 
 
 def test_full_attention_workload_sampled():
