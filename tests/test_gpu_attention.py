@@ -1,7 +1,7 @@
 """Shared-K/V dual attention on the GPU (df_attention_dual) against the
 oracle: ragged small cases element by element, edge lengths, and the full
-attention-only workload (B=32, H=32, Dh=128, len in [1024, 4096]) on sampled
-(sequence, head) pairs.
+attention-only workload (B=32, H=32, Dh=128, len in [1024, 4096]) on every
+(sequence, head) pair.
 
 Tolerance (fp32 accumulation against float64): a score's rounding error is
 at most about Dh * 2^-24 * sum|q_i k_i| ~ 6e-5 for N(0,1) inputs, so output
@@ -88,7 +88,11 @@ def test_long_waves_skewed_split(B, H, lens):
     _run(_abi.DF_BF16, B, H, 64, 131072, lens, seed=34)
 
 
-def test_full_attention_workload_sampled():
+def test_full_attention_workload_all_pairs():
+    """The attention-only workload at full size (32 sequences x 32 heads,
+    lengths uniform in [1024, 4096]: 2,594,976 keys, so the launch takes the
+    XCD-skewed split): every (sequence, head) pair and both flows against
+    the oracle."""
     c = C2_ATTN
     src = AttnInputs(c)
     lens = src.lengths()
@@ -113,17 +117,16 @@ def test_full_attention_workload_sampled():
     torch.cuda.synchronize()
     go, gl = o.cpu().numpy(), lse.cpu().numpy()
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
-    bs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, c.B - 1, 7})
     worst = 0.0
-    for b in bs:
+    for b in range(c.B):
         Kb = odf.to_f64(src.kv_block("k", b, int(lens[b])))
         Vb = odf.to_f64(src.kv_block("v", b, int(lens[b])))
-        for h in (0, 5, c.H - 1):
+        for h in range(c.H):
             qq2 = q2[b, h] + a.reshape(c.H, c.Dh)[h] * q1[b, h]
             for f, qq in enumerate((q1[b, h], qq2)):
                 ro, rl = odf.attention_one(qq.astype(np.float64), Kb[h], Vb[h])
                 worst = max(worst, max_abs(go[b, f, h], ro), abs(gl[b, f, h] - rl))
-    say(f"  sampled max error {worst:.3e}")
+    say(f"  all pairs max error {worst:.3e}")
     assert worst < TOL
 
 
